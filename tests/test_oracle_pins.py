@@ -1,0 +1,283 @@
+"""Pins of the fp64 oracle to what the pages and the mathematics fix.
+
+None of these checks retypes the oracle's own formula: the mask is rebuilt from the first
+page's swa_mask recipe (section 核心方法 1 of "滑动窗口注意力（SWA）配 sinks 比
+post-training 线性注意力更划算"), general outputs are compared with torch's
+scaled_dot_product_attention in float64 given that recipe mask, and special cases are
+compared with their closed forms.  A dropped term, a wrong sign or index, a transposed
+operand or a wrong GQA mapping in the oracle fails at least one test here.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import oracle as orc
+from sliding_window_attention_02_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def recipe_mask(L, w, s):
+    """The first page's mask recipe as printed: per row, the window of the w most recent
+    positions up to the row, OR the first s columns for every row (no causal cut)."""
+    t = np.arange(L)[:, None]
+    i = np.arange(L)[None, :]
+    window = (i >= t - w + 1) & (i <= t)
+    sinks = np.broadcast_to(i < s, (L, L))
+    return window | sinks
+
+
+def causal_recipe_mask(L, w_loc, s):
+    """The reading adopted for the recipe: intersect it with causality (i <= t)."""
+    return recipe_mask(L, w_loc, s) & np.tri(L, dtype=bool)
+
+
+def sdpa_reference(q, k, v, allowed, scale):
+    """torch SDPA in float64 on the CPU with an explicit boolean mask; GQA by repeating each
+    kv-head over its contiguous group of q-heads."""
+    q = torch.as_tensor(q, dtype=torch.float64)
+    k = torch.as_tensor(k, dtype=torch.float64)
+    v = torch.as_tensor(v, dtype=torch.float64)
+    g = q.shape[2] // k.shape[2]
+    qh = q.permute(0, 2, 1, 3)
+    kh = k.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)
+    vh = v.repeat_interleave(g, dim=2).permute(0, 2, 1, 3)
+    m = torch.as_tensor(allowed)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=m, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def f64(x):
+    return x.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- window convention
+
+
+def test_local_window_conventions():
+    assert orc.local_window(64, 4, orc.ADDITIVE) == 64
+    assert orc.local_window(64, 4, orc.TOTAL) == 60
+    assert orc.local_window(5, 4, orc.TOTAL) == 1
+    for bad in [(4, 4, orc.TOTAL), (3, 4, orc.TOTAL), (0, 0, orc.ADDITIVE), (4, -1, orc.ADDITIVE),
+                (4, 0, 7)]:
+        with pytest.raises(ValueError):
+            orc.local_window(*bad)
+
+
+# ---------------------------------------------------------------- allowed sets
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 7, 16, 33, 40])
+def test_mask_equals_causal_recipe_and_closed_forms(L):
+    for w_loc in range(1, L + 6):
+        for s in range(0, 10):
+            m = orc.mask(L, w_loc, s)
+            assert np.array_equal(m, causal_recipe_mask(L, w_loc, s)), (L, w_loc, s)
+            # two disjoint ranges [0, min(s, t+1)) and [max(s, t-w_loc+1), t]
+            t = np.arange(L)[:, None]
+            i = np.arange(L)[None, :]
+            ranges = (i < np.minimum(s, t + 1)) | ((i >= np.maximum(s, t - w_loc + 1)) & (i <= t))
+            assert np.array_equal(m, ranges)
+            assert np.array_equal(m.sum(1), np.minimum(np.arange(L) + 1, w_loc + s))
+
+
+def test_printed_recipe_is_noncausal_before_the_sinks():
+    """Reading: sinks past the query are dropped.  The printed recipe marks them."""
+    L, w, s = 8, 3, 4
+    raw = recipe_mask(L, w, s)
+    assert raw[0, 3] and not orc.mask(L, w, s)[0, 3]
+    assert not np.triu(orc.mask(L, w, s), 1).any()
+
+
+def test_window_counts_self_w_keys():
+    """Token i sees i-W+1..i: W keys including itself (wiblog page, SWA 核心机制)."""
+    W = 7
+    m = orc.mask(50, W, 0)
+    for t in range(W - 1, 50):
+        assert list(np.nonzero(m[t])[0]) == list(range(t - W + 1, t + 1))
+
+
+def test_swa64_4_keeps_68_tokens():
+    g = golden("swa64_4_cache_tokens.json")
+    t = g["context"] - 1
+    kept = sum(orc.allowed(t, i, g["w"], g["s"]) for i in range(t + 1))
+    assert kept == g["tokens_held"]
+    slots = orc.ring_simulate(g["context"], g["w"], g["s"])
+    assert int((slots >= 0).sum()) == g["tokens_held"]
+
+
+def test_ring_worked_example_window4():
+    g = golden("ring_window4_example.json")
+    slots = orc.ring_simulate(len(g["appended_positions"]), g["window"], g["sinks"])
+    assert sorted(slots.tolist()) == g["held_positions"]
+    assert slots.tolist() == g["slot_contents"]
+    for p in g["evicted_positions"]:
+        assert p not in slots
+
+
+def test_ring_slot_map_with_pinned_sinks():
+    """Reading of the slot map: sinks pinned in slots 0..s-1, position p >= s in slot
+    s + (p mod w_loc)."""
+    slots = orc.ring_simulate(101, 64, 4)
+    assert slots[:4].tolist() == [0, 1, 2, 3]
+    assert slots[4 + 100 % 64] == 100 and slots[4 + 99 % 64] == 99
+    assert slots[4 + 37 % 64] == 37 and slots[4 + 36 % 64] == 100
+
+
+@pytest.mark.parametrize("w_loc,s", [(64, 4), (5, 0), (3, 2), (1, 3), (16, 7)])
+def test_ring_holds_exactly_the_allowed_set(w_loc, s):
+    L = 300
+    ref = causal_recipe_mask(L, w_loc, s)
+    for t in range(L):
+        slots = orc.ring_simulate(t + 1, w_loc, s)
+        held = sorted(int(p) for p in slots if p >= 0)
+        assert held == list(np.nonzero(ref[t])[0]), (t, w_loc, s)
+
+
+# ---------------------------------------------------------------- attention outputs
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d", [(1, 9, 1, 1, 4), (2, 17, 4, 2, 8), (1, 33, 8, 2, 16),
+                                          (1, 20, 4, 4, 5)])
+def test_full_window_equals_dense_causal_attention(B, L, Hq, Hkv, d):
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=7)
+    scale = 0.37
+    causal = np.tri(L, dtype=bool)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), causal, scale)
+    for w, s in [(L, 0), (L + 5, 0), (L, 3), (L - 2, 2)]:  # w_loc + s >= L: every key <= t
+        out = orc.prefill(f64(q), f64(k), f64(v), w, s, scale)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@settings(max_examples=40, deadline=None)
+@given(B=st.integers(1, 2), L=st.integers(1, 40), Hkv=st.integers(1, 3), g=st.sampled_from([1, 2, 4]),
+       d=st.integers(1, 12), w=st.integers(1, 45), s=st.integers(0, 9), conv=st.sampled_from([0, 1]),
+       seed=st.integers(0, 10_000))
+def test_general_case_equals_sdpa_with_recipe_mask(B, L, Hkv, g, d, w, s, conv, seed):
+    if conv == orc.TOTAL and w - s < 1:
+        w = s + 1
+    w_loc = w if conv == orc.ADDITIVE else w - s
+    q, k, v = inputs.random_qkv(B, L, Hkv * g, Hkv, d, seed=seed, sink_boost_n=4, sink_boost=4.0)
+    scale = 1.0 / np.sqrt(d)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), causal_recipe_mask(L, w_loc, s), scale)
+    out = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_tiny_workload_equals_sdpa():
+    wl = inputs.prefill_workloads()["tiny_swa64_4"]
+    q, k, v = inputs.prefill_inputs(wl)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), causal_recipe_mask(wl.L, wl.w, wl.s), wl.scale)
+    out = orc.prefill(f64(q), f64(k), f64(v), wl.w, wl.s, wl.scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_window_one_no_sinks_returns_own_value():
+    q, k, v = inputs.random_qkv(2, 30, 4, 2, 16, seed=3)
+    out = orc.prefill(f64(q), f64(k), f64(v), 1, 0, 0.25)
+    want = np.repeat(f64(v), 2, axis=2)
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("w,s", [(5, 0), (5, 3), (1, 4), (12, 2), (64, 4)])
+def test_zero_query_gives_mean_over_allowed_set(w, s):
+    """q = 0 makes every allowed weight 1/|A(t)|: with one-hot values the output row is the
+    indicator of A(t) divided by its size."""
+    L = 96
+    q = np.zeros((1, L, 2, L))
+    k = f64(inputs.random_qkv(1, L, 1, 1, L, seed=11)[1])
+    v = np.eye(L)[None, :, None, :]
+    out = orc.prefill(q, k, v, w, s, 1.0)
+    allowed = causal_recipe_mask(L, w, s)
+    want = allowed / allowed.sum(1, keepdims=True)
+    for h in range(2):
+        np.testing.assert_allclose(out[0, :, h, :], want, rtol=0, atol=1e-15)
+
+
+def test_row_weights_sum_to_one_and_output_in_hull():
+    L, d, w, s = 70, 8, 16, 3
+    q, k, v = inputs.random_qkv(1, L, 1, 1, d, seed=5, sink_boost_n=4, sink_boost=4.0)
+    qd, kd, vd = f64(q)[0, :, 0], f64(k)[0, :, 0], f64(v)[0, :, 0]
+    out = orc.prefill(f64(q), f64(k), f64(v), w, s, 0.3)[0, :, 0]
+    allowed = causal_recipe_mask(L, w, s)
+    for t in range(L):
+        p = orc.row_weights(qd[t], kd, t, w, s, 0.3)
+        assert abs(p.sum() - 1.0) < 1e-12
+        assert np.all(p[~allowed[t, : t + 1]] == 0.0) and np.all(p[allowed[t, : t + 1]] > 0.0)
+        vs = vd[: t + 1][allowed[t, : t + 1]]
+        assert np.all(out[t] >= vs.min(0) - 1e-12) and np.all(out[t] <= vs.max(0) + 1e-12)
+
+
+def test_total_convention_is_additive_with_shorter_window():
+    q, k, v = inputs.random_qkv(1, 50, 4, 2, 8, seed=9, sink_boost_n=4, sink_boost=4.0)
+    a = orc.prefill(f64(q), f64(k), f64(v), 20, 4, 0.3, orc.TOTAL)
+    b = orc.prefill(f64(q), f64(k), f64(v), 16, 4, 0.3, orc.ADDITIVE)
+    assert np.array_equal(a, b)
+
+
+def test_large_logits_stay_finite():
+    q, k, v = inputs.random_qkv(1, 24, 2, 1, 16, seed=2)
+    scale = 200.0  # logits of order 1e3: exp without the max shift would overflow
+    out = orc.prefill(f64(q), f64(k), f64(v), 24, 0, scale)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), np.tri(24, dtype=bool), scale)
+    assert np.isfinite(out).all()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------- decode rows
+
+
+def test_decode_row_matches_prefill_row_any_order_and_ignores_extra_entries():
+    L, Hq, Hkv, d, w, s = 60, 4, 2, 8, 10, 3
+    q, k, v = inputs.random_qkv(1, L, Hq, Hkv, d, seed=21, sink_boost_n=4, sink_boost=4.0)
+    ref = orc.prefill(f64(q), f64(k), f64(v), w, s, 0.4)
+    rng = np.random.default_rng(0)
+    for t in [0, 1, 2, 5, 12, 13, 40, 59]:
+        perm = rng.permutation(t + 1)
+        out, used = orc.decode_row(f64(q)[0, t], perm, f64(k)[0, perm], f64(v)[0, perm], t, w, s, 0.4)
+        assert used == min(t + 1, w + s)
+        np.testing.assert_allclose(out, ref[0, t], rtol=0, atol=1e-13)
+    with pytest.raises(ValueError):
+        orc.decode_row(f64(q)[0, 3], [0, 0], f64(k)[0, :2], f64(v)[0, :2], 3, w, s, 0.4)
+
+
+@pytest.mark.parametrize("w_loc,s", [(16, 3), (64, 4), (4, 0)])
+def test_ring_storage_order_decode_equals_prefill_row(w_loc, s):
+    """Attending over the ring's valid slots in storage order (no reordering by position)
+    reproduces prefill row t through sink fill, ring fill and wrap-around."""
+    L, Hq, Hkv, d = 150, 4, 2, 8
+    q, k, v = inputs.random_qkv(1, L, Hq, Hkv, d, seed=31, sink_boost_n=4, sink_boost=4.0)
+    qd, kd, vd = f64(q)[0], f64(k)[0], f64(v)[0]
+    ref = orc.prefill(f64(q), f64(k), f64(v), w_loc, s, 0.35)[0]
+    for t in range(L):
+        slots = orc.ring_simulate(t + 1, w_loc, s)
+        held = np.array([p for p in slots if p >= 0], dtype=np.int64)
+        out, used = orc.decode_row(qd[t], held, kd[held], vd[held], t, w_loc, s, 0.35)
+        assert used == len(held)
+        np.testing.assert_allclose(out, ref[t], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- inputs
+
+
+def test_inputs_are_seeded_and_sink_boost_is_exact():
+    a = inputs.random_qkv(1, 16, 2, 1, 8, seed=4, sink_boost_n=4, sink_boost=4.0)
+    b = inputs.random_qkv(1, 16, 2, 1, 8, seed=4, sink_boost_n=4, sink_boost=4.0)
+    c = inputs.random_qkv(1, 16, 2, 1, 8, seed=4)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y) and x.dtype == torch.bfloat16
+    assert torch.equal(a[1][:, :4].float(), 4 * c[1][:, :4].float())
+    assert torch.equal(a[1][:, 4:], c[1][:, 4:])
+    k1, v1 = inputs.kv_at(5, 262144, 2, 8, 16)
+    k2, v2 = inputs.kv_at(5, 262144, 2, 8, 16)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2) and not torch.equal(k1, v1)
+    assert not torch.equal(inputs.kv_at(5, 262145, 2, 8, 16)[0], k1)
