@@ -1,0 +1,153 @@
+/*
+ * swa.h -- C ABI of libswa.so: SWA(w,s) causal softmax attention on MI355X (gfx950).
+ *
+ * SWA(w,s): query t attends to the keys at positions max(0, t-w_loc+1) .. t (the
+ * w_loc most recent tokens, itself included) together with the first s positions
+ * ("attention sinks"), restricted to positions <= t, with a softmax taken over that
+ * allowed set only.  Sources: page "滑动窗口注意力（SWA）配 sinks 比 post-training
+ * 线性注意力更划算" (papers.ananclaw.com explainer of arXiv 2608.28444), section
+ * 核心方法 1 (the notation paragraph, the x_t equation and the swa_mask recipe);
+ * page "从长文档摘要说起：为什么注意力范围成了瓶颈" (wiblog.cn), section "SWA 的核心机制"
+ * (token i sees i-W+1 .. i).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronises.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL means the null stream) and runs asynchronously.
+ *   - bf16 means IEEE bfloat16 stored as 16-bit words; all tensors are dense,
+ *     row-major (last index fastest) and 16-byte aligned.
+ *   - Arguments are validated on the host before any HIP call.  A non-zero return
+ *     leaves the device untouched (for SWA_EINVAL / SWA_EUNSUPPORTED) and sets a
+ *     thread-local message readable with swa_last_error().
+ *   - Window convention `conv`: SWA_CONV_ADDITIVE gives w_loc = w (w recent keys plus
+ *     s sinks, the "64+4=68 tokens" reading of the first page's deployment notes);
+ *     SWA_CONV_TOTAL gives w_loc = w - s (a total window of w that includes the sinks,
+ *     as the PaperWeekly page "几亿Token白练了？" phrases SWA(64,4)).  w_loc must be >= 1.
+ *   - Grouped-query attention: Hq % Hkv == 0 and q-head h reads kv-head h / (Hq/Hkv).
+ *   - Supported head dimensions: d = 64 and d = 128 (others give SWA_EUNSUPPORTED).
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SWA_OK 0
+#define SWA_EINVAL (-1)        /* bad argument (null/misaligned pointer, bad size...) */
+#define SWA_EUNSUPPORTED (-2)  /* valid request this build does not implement (d, sizes) */
+#define SWA_EHIP (-3)          /* the HIP runtime reported an error at launch */
+
+/* Window conventions. */
+#define SWA_CONV_ADDITIVE 0
+#define SWA_CONV_TOTAL 1
+
+/*
+ * swa_prefill -- SWA(w,s) attention over whole sequences.
+ *
+ * Operation: for every batch b, position t < L and q-head h,
+ *   out[b][t][h][:] = sum_{i in A(t)} softmax_i(scale * <q[b][t][h], k[b][i][g(h)]>)
+ *                     * v[b][i][g(h)][:]
+ * with A(t) = { i <= t : i >= t - w_loc + 1 or i < s } and g(h) = h / (Hq/Hkv).
+ * Defined by the first page's x_t equation and swa_mask recipe (section 核心方法 1),
+ * with the readings stated above.  The computation visits only key tiles that meet
+ * A(t) for some query of a tile, the tile skipping described on page "Hybrid Sliding
+ * Window Attention" (bittide), section 三.3 (FlashAttention-2/3 window support).
+ *
+ *   q    bf16 [B][L][Hq][d]     (in)
+ *   k    bf16 [B][L][Hkv][d]    (in)
+ *   v    bf16 [B][L][Hkv][d]    (in)
+ *   out  fp32 [B][L][Hq][d]     (out; every element written)
+ *   scale  logit multiplier (1/sqrt(d) in the x_t equation); finite and > 0.
+ * Arithmetic: bf16 products with fp32 accumulation, fp32 softmax, probabilities
+ * rounded to bf16 for the value product.
+ * Errors: SWA_EINVAL for null or non-16-byte-aligned pointers, B, L, Hq, Hkv < 1,
+ * Hq % Hkv != 0, w < 1, s < 0, unknown conv, w_loc < 1, non-finite or non-positive
+ * scale; SWA_EUNSUPPORTED for d not in {64, 128} or a sequence of more than 2^31 - 1
+ * elements in q or out; SWA_EHIP if the launch fails.
+ */
+int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv,
+                int L, int d, int w, int s, float scale, int conv, void *stream);
+
+/*
+ * swa_kv_append -- write new tokens' keys and values into the bounded decode cache.
+ *
+ * Cache layout (per batch b and kv-head): s pinned sink slots followed by a ring of
+ * w_loc slots, i.e. k_cache / v_cache are bf16 [B][Hkv][s + w_loc][d].  Position p goes
+ * to slot p when p < s, else to slot s + (p mod w_loc), replacing the oldest ring entry.
+ * The rotation (evict the oldest, circular buffer addressed modulo the window) is the
+ * one on page "从长文档摘要说起" (wiblog.cn), section "与 KV Cache 的配合：轮转替换策略";
+ * the pinned sinks follow the first page's deployment notes (64+4=68 tokens kept).
+ *
+ *   k_new, v_new  bf16 [B][n_new][Hkv][d]   (in) tokens at positions pos[b] .. pos[b]+n_new-1
+ *   pos           int64 [B] device          (in) absolute position of k_new[b][0]
+ * When n_new > w_loc only the positions that survive the call are written (the sinks
+ * and the last w_loc positions), so every slot is written at most once.  Negative
+ * positions are skipped (nothing written).
+ * Errors: as swa_prefill, plus SWA_EINVAL for n_new < 1 or a null pos.
+ */
+int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                  const int64_t *pos, int B, int Hkv, int d, int w, int s, int n_new, int conv,
+                  void *stream);
+
+/*
+ * swa_decode_workspace_bytes -- device workspace that swa_decode_step needs for this
+ * shape (0 when the step runs without a split).  Returns 0 for invalid arguments too.
+ */
+size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, int conv);
+
+/*
+ * swa_decode_step -- one-token GQA decode over the bounded cache.
+ *
+ * For each batch b with query position t = pos[b] (already appended with
+ * swa_kv_append), out[b][h] is the SWA(w,s) attention row t of q[b][h] over the cache:
+ * the sinks 0 .. min(s, t+1)-1 and the ring slots holding positions
+ * max(s, t-w_loc+1) .. t.  Slot validity is derived from t alone, so stale slots from
+ * earlier use of the cache are never read.  The cache is read in storage order; the
+ * softmax sum does not depend on order.  The slot range is split over workgroups and
+ * the partial (max, sum, weighted values) are merged in a fixed order.
+ *
+ *   q          bf16 [B][Hq][d]   (in)
+ *   k_cache,   bf16 [B][Hkv][s + w_loc][d] (in)
+ *   v_cache
+ *   out        fp32 [B][Hq][d]   (out)
+ *   pos        int64 [B] device  (in)  must be >= 0
+ *   workspace  device scratch of at least swa_decode_workspace_bytes(...) bytes, or
+ *              NULL when that is 0; contents on entry are ignored.
+ * Errors: as swa_prefill, plus SWA_EINVAL for a too-small workspace.  Concurrent calls
+ * that share a workspace must be ordered by the caller.
+ */
+int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, float *out,
+                    const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s, float scale,
+                    int conv, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char *swa_last_error(void);
+
+/*
+ * Test hooks: dump the allowed-index sets exactly as the kernels derive them, using the
+ * same device functions as the hot kernels.
+ *
+ * swa_debug_prefill_mask: mask uint8 [L][L] device (out).  mask[t][i] = 1 iff the
+ * prefill kernel's tile walk for the tile holding query t visits key i and either
+ * classifies the tile as mask-free or its element predicate admits (t, i).  Requires
+ * L <= 8192.
+ *
+ * swa_debug_decode_slots: slot_pos int64 [B][s + w_loc] device (out): the position the
+ * decode kernel reads from each slot for query position pos[b], or -1 if the slot is
+ * skipped.
+ */
+int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, int conv,
+                           void *stream);
+int swa_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w, int s, int conv,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

@@ -62,6 +62,8 @@ def _load():
     lib.swa_oracle_prefill.restype = i32
     lib.swa_oracle_decode_row.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, vp]
     lib.swa_oracle_decode_row.restype = i64
+    lib.swa_oracle_decode_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i64, i64, i64, i64, dbl, vp, i32]
+    lib.swa_oracle_decode_rows.restype = i32
     lib.swa_oracle_ring_simulate.argtypes = [i64, i64, i64, vp]
     lib.swa_oracle_ring_simulate.restype = i32
     _lib = lib
@@ -148,6 +150,25 @@ def decode_row(q, pos, k, v, t: int, w: int, s: int, scale: float, conv: int = A
     if kept < 0:
         raise ValueError("swa_oracle_decode_row: bad arguments or duplicate positions")
     return out, int(kept)
+
+
+def decode_rows(q, pos, k, v, t, w: int, s: int, scale: float, conv: int = ADDITIVE,
+                nthreads: int | None = None) -> np.ndarray:
+    """decode_row for every batch item: q [B][Hq][d], pos [n] shared candidate positions,
+    k/v [B][n][Hkv][d], t [B] query positions -> fp64 [B][Hq][d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    t = np.ascontiguousarray(np.asarray(t, dtype=np.int64))
+    B, Hq, d = q.shape
+    _, n, Hkv, _ = k.shape
+    assert k.shape == (B, n, Hkv, d) and v.shape == k.shape and pos.shape == (n,) and t.shape == (B,)
+    w_loc = local_window(w, s, conv)
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    rc = _load().swa_oracle_decode_rows(_ptr(q), _ptr(pos), _ptr(k), _ptr(v), B, n, _ptr(t), Hq, Hkv, d,
+                                        w_loc, s, float(scale), _ptr(out), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("swa_oracle_decode_rows: bad arguments or duplicate positions")
+    return out
 
 
 def ring_simulate(n_appended: int, w_loc: int, s: int) -> np.ndarray:

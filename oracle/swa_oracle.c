@@ -294,3 +294,68 @@ int swa_oracle_ring_simulate(int64_t n_appended, int64_t w_loc, int64_t s, int64
     }
     return 0;
 }
+
+typedef struct {
+    const double *q, *k, *v;
+    const int64_t *pos, *t;
+    double *out;
+    int64_t B, n, Hq, Hkv, d, w_loc, s;
+    double scale;
+    int64_t nthreads, tid, status;
+} decode_job;
+
+static void *decode_worker(void *arg)
+{
+    decode_job *j = (decode_job *)arg;
+    j->status = 0;
+    for (int64_t b = j->tid; b < j->B; b += j->nthreads) {
+        const int64_t kept = swa_oracle_decode_row(
+            j->q + b * j->Hq * j->d, j->pos, j->k + b * j->n * j->Hkv * j->d,
+            j->v + b * j->n * j->Hkv * j->d, j->n, j->t[b], j->Hq, j->Hkv, j->d, j->w_loc, j->s,
+            j->scale, j->out + b * j->Hq * j->d);
+        if (kept < 0)
+            j->status = -1;
+    }
+    return NULL;
+}
+
+/* Decode rows of a batch, one swa_oracle_decode_row per batch item, items spread over
+ * threads.  q: [B][Hq][d]; pos: [n] shared candidate positions; k, v: [B][n][Hkv][d];
+ * t: [B] query positions; out: [B][Hq][d].  Returns 0, or -1 if any row failed. */
+int swa_oracle_decode_rows(const double *q, const int64_t *pos, const double *k, const double *v,
+                           int64_t B, int64_t n, const int64_t *t, int64_t Hq, int64_t Hkv,
+                           int64_t d, int64_t w_loc, int64_t s, double scale, double *out,
+                           int nthreads)
+{
+    if (B < 1 || !t)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > B)
+        nthreads = (int)B;
+    decode_job *jobs = (decode_job *)calloc((size_t)nthreads, sizeof(decode_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    int started = 0, rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        decode_job j = {q, k, v, pos, t, out, B, n, Hq, Hkv, d, w_loc, s, scale, nthreads, i, -3};
+        jobs[i] = j;
+        if (pthread_create(&th[i], NULL, decode_worker, &jobs[i]) != 0) {
+            rc = -1;
+            break;
+        }
+        ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+        pthread_join(th[i], NULL);
+        if (jobs[i].status != 0)
+            rc = -1;
+    }
+    free(jobs);
+    free(th);
+    return rc;
+}

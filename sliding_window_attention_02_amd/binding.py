@@ -1,0 +1,191 @@
+"""ctypes binding of libswa.so: argument marshalling only.
+
+Each function checks device, dtype, contiguity and shapes of torch tensors, then passes raw
+device pointers, sizes and the current HIP stream to the C ABI declared in include/swa.h.
+Every step of the computation runs in the HIP kernels; there is no fallback.  If the
+library has not been built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+ADDITIVE = 0
+TOTAL = 1
+
+SWA_OK = 0
+SWA_EINVAL = -1
+SWA_EUNSUPPORTED = -2
+SWA_EHIP = -3
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+
+EXPORTS = (
+    "swa_prefill",
+    "swa_kv_append",
+    "swa_decode_workspace_bytes",
+    "swa_decode_step",
+    "swa_last_error",
+    "swa_debug_prefill_mask",
+    "swa_debug_decode_slots",
+)
+
+_lib = None
+
+
+class SwaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libswa.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sliding_window_attention_02_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, vp, f32, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    L.swa_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.swa_prefill.restype = i32
+    L.swa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    L.swa_kv_append.restype = i32
+    L.swa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.swa_decode_workspace_bytes.restype = sz
+    L.swa_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.swa_decode_step.restype = i32
+    L.swa_last_error.argtypes = []
+    L.swa_last_error.restype = ctypes.c_char_p
+    L.swa_debug_prefill_mask.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
+    L.swa_debug_prefill_mask.restype = i32
+    L.swa_debug_decode_slots.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    L.swa_debug_decode_slots.restype = i32
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().swa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != SWA_OK:
+        raise SwaError(rc, last_error())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def local_window(w: int, s: int, conv: int = ADDITIVE) -> int:
+    """Local window length: w (additive convention) or w - s (total-window convention)."""
+    wl = w if conv == ADDITIVE else w - s
+    if conv not in (ADDITIVE, TOTAL) or w < 1 or s < 0 or wl < 1:
+        raise ValueError(f"no local window for w={w}, s={s}, conv={conv}")
+    return wl
+
+
+def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADDITIVE, out=None):
+    """SWA(w,s) prefill.  q bf16 [B][L][Hq][d], k/v bf16 [B][L][Hkv][d] -> fp32 [B][L][Hq][d]."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][L][Hq][d]")
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2] if k.dim() == 4 else -1
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, L, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, L, Hkv, d))
+    if out is None:
+        out = torch.empty((B, L, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, L, Hq, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, d,
+                             w, s, scale, conv, _stream(q)))
+    return out
+
+
+def alloc_cache(B: int, Hkv: int, d: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
+    """Empty (k_cache, v_cache), bf16 [B][Hkv][s + w_loc][d] each."""
+    n = s + local_window(w, s, conv)
+    k = torch.zeros((B, Hkv, n, d), dtype=torch.bfloat16, device=device)
+    return k, torch.zeros_like(k)
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, pos, w: int, s: int, conv: int = ADDITIVE):
+    """Write k_new/v_new bf16 [B][n_new][Hkv][d] at positions pos[b] .. pos[b]+n_new-1."""
+    B, Hkv, n_slots, d = k_cache.shape
+    n_new = k_new.shape[1]
+    if n_slots != s + local_window(w, s, conv):
+        raise ValueError("cache slot count does not match s + w_loc")
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _need(k_new, "k_new", torch.bfloat16, (B, n_new, Hkv, d))
+    _need(v_new, "v_new", torch.bfloat16, (B, n_new, Hkv, d))
+    _need(pos, "pos", torch.int64, (B,))
+    _check(lib().swa_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                               pos.data_ptr(), B, Hkv, d, w, s, n_new, conv, _stream(k_cache)))
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, w: int, s: int, conv: int = ADDITIVE) -> int:
+    return int(lib().swa_decode_workspace_bytes(B, Hq, Hkv, d, w, s, conv))
+
+
+def alloc_workspace(B: int, Hq: int, Hkv: int, d: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
+    n = decode_workspace_bytes(B, Hq, Hkv, d, w, s, conv)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def decode_step(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = None, conv: int = ADDITIVE,
+                out=None, workspace=None):
+    """One-token decode: q bf16 [B][Hq][d] at positions pos[b] (already appended) -> fp32 [B][Hq][d]."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _need(pos, "pos", torch.int64, (B,))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, d))
+    need = decode_workspace_bytes(B, Hq, Hkv, d, w, s, conv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                 pos.data_ptr(), B, Hq, Hkv, d, w, s, scale, conv, ws_ptr or None, ws_bytes,
+                                 _stream(q)))
+    return out
+
+
+def debug_prefill_mask(L: int, Hq: int, Hkv: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
+    """uint8 [L][L]: the (query, key) pairs the prefill kernel's tile walk admits."""
+    m = torch.empty((L, L), dtype=torch.uint8, device=device)
+    _check(lib().swa_debug_prefill_mask(m.data_ptr(), L, Hq, Hkv, w, s, conv, _stream(m)))
+    return m
+
+
+def debug_decode_slots(pos, w: int, s: int, conv: int = ADDITIVE):
+    """int64 [B][s + w_loc]: position the decode kernel reads from each slot, -1 if skipped."""
+    _need(pos, "pos", torch.int64)
+    B = pos.shape[0]
+    out = torch.empty((B, s + local_window(w, s, conv)), dtype=torch.int64, device=pos.device)
+    _check(lib().swa_debug_decode_slots(out.data_ptr(), pos.data_ptr(), B, w, s, conv, _stream(pos)))
+    return out

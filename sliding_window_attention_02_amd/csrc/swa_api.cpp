@@ -1,0 +1,223 @@
+// swa_api.cpp -- the C ABI of libswa.so (declared in include/swa.h).
+//
+// Every entry point validates its arguments on the host before touching HIP, resolves
+// the window convention to the local window w_loc, and enqueues kernels on the caller's
+// stream.  Nothing here allocates, frees or synchronises device memory.
+#include "../../include/swa.h"
+#include "swa_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return SWA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define CHECK_PTR(p)                                                                   \
+    do {                                                                               \
+        if ((p) == nullptr)                                                            \
+            return fail(SWA_EINVAL, "%s: " #p " is null", fn);                         \
+        if (!aligned16(p))                                                             \
+            return fail(SWA_EINVAL, "%s: " #p " is not 16-byte aligned", fn);          \
+    } while (0)
+
+// Local window from (w, s, conv): w for SWA_CONV_ADDITIVE, w - s for SWA_CONV_TOTAL.
+int resolve_window(const char *fn, int w, int s, int conv, int *w_loc)
+{
+    if (w < 1)
+        return fail(SWA_EINVAL, "%s: w must be >= 1 (got %d)", fn, w);
+    if (s < 0)
+        return fail(SWA_EINVAL, "%s: s must be >= 0 (got %d)", fn, s);
+    if (conv == SWA_CONV_ADDITIVE)
+        *w_loc = w;
+    else if (conv == SWA_CONV_TOTAL)
+        *w_loc = w - s;
+    else
+        return fail(SWA_EINVAL, "%s: unknown window convention %d", fn, conv);
+    if (*w_loc < 1)
+        return fail(SWA_EINVAL, "%s: the total window w=%d leaves no local window after s=%d sinks", fn, w,
+                    s);
+    return SWA_OK;
+}
+
+int check_heads(const char *fn, int B, int Hq, int Hkv, int d)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1)
+        return fail(SWA_EINVAL, "%s: B, Hq, Hkv must be >= 1 (got %d, %d, %d)", fn, B, Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(SWA_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+    if (d != 64 && d != 128)
+        return fail(SWA_EUNSUPPORTED, "%s: head dimension d=%d is not supported (64 or 128)", fn, d);
+    return SWA_OK;
+}
+
+int check_scale(const char *fn, float scale)
+{
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(SWA_EINVAL, "%s: scale must be finite and > 0", fn);
+    return SWA_OK;
+}
+
+int hip_status(const char *fn, hipError_t e)
+{
+    if (e != hipSuccess)
+        return fail(SWA_EHIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *swa_last_error(void) { return g_last_error.c_str(); }
+
+int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv, int L,
+                int d, int w, int s, float scale, int conv, void *stream)
+{
+    const char *fn = "swa_prefill";
+    CHECK_PTR(q);
+    CHECK_PTR(k);
+    CHECK_PTR(v);
+    CHECK_PTR(out);
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    if (L < 1)
+        return fail(SWA_EINVAL, "%s: L must be >= 1 (got %d)", fn, L);
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((rc = check_scale(fn, scale)))
+        return rc;
+    if ((long long)L * Hq * d > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: one sequence of q holds more than 2^31-1 elements", fn);
+    return hip_status(fn, swa::launch_prefill(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int64_t *pos,
+                  int B, int Hkv, int d, int w, int s, int n_new, int conv, void *stream)
+{
+    const char *fn = "swa_kv_append";
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    CHECK_PTR(k_new);
+    CHECK_PTR(v_new);
+    if (pos == nullptr)
+        return fail(SWA_EINVAL, "%s: pos is null", fn);
+    int rc = check_heads(fn, B, Hkv, Hkv, d);
+    if (rc)
+        return rc;
+    if (n_new < 1)
+        return fail(SWA_EINVAL, "%s: n_new must be >= 1 (got %d)", fn, n_new);
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    return hip_status(fn, swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, B, Hkv, d, w_loc, s,
+                                                n_new, static_cast<hipStream_t>(stream)));
+}
+
+size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, int conv)
+{
+    const char *fn = "swa_decode_workspace_bytes";
+    if (check_heads(fn, B, Hq, Hkv, d))
+        return 0;
+    int w_loc = 0;
+    if (resolve_window(fn, w, s, conv, &w_loc))
+        return 0;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return 0;
+    return swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes;
+}
+
+int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, float *out, const int64_t *pos,
+                    int B, int Hq, int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    const char *fn = "swa_decode_step";
+    CHECK_PTR(q);
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    CHECK_PTR(out);
+    if (pos == nullptr)
+        return fail(SWA_EINVAL, "%s: pos is null", fn);
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((rc = check_scale(fn, scale)))
+        return rc;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    if (plan.workspace_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+            return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, plan.workspace_bytes,
+                        workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if (!aligned16(workspace))
+            return fail(SWA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, swa::launch_decode(q, k_cache, v_cache, out, pos, B, Hq, Hkv, d, w_loc, s, scale,
+                                             workspace, plan, static_cast<hipStream_t>(stream)));
+}
+
+int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, int conv, void *stream)
+{
+    const char *fn = "swa_debug_prefill_mask";
+    if (mask == nullptr)
+        return fail(SWA_EINVAL, "%s: mask is null", fn);
+    int rc = check_heads(fn, 1, Hq, Hkv, 64);
+    if (rc)
+        return rc;
+    if (L < 1 || L > 8192)
+        return fail(SWA_EINVAL, "%s: L must be in [1, 8192] (got %d)", fn, L);
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    return hip_status(fn, swa::launch_debug_prefill_mask(mask, L, Hq, Hkv, w_loc, s,
+                                                         static_cast<hipStream_t>(stream)));
+}
+
+int swa_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w, int s, int conv, void *stream)
+{
+    const char *fn = "swa_debug_decode_slots";
+    if (slot_pos == nullptr || pos == nullptr)
+        return fail(SWA_EINVAL, "%s: null pointer", fn);
+    if (B < 1)
+        return fail(SWA_EINVAL, "%s: B must be >= 1", fn);
+    int w_loc = 0;
+    int rc = resolve_window(fn, w, s, conv, &w_loc);
+    if (rc)
+        return rc;
+    return hip_status(fn, swa::launch_debug_decode_slots(slot_pos, pos, B, w_loc, s,
+                                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

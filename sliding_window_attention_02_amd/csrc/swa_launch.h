@@ -1,0 +1,51 @@
+// swa_launch.h -- host-side launchers shared between the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// ----------------------------------------------------------------------------- prefill
+//
+// A workgroup computes 128 query rows: Tm consecutive tokens times Gw q-heads of one
+// kv-head (GQA packing), so each K/V tile staged in LDS serves Gw heads at once.
+struct PrefillGeometry {
+    int G;          // q-heads per kv-head
+    int Gw;         // q-heads per workgroup (largest divisor of G that is <= 4)
+    int Tm;         // tokens per workgroup (128 / Gw)
+    int n_hslices;  // G / Gw
+    int n_qtiles;   // ceil(L / Tm)
+};
+PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
+
+hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
+                          int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream);
+
+hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w_loc, int s,
+                                     hipStream_t stream);
+
+// ------------------------------------------------------------------------------ decode
+struct DecodePlan {
+    int n_slots;          // s + w_loc
+    int Gb;               // q-heads per workgroup (largest divisor of G that is <= 8)
+    int n_hslices;        // G / Gb
+    int n_split;          // workgroups over the slot range of one (b, kv-head, head slice)
+    int slots_per_split;  // slots per split
+    size_t workspace_bytes;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s);
+
+hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                            const int64_t *pos, int B, int Hkv, int d, int w_loc, int s, int n_new,
+                            hipStream_t stream);
+
+hipError_t launch_decode(const void *q, const void *k_cache, const void *v_cache, float *out,
+                         const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
+                         float scale, void *workspace, const DecodePlan &plan, hipStream_t stream);
+
+hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,
+                                     hipStream_t stream);
+
+}  // namespace swa

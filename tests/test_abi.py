@@ -1,0 +1,126 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every symbol that
+include/swa.h declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_attention_02_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+A = 0x10000  # a 16-byte aligned fake address: never dereferenced, every call below fails validation
+MIS = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sliding_window_attention_02_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(binding.EXPORTS) == set(names), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def err(lib):
+    return lib.swa_last_error().decode()
+
+
+def prefill(lib, q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, L=16, d=128, w=8, s=4, scale=0.1, conv=0):
+    return lib.swa_prefill(q, k, v, o, B, Hq, Hkv, L, d, w, s, scale, conv, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), binding.SWA_EINVAL, "q is null"),
+    (dict(o=None), binding.SWA_EINVAL, "out is null"),
+    (dict(k=MIS), binding.SWA_EINVAL, "k is not 16-byte aligned"),
+    (dict(B=0), binding.SWA_EINVAL, "B, Hq, Hkv"),
+    (dict(Hq=6, Hkv=4), binding.SWA_EINVAL, "multiple"),
+    (dict(d=96), binding.SWA_EUNSUPPORTED, "d=96"),
+    (dict(L=0), binding.SWA_EINVAL, "L must be"),
+    (dict(w=0), binding.SWA_EINVAL, "w must be"),
+    (dict(s=-1), binding.SWA_EINVAL, "s must be"),
+    (dict(conv=5), binding.SWA_EINVAL, "convention"),
+    (dict(w=4, s=4, conv=1), binding.SWA_EINVAL, "no local window"),
+    (dict(scale=float("nan")), binding.SWA_EINVAL, "scale"),
+    (dict(scale=0.0), binding.SWA_EINVAL, "scale"),
+    (dict(scale=-1.0), binding.SWA_EINVAL, "scale"),
+    (dict(L=1 << 20, Hq=32, Hkv=8), binding.SWA_EUNSUPPORTED, "2^31"),
+])
+def test_prefill_rejects_on_host(lib, kw, code, msg):
+    assert prefill(lib, **kw) == code
+    assert msg in err(lib)
+
+
+def test_kv_append_rejects_on_host(lib):
+    f = lib.swa_kv_append
+    assert f(A, A, A, A, None, 1, 8, 128, 64, 4, 1, 0, None) == binding.SWA_EINVAL
+    assert "pos is null" in err(lib)
+    assert f(A, A, A, A, A, 1, 8, 128, 64, 4, 0, 0, None) == binding.SWA_EINVAL
+    assert "n_new" in err(lib)
+    assert f(A, A, A, A, A, 1, 8, 80, 64, 4, 1, 0, None) == binding.SWA_EUNSUPPORTED
+    assert f(None, A, A, A, A, 1, 8, 128, 64, 4, 1, 0, None) == binding.SWA_EINVAL
+    assert f(A, A, A, A, A, 1, 8, 128, 3, 4, 1, 1, None) == binding.SWA_EINVAL
+
+
+def test_decode_workspace_query_and_rejection(lib):
+    # 512 (b, kv-head) pairs fill the chip: no split, no workspace.
+    assert lib.swa_decode_workspace_bytes(64, 32, 8, 128, 64, 4, 0) == 0
+    # One sequence: the 68 slots are split; partials are (max, sum, d values) per q-head and split.
+    ws = lib.swa_decode_workspace_bytes(1, 32, 8, 128, 64, 4, 0)
+    assert ws > 0 and ws % (32 * (128 + 2) * 4) == 0
+    assert lib.swa_decode_workspace_bytes(1, 32, 8, 96, 64, 4, 0) == 0
+    f = lib.swa_decode_step
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None)
+    assert rc == binding.SWA_EINVAL and "workspace" in err(lib)
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, A, ws - 4, None)
+    assert rc == binding.SWA_EINVAL and "workspace" in err(lib)
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, MIS, ws, None)
+    assert rc == binding.SWA_EINVAL and "aligned" in err(lib)
+    assert f(A, A, A, A, None, 1, 32, 8, 128, 64, 4, 0.1, 0, A, ws, None) == binding.SWA_EINVAL
+    assert f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.0, 0, A, ws, None) == binding.SWA_EINVAL
+
+
+def test_debug_hooks_reject_on_host(lib):
+    assert lib.swa_debug_prefill_mask(None, 16, 4, 4, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_prefill_mask(A, 9000, 4, 4, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_decode_slots(A, None, 1, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_decode_slots(A, A, 1, 2, 2, 1, None) == binding.SWA_EINVAL
+
+
+def test_error_message_is_per_call(lib):
+    assert prefill(lib, B=0) == binding.SWA_EINVAL
+    first = err(lib)
+    assert prefill(lib, d=32) == binding.SWA_EUNSUPPORTED
+    assert err(lib) != first
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.prefill(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), 4, 0)
+
+
+def test_local_window_matches_convention():
+    assert binding.local_window(64, 4, binding.ADDITIVE) == 64
+    assert binding.local_window(64, 4, binding.TOTAL) == 60
+    with pytest.raises(ValueError):
+        binding.local_window(4, 4, binding.TOTAL)

@@ -1,0 +1,54 @@
+"""Work/traffic accounting pinned to the pages' printed arithmetic and to the oracle mask."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from sliding_window_attention_02_amd import accounting as acc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_kv_cache_bytes_mistral():
+    g = golden("kv_cache_bytes.json")
+    full = acc.kv_cache_bytes(g["layers"], g["seq"], g["d_q"], g["n_kv"], g["bytes_per_value"])
+    assert full == g["full_cache_bytes"] == 2 ** 31
+    swa = acc.kv_cache_bytes(g["layers"], g["window"], g["d_q"], g["n_kv"], g["bytes_per_value"])
+    assert swa == g["swa_cache_bytes"]
+    long_full = acc.kv_cache_bytes(g["layers"], g["long_context"], g["d_q"], g["n_kv"], 2)
+    num, den = g["saving_fraction_at_long_context"]
+    assert (long_full - swa) * den == long_full * num
+    assert g["window"] * g["layers"] == g["receptive_field"]
+
+
+def test_flops_per_pair_follow_the_table():
+    g = golden("flop_table.json")
+    d = 128
+    assert acc.useful_flops(1, 1, 1, d, 1, 0) == g["matmul_flops_per_pair_per_head_over_d"] * d
+
+
+@pytest.mark.parametrize("L,w,s", [(1, 1, 0), (40, 7, 3), (33, 64, 4), (100, 5, 0), (64, 64, 4)])
+def test_pair_count_equals_mask_sum(L, w, s):
+    assert acc.pairs_per_head(L, w, s) == int(orc.mask(L, w, s).sum())
+
+
+def test_workload_figures():
+    # Llama-3.1-8B shape, SWA(64,4), L=4096: 276,250 pairs per head.
+    assert acc.pairs_per_head(4096, 64, 4) == 276250
+    assert acc.useful_flops(1, 32, 4096, 128, 64, 4) == 4 * 128 * 32 * 276250
+    assert acc.prefill_bytes(1, 4096, 32, 8, 128) == 4096 * (32 * 128 * 6 + 2 * 8 * 128 * 2)
+    # decode SWA(64,4) at t >= 67 reads 68 keys per kv-head
+    assert acc.decode_kv_bytes(1, 8, 128, acc.decode_keys(262144, 64, 4)) == 278528
+
+
+def test_executed_pairs_cover_useful_pairs():
+    for L, Hq, Hkv, w, s in [(4096, 32, 8, 64, 4), (1000, 4, 4, 300, 0), (777, 12, 4, 64, 70)]:
+        useful = acc.pairs_per_head(L, w, s) * Hq
+        assert acc.prefill_executed_pairs(L, Hq, Hkv, w, s) >= useful

@@ -1,0 +1,178 @@
+"""GPU parity of swa_prefill against the fp64 oracle (called through the C ABI).
+
+Tolerance: max |gpu - oracle| <= 2e-2 on every compared element (bf16 inputs, bf16
+products with fp32 accumulation, fp32 softmax, probabilities rounded to bf16 for the value
+product).  Index sets are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_attention_02_amd as swa
+from oracle import oracle as orc
+from sliding_window_attention_02_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ index sets
+
+
+MASK_CASES = [
+    # L, Hq, Hkv, w, s, conv
+    (1, 4, 4, 1, 0, 0), (1, 4, 1, 64, 4, 0), (5, 4, 4, 2, 1, 0), (64, 4, 1, 64, 4, 0),
+    (65, 4, 1, 64, 4, 0), (127, 8, 2, 5, 3, 0), (128, 4, 4, 1, 0, 0), (129, 4, 4, 65, 64, 0),
+    (300, 32, 8, 64, 4, 0), (300, 12, 4, 33, 70, 0), (333, 6, 1, 100, 63, 0), (500, 16, 2, 200, 65, 0),
+    (1000, 4, 4, 5000, 0, 0), (1000, 32, 8, 128, 4, 1), (1025, 4, 1, 256, 200, 1), (777, 5, 1, 96, 1, 0),
+    (4096, 32, 8, 64, 4, 0), (2048, 32, 8, 512, 4, 0),
+]
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,w,s,conv", MASK_CASES)
+def test_prefill_index_set_white_box(L, Hq, Hkv, w, s, conv):
+    say("mask", L, Hq, Hkv, w, s, conv)
+    got = swa.debug_prefill_mask(L, Hq, Hkv, w, s, conv).cpu().numpy().astype(bool)
+    ref = orc.mask(L, orc.local_window(w, s, conv), s)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("d,L,Hq,Hkv,w,s,conv", [
+    (128, 128, 4, 2, 5, 3, 0), (128, 100, 8, 2, 64, 4, 0), (64, 64, 4, 4, 7, 0, 0), (128, 128, 3, 1, 1, 0, 0),
+    (128, 128, 4, 4, 128, 0, 0), (64, 64, 2, 1, 10, 70, 0), (128, 97, 32, 8, 20, 4, 1), (64, 61, 16, 2, 3, 2, 0),
+])
+def test_prefill_index_set_black_box(d, L, Hq, Hkv, w, s, conv):
+    """q = 0 and one-hot values: output row t is exactly 1/|A(t)| on A(t) and 0 elsewhere."""
+    say("onehot", d, L, Hq, Hkv, w, s, conv)
+    q = torch.zeros(1, L, Hq, d, dtype=torch.bfloat16)
+    k = inputs.random_qkv(1, L, 1, Hkv, d, seed=3)[1]
+    v = torch.zeros(1, L, Hkv, d, dtype=torch.bfloat16)
+    for i in range(L):
+        v[0, i, :, i] = 1.0
+    out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, 1.0, conv).cpu().numpy()
+    ref = orc.mask(L, orc.local_window(w, s, conv), s)
+    cnt = ref.sum(1).astype(np.float32)
+    for h in range(Hq):
+        o = out[0, :, h, :]
+        assert np.array_equal(o[:, :L] != 0, ref)
+        assert np.all(o[:, L:] == 0)
+        np.testing.assert_allclose(o[:, :L][ref], np.repeat(1.0 / cnt, ref.sum(1)), rtol=1e-6, atol=0)
+
+
+# ------------------------------------------------------------------ values
+
+
+PARITY = [
+    # B, L, Hq, Hkv, d, w, s, conv, std, boost_n
+    (2, 300, 8, 2, 128, 64, 4, 0, 1.0, 4),
+    (1, 1000, 32, 8, 128, 64, 4, 0, 0.5, 4),
+    (2, 777, 32, 8, 128, 128, 4, 0, 1.0, 4),
+    (1, 1000, 16, 4, 128, 256, 0, 0, 1.0, 4),
+    (1, 1100, 8, 2, 128, 512, 4, 0, 1.0, 4),
+    (1, 1500, 8, 2, 128, 1000, 4, 0, 1.0, 0),
+    (1, 200, 12, 4, 128, 33, 70, 0, 1.0, 4),
+    (1, 333, 16, 2, 64, 50, 5, 1, 1.0, 4),
+    (1, 129, 4, 4, 64, 1, 0, 0, 1.0, 0),
+    (1, 1, 4, 1, 128, 64, 4, 0, 1.0, 4),
+    (1, 64, 4, 1, 128, 1000, 0, 0, 1.0, 0),
+    (3, 190, 6, 3, 64, 17, 2, 0, 2.0, 4),
+    (1, 513, 5, 1, 128, 100, 1, 0, 1.0, 4),
+]
+
+
+def check_close(got, ref, what):
+    err = np.abs(got - ref)
+    say(f"{what}: max {err.max():.3e} mean {err.mean():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= TOL, what
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,w,s,conv,std,boost", PARITY)
+def test_prefill_matches_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost):
+    say("parity", B, L, Hq, Hkv, d, w, s, conv)
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=L + 17 * w + s, std=std, sink_boost_n=boost, sink_boost=4.0)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, scale, conv).cpu().numpy()
+    ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    check_close(out, ref, "prefill")
+
+
+def test_tiny_workload_full_parity():
+    wl = inputs.prefill_workloads()["tiny_swa64_4"]
+    q, k, v = inputs.prefill_inputs(wl)
+    out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), wl.w, wl.s, wl.scale).cpu().numpy()
+    ref = orc.prefill(f64(q), f64(k), f64(v), wl.w, wl.s, wl.scale)
+    check_close(out, ref, wl.name)
+
+
+def sample_rows(L, w_loc, s, rng, n_random=12):
+    fixed = [0, 1, 2, 3, 4, 5, 31, 32, 63, 64, 65, 66, 67, 68, 127, 128, w_loc - 1, w_loc, w_loc + 1,
+             w_loc + s, w_loc + s + 1, L // 2, L - 65, L - 2, L - 1]
+    rows = {t for t in fixed if 0 <= t < L}
+    rows |= set(int(x) for x in rng.integers(0, L, n_random))
+    return sorted(rows)
+
+
+def oracle_rows(q, k, v, b, rows, w, s, conv, scale):
+    """Oracle rows for sampled positions, each from the sinks plus a margin below the window
+    (entries outside A(t) are dropped by the oracle's own predicate)."""
+    w_loc = orc.local_window(w, s, conv)
+    out = {}
+    for t in rows:
+        cand = sorted(set(range(min(s, t + 1))) | set(range(max(0, t - w_loc - 2), t + 1)))
+        out[t], used = orc.decode_row(f64(q[b, t]), cand, f64(k[b, cand]), f64(v[b, cand]), t, w, s, scale, conv)
+        assert used == min(t + 1, w_loc + s)
+    return out
+
+
+@pytest.mark.parametrize("name", ["llama8b_swa64_4", "sweep_w128_s0", "sweep_w512_s4", "mistral7b_w4096_s4",
+                                  "mistral7b_w4096_s0"])
+def test_full_size_workloads_sampled_rows(name):
+    """Full-size workloads in the benchmark's launch configuration, checked on sampled rows."""
+    wl = inputs.prefill_workloads()[name]
+    say("full", name)
+    q, k, v = inputs.prefill_inputs(wl)
+    out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), wl.w, wl.s, wl.scale, wl.conv).cpu()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(wl.seed)
+    w_loc = orc.local_window(wl.w, wl.s, wl.conv)
+    for b in sorted({0, wl.B - 1}):
+        rows = sample_rows(wl.L, w_loc, wl.s, rng)
+        ref = oracle_rows(q, k, v, b, rows, wl.w, wl.s, wl.conv, wl.scale)
+        got = np.stack([out[b, t].numpy() for t in rows])
+        check_close(got, np.stack([ref[t] for t in rows]), f"{name} b={b}")
+
+
+def test_prefill_is_deterministic_and_keeps_guard_bands():
+    B, L, Hq, Hkv, d = 1, 700, 32, 8, 128
+    q, k, v = [t.cuda() for t in inputs.random_qkv(B, L, Hq, Hkv, d, seed=5, sink_boost_n=4, sink_boost=4.0)]
+    n = B * L * Hq * d
+    guard = 1024
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[guard:guard + n].view(B, L, Hq, d)
+    swa.prefill(q, k, v, 64, 4, out=out)
+    first = out.clone()
+    swa.prefill(q, k, v, 64, 4, out=out)
+    assert torch.equal(first, out)
+    assert torch.isfinite(out).all()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+
+
+def test_prefill_on_a_side_stream():
+    q, k, v = [t.cuda() for t in inputs.random_qkv(1, 256, 8, 2, 128, seed=8)]
+    ref = swa.prefill(q, k, v, 32, 4)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = swa.prefill(q, k, v, 32, 4)
+    s.synchronize()
+    assert torch.equal(out, ref)
