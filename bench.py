@@ -1,0 +1,280 @@
+"""Benchmark: SWA(w,s) prefill useful TFLOP/s + decode tokens/s on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill of the Llama-3.1-8B-shaped SWA(64,4) workload (B=1, L=4096, Hq=32, Hkv=8,
+    d=128, bf16 inputs N(0,1)*0.5, sink keys x4, fp32 output), one swa_prefill launch;
+  * 256 decode tokens of the SWA(64,4) ring-cache workload at batch 64 (Hq=32, Hkv=8,
+    d=128), each token one swa_kv_append + swa_decode_step, positions 2^18 .. 2^18+255,
+    captured once in a HIP graph and replayed.
+Inputs are resident in HBM before the timed region.  The timed region is bracketed by
+torch.cuda.synchronize(); HIP events on the launch stream time every prefill launch and
+every decode replay inside it.
+
+Printed JSON line (one):
+  value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill launch time
+  decode           tokens/s of the decode leg and its HBM figures
+  roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
+                   launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
+                   38.5 useful flop per algorithmic byte, far below the 315 flop/byte ridge)
+  cpu_baseline     the fp64 oracle timed on host cores on the same prefill workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SRC = os.path.join(ROOT, "sliding_window_attention_02_amd", "csrc", "swa_prefill.hip")
+DEVICE_SRC = os.path.join(ROOT, "sliding_window_attention_02_amd", "csrc", "swa_device.h")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in (PREFILL_SRC, DEVICE_SRC):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"prefill_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel source digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9]+)", text)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
+        return None
+    return int(m_b.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_swa64_4", help="prefill workload name")
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-tokens", type=int, default=256)
+    ap.add_argument("--decode-start", type=int, default=2 ** 18)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cores))")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_probe(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 3}))
+
+
+def cpu_baseline(wl, q, k, v, threads: int):
+    """The oracle as it stands on the host cores: the whole prefill workload, timed once."""
+    from oracle import oracle as orc
+    from sliding_window_attention_02_amd import accounting as acc
+
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    orc.prefill(qd, kd, vd, wl.w, wl.s, wl.scale, wl.conv, nthreads=threads)
+    dt = time.perf_counter() - t0
+    w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+    flops = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {wl.name} prefill (B={wl.B}, L={wl.L}, Hq={wl.Hq}, Hkv={wl.Hkv}, d={wl.d}, "
+                      f"SWA({wl.w},{wl.s})) once in fp64, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the SWA(w,s) library runs on a single device and has "
+              "no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+
+    import torch
+
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import accounting as acc
+    from sliding_window_attention_02_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- prefill inputs
+    wl = inputs.prefill_workloads()[args.workload]
+    w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+    q, k, v = inputs.prefill_inputs(wl)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    algo_bytes = acc.prefill_bytes(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d)
+    executed = 4 * wl.d * wl.B * acc.prefill_executed_pairs(wl.L, wl.Hq, wl.Hkv, w_loc, wl.s)
+
+    # ---------------------------------------------------------------- decode inputs
+    dw = inputs.decode_workloads()["decode_swa64_4_b64"]
+    DB, T, P = args.decode_batch, args.decode_tokens, args.decode_start
+    dw_loc = dw.w if dw.conv == 0 else dw.w - dw.s
+    gen = dict(B=DB, Hkv=dw.Hkv, d=dw.d, std=dw.std, sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost)
+    kc, vc = swa.alloc_cache(DB, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    ws = swa.alloc_workspace(DB, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    seed_pos = list(range(dw.s)) + list(range(P - dw_loc, P))
+    sk, sv = inputs.kv_span(dw.seed, seed_pos, **gen)
+    swa.kv_append(kc, vc, sk[:, :dw.s].contiguous().to(dev), sv[:, :dw.s].contiguous().to(dev),
+                  torch.zeros(DB, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    swa.kv_append(kc, vc, sk[:, dw.s:].contiguous().to(dev), sv[:, dw.s:].contiguous().to(dev),
+                  torch.full((DB,), P - dw_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    dq = torch.stack([inputs.q_at(dw.seed, P + i, DB, dw.Hq, dw.d, dw.std) for i in range(T)]).to(dev)
+    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(T)]
+    dk = torch.stack([x[0][:, None] for x in kvs]).to(dev)  # [T][B][1][Hkv][d]
+    dv = torch.stack([x[1][:, None] for x in kvs]).to(dev)
+    dpos = (P + torch.arange(T, dtype=torch.int64)).repeat_interleave(DB).view(T, DB).to(dev)
+    dout = torch.empty((T, DB, dw.Hq, dw.d), dtype=torch.float32, device=dev)
+    # The graph replays T append+attend steps.  The cache is restored to the state after
+    # position P-1 before every replay, so each replay decodes the same token sequence.
+    snap_k, snap_v = kc.clone(), vc.clone()
+
+    def decode_steps():
+        for i in range(T):
+            swa.kv_append(kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.conv)
+            swa.decode_step(dq[i], kc, vc, dpos[i], dw.w, dw.s, dw.scale, dw.conv, out=dout[i], workspace=ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        decode_steps()  # eager warm-up on the capture stream
+    stream.synchronize()
+    kc.copy_(snap_k)
+    vc.copy_(snap_v)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        decode_steps()
+    torch.cuda.synchronize()
+
+    def step(evs=None, i=0):
+        # Decode replay first, then the prefill: the prefill's start event is always queued
+        # behind GPU work, so its interval never includes host launch latency.
+        kc.copy_(snap_k)
+        vc.copy_(snap_v)
+        if evs is not None:
+            evs[2][i].record()
+        graph.replay()
+        if evs is not None:
+            evs[3][i].record()
+            evs[0][i].record()
+        swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out)
+        if evs is not None:
+            evs[1][i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(4)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [evs[0][i].elapsed_time(evs[1][i]) for i in range(K)]
+    dec_ms = [evs[2][i].elapsed_time(evs[3][i]) for i in range(K)]
+    pre_mean = sum(pre_ms) / K
+    dec_mean = sum(dec_ms) / K
+    pre_sorted = sorted(pre_ms)
+    tflops = useful / (pre_mean * 1e-3) / 1e12
+    achieved_gbs = algo_bytes / (pre_mean * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+
+    dec_tokens_s = T * DB / (dec_mean * 1e-3)
+    n_keys = acc.decode_keys(P, dw_loc, dw.s)
+    dec_kv_bytes = acc.decode_kv_bytes(DB, dw.Hkv, dw.d, n_keys)
+    dec_step_us = dec_mean * 1e3 / T
+    dec_gbs = dec_kv_bytes / (dec_step_us * 1e-6) / 1e9
+
+    base = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        base = cpu_baseline(wl, q, k, v, threads)
+
+    rec = {
+        "metric": "SWA(w,s) prefill useful TFLOP/s + decode tokens/s, % of MFMA/HBM roofline",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name} prefill + decode_swa64_4_b{DB} ({T} tokens per step)",
+            "prefill": {"B": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "w": wl.w, "s": wl.s,
+                        "conv": "additive" if wl.conv == 0 else "total", "inputs": f"bf16 N(0,1)*{wl.std}",
+                        "out": "fp32"},
+            "decode": {"B": DB, "Hq": dw.Hq, "Hkv": dw.Hkv, "d": dw.d, "w": dw.w, "s": dw.s,
+                       "positions": [P, P + T - 1], "tokens_per_step": T, "hip_graph": True},
+        },
+        "prefill": {
+            "mean_launch_us": round(pre_mean * 1e3, 3),
+            "p10_us": round(pre_sorted[K // 10] * 1e3, 3),
+            "p90_us": round(pre_sorted[(9 * K) // 10] * 1e3, 3),
+            "useful_tflops": round(tflops, 3),
+            "frac_of_bf16_mfma_peak": round(tflops / acc.PEAK_BF16_TFLOPS, 5),
+            "executed_mfma_tflops": round(executed / (pre_mean * 1e-3) / 1e12, 3),
+            "useful_gflop_per_launch": round(useful / 1e9, 4),
+            "algorithmic_mb_per_launch": round(algo_bytes / 1e6, 3),
+        },
+        "decode": {
+            "tokens_per_s": round(dec_tokens_s, 1),
+            "us_per_token_step": round(dec_step_us, 3),
+            "kv_bytes_per_step": dec_kv_bytes,
+            "kv_gb_per_s": round(dec_gbs, 2),
+            "frac_of_hbm_peak": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
+            "note": "the 17.8 MB working set stays in the 256 MB Infinity Cache across steps",
+        },
+        "roofline": {
+            "kernel": "prefill_kernel<128>",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 2),
+            "peak": acc.PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / acc.PEAK_HBM_GBS, 5),
+            "traffic": traffic,
+        },
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
