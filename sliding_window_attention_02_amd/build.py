@@ -52,8 +52,19 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    check_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_stubs(path: str) -> None:
+    """Fail if a kernel's host launch stub is undefined (the host pass can drop it silently
+    when a device-only construct in the kernel does not type-check for the host)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", path], check=True, capture_output=True,
+                         text=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines() if "__device_stub__" in line]
+    if missing:
+        raise RuntimeError(f"{path}: undefined kernel launch stubs: {missing}")
 
 
 if __name__ == "__main__":

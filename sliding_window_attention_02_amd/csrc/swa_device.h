@@ -46,14 +46,36 @@ __device__ __forceinline__ TileWalk plan_tiles(int t0, int t1, int w_loc, int s,
     return tw;
 }
 
-// True when every (t, i) with t in [t0, t1] and i in the tile starting at j0 is allowed,
-// so the tile needs no element mask.
-__device__ __forceinline__ bool tile_mask_free(int j0, int tile_n, int t0, int t1, int w_loc, int s)
+// A tile is processed in chunks of kChunkN keys.  Sets [c_lo, c_hi], the smallest chunk
+// range that covers every chunk holding a key of A(t) for some t in [t0, t1] (the needed
+// keys of a q-tile are the sinks [0, min(s, t1+1)) and the window [max(0, t0-w_loc+1), t1]);
+// chunks outside the range are skipped, loads and exp alike.
+constexpr int kChunkN = 32;
+
+__device__ __forceinline__ void tile_chunks(int j0, int n_chunks, int t0, int t1, int w_loc, int s,
+                                            int &c_lo, int &c_hi)
 {
-    const int j1 = j0 + tile_n - 1;
-    const bool causal = j1 <= t0;
-    const bool in_window = j0 > t1 - w_loc;
-    const bool all_sinks = j1 < s;
+    const int lo = (t0 - w_loc + 1 > 0) ? t0 - w_loc + 1 : 0;
+    const int sink_end = s < t1 + 1 ? s : t1 + 1;
+    c_lo = n_chunks;
+    c_hi = -1;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int a = j0 + c * kChunkN, b = a + kChunkN - 1;
+        const bool need = a < sink_end || (b >= lo && a <= t1);
+        if (need) {
+            c_lo = c < c_lo ? c : c_lo;
+            c_hi = c;
+        }
+    }
+}
+
+// True when every (t, i) with t in [t0, t1] and i in [k_lo, k_hi] is allowed, so those
+// keys need no element mask.
+__device__ __forceinline__ bool range_mask_free(int k_lo, int k_hi, int t0, int t1, int w_loc, int s)
+{
+    const bool causal = k_hi <= t0;
+    const bool in_window = k_lo > t1 - w_loc;
+    const bool all_sinks = k_hi < s;
     return causal && (in_window || all_sinks);
 }
 

@@ -40,6 +40,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileN = 64;     // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves
@@ -58,15 +60,31 @@ struct PrefillArgs {
 
 template <int D>
 struct Lds {
-    static constexpr int kKStride = D + 8;       // bf16 per K row
-    static constexpr int kVStride = kTileN + 8;  // bf16 per V^T row
-    static constexpr int kKElems = kTileN * kKStride;
-    static constexpr int kVElems = D * kVStride;
+    static constexpr int kPieces = D / 8;                // 16-byte pieces per row
+    static constexpr int kRowBytes = D * 2;              // rows are unpadded
+    static constexpr int kTileBytes = kTileN * kRowBytes;
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 64-lane 16-byte load fills
+    static constexpr int kLoadsPerTile = kTileBytes / 1024;
 };
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// XOR swizzles of the 16-byte pieces of a row (physical piece = logical piece ^ swizzle).
+// K: the 16 rows one S^T fragment read touches (32*kc + 8a + 4h + b, a, b = 0..3) get 16
+// distinct swizzles, so the 16-byte reads of any 8 or 16 consecutive lanes hit distinct
+// bank groups.  V: the transposed 8-byte reads take rows r..r+3 (r = 0 mod 4) at pieces
+// P, P+1 (P even); swizzles 0, 2, 4, 6 spread them over 8 distinct pieces.
+template <int D>
+__device__ __forceinline__ int swz_k(int r)
+{
+    return D == 128 ? ((((r >> 3) & 3) << 2) | (r & 3)) : ((((r >> 3) & 1) << 2) | (r & 3));
+}
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// LDS pointer in the local address space, as the direct global -> LDS load takes it.  The
+// cast is written inline: an implicit conversion (or a helper function) there makes the host
+// pass drop the kernel's launch stub.
+#define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Maps the hardware workgroup id to (b, kv-head, head slice, q-tile).
 struct BlockCoord {
@@ -93,16 +111,17 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
-    constexpr int kChunks = D / 8;                           // 16-byte chunks per row
-    constexpr int kKSteps = D / 32;                          // MFMA k-steps for S
-    constexpr int kDBlocks = D / 16;                         // 16-row blocks of O^T
-    constexpr int kKUnits = kTileN * kChunks / kThreads;     // K chunks per thread
-    constexpr int kVUnits = (kTileN / 2) * kChunks / kThreads;  // V key-pair chunks per thread
-    constexpr int kKStride = Lds<D>::kKStride;
-    constexpr int kVStride = Lds<D>::kVStride;
+    constexpr int kPieces = Lds<D>::kPieces;
+    constexpr int kKSteps = D / 32;    // MFMA k-steps for S
+    constexpr int kDBlocks = D / 16;   // 16-row blocks of O^T
+    constexpr int kRowBytes = Lds<D>::kRowBytes;
+    constexpr int kTileBytes = Lds<D>::kTileBytes;
+    constexpr int kRowsPerLoad = Lds<D>::kRowsPerLoad;
+    constexpr int kLoadsPerWave = Lds<D>::kLoadsPerTile / (kThreads / 64);
+    static_assert(kLoadsPerWave >= 1, "tile load split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][Lds<D>::kKElems];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][Lds<D>::kVElems];
+    // Two buffers of (K tile, V tile), both row-major with swizzled 16-byte pieces.
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -113,6 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const BlockCoord bc = block_coord(a);
     const int t0 = bc.qt * a.Tm;
     const int t1 = min(t0 + a.Tm - 1, a.L - 1);
+    const float c = a.scale_log2;
 
     // This lane's query column in each of its two 16-column blocks.
     int tok[2], head[2];
@@ -136,162 +156,232 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         for (int kk = 0; kk < kKSteps; ++kk) {
             u32x4 x = {0u, 0u, 0u, 0u};
             if (valid[qb])
-                x = ld16(qrow + kk * 32 + g16 * 8);
+                x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qrow + kk * 32 + g16 * 8));
             qf[qb][kk] = as_bf16x8(x);
         }
     }
 
-    const size_t kv_row = (size_t)a.Hkv * D;  // elements between consecutive positions
+    const int kv_row = a.Hkv * D;  // elements between consecutive positions
     const uint16_t *kbase = a.k + ((size_t)bc.b * a.L * a.Hkv + bc.hkv) * D;
     const uint16_t *vbase = a.v + ((size_t)bc.b * a.L * a.Hkv + bc.hkv) * D;
 
-    const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
-    const int ntiles = tw.count();
+    // Direct global -> LDS loads: load j of a tile fills LDS bytes [1024 j, 1024 j + 1024),
+    // lane l the 16 bytes at 16 l: row kRowsPerLoad*j + l / kPieces, physical piece
+    // l % kPieces, which holds logical piece (physical ^ swizzle).  This wave issues loads
+    // j = wave*kLoadsPerWave .. +kLoadsPerWave-1.  Rows past the end of the sequence read the
+    // last row (finite values; such keys are always masked).
+    int ld_row[kLoadsPerWave], ld_kpiece[kLoadsPerWave], ld_vpiece[kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int j = wave * kLoadsPerWave + i;
+        ld_row[i] = kRowsPerLoad * j + lane / kPieces;
+        const int phys = lane % kPieces;
+        ld_kpiece[i] = phys ^ swz_k<D>(ld_row[i]);
+        ld_vpiece[i] = phys ^ swz_v(ld_row[i]);
+    }
+    auto issue_tile = [&](int j0, int buf) {
+        const int last = a.L - 1;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+            const int j = wave * kLoadsPerWave + i;
+            const int key = min(j0 + ld_row[i], last);
+            // (the builtin takes a non-const global pointer; the source is only read)
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(kbase + key * kv_row + ld_kpiece[i] * 8),
+                                             SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vbase + key * kv_row + ld_vpiece[i] * 8),
+                                             SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0, 0);
+        }
+    };
 
-    // Global -> register staging of one tile.
-    u32x4 kst[kKUnits];
-    u32x4 vst[kVUnits][2];
-    auto stage = [&](int jt) {
-        const int j0 = jt * kTileN;
+    // LDS read offsets (bytes, within a tile) that do not depend on the tile.
+    // K fragment (kc, h, kk): row 32kc + 8(c16/4) + 4h + c16%4, logical piece 4kk + g16.
+    int k_off[2][2][kKSteps];
 #pragma unroll
-        for (int u = 0; u < kKUnits; ++u) {
-            const int unit = tid + u * kThreads;
-            const int row = unit / kChunks, ch = unit % kChunks;
-            const int key = j0 + row;
-            kst[u] = u32x4{0u, 0u, 0u, 0u};
-            if (key < a.L)
-                kst[u] = ld16(kbase + (size_t)key * kv_row + ch * 8);
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = kc * kChunkN + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
+#pragma unroll
+            for (int kk = 0; kk < kKSteps; ++kk)
+                k_off[kc][h][kk] = row * kRowBytes + 16 * ((4 * kk + g16) ^ swz_k<D>(row));
         }
-#pragma unroll
-        for (int u = 0; u < kVUnits; ++u) {
-            const int unit = tid + u * kThreads;
-            const int kp = unit % (kTileN / 2), ch = unit / (kTileN / 2);
-            const int key = j0 + 2 * kp;
-            vst[u][0] = u32x4{0u, 0u, 0u, 0u};
-            vst[u][1] = u32x4{0u, 0u, 0u, 0u};
-            if (key < a.L)
-                vst[u][0] = ld16(vbase + (size_t)key * kv_row + ch * 8);
-            if (key + 1 < a.L)
-                vst[u][1] = ld16(vbase + (size_t)(key + 1) * kv_row + ch * 8);
-        }
-    };
-    // Register -> LDS: K row-major, V transposed with two keys packed per 32-bit word.
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < kKUnits; ++u) {
-            const int unit = tid + u * kThreads;
-            const int row = unit / kChunks, ch = unit % kChunks;
-            *reinterpret_cast<u32x4 *>(&lds_k[buf][row * kKStride + ch * 8]) = kst[u];
-        }
-#pragma unroll
-        for (int u = 0; u < kVUnits; ++u) {
-            const int unit = tid + u * kThreads;
-            const int kp = unit % (kTileN / 2), ch = unit / (kTileN / 2);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = vst[u][0][e >> 1], hi = vst[u][1][e >> 1];
-                const uint32_t packed = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                                : ((lo & 0xffffu) | (hi << 16));
-                *reinterpret_cast<uint32_t *>(&lds_v[buf][(ch * 8 + e) * kVStride + 2 * kp]) = packed;
-            }
-        }
-    };
+    // V^T fragment (db, kc) from two transposed 8-byte reads (h = 0, 1): lane 16g + s reads
+    // row 32kc + 8g + 4h + s/4 at d = 16db + 4(s%4) .. +3; the read hands lane s the values
+    // at d = 16db + s of the four rows 32kc + 8g + 4h .. +3.
+    const int vt_row0 = 8 * g16 + (c16 >> 2);  // + 32kc + 4h
+    const int vt_half = 8 * (c16 & 1);          // byte offset inside the 16-byte piece
+    const int vt_pbit = (c16 >> 1) & 1;         // which piece of the 2-piece column block
 
     f32x4 o[kDBlocks][2];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
         o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    // Softmax state per query column, in log2 units: the reference maximum m_ref the
+    // probabilities are taken against.  The running sum of the probabilities is computed
+    // by the matrix cores from the same bf16-rounded values that weight V: a constant
+    // A fragment whose row 0 is all ones turns one extra MFMA per chunk into
+    // lsum[0] += sum_k P^T[k][q] (lane group 0 holds it; the other rows are zero).  The
+    // dominant weight's rounding then cancels between numerator and denominator.
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const __bf16 one_or_zero = static_cast<__bf16>(c16 == 0 ? 1.f : 0.f);
+    const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
+                             one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
-    stage(tw.tile(0));
-    commit(0);
+    const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
+    const int ntiles = tw.count();
+
+    int j0 = tw.tile(0) * kTileN, c_lo, c_hi;
+    tile_chunks(j0, 2, t0, t1, a.w_loc, a.s, c_lo, c_hi);
+    issue_tile(j0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
 
     for (int n = 0; n < ntiles; ++n) {
         const int buf = n & 1;
-        const int j0 = tw.tile(n) * kTileN;
-        if (n + 1 < ntiles)
-            stage(tw.tile(n + 1));
+        const unsigned char *kt = lds[buf][0];
+        const unsigned char *vt = lds[buf][1];
+        int nj0 = 0, nc_lo = 2, nc_hi = -1;
+        if (n + 1 < ntiles) {
+            nj0 = tw.tile(n + 1) * kTileN;
+            tile_chunks(nj0, 2, t0, t1, a.w_loc, a.s, nc_lo, nc_hi);
+            issue_tile(nj0, buf ^ 1);
+        }
 
-        // S^T = K Q^T.  Row m of 16-key block kb holds key 32*(kb/2) + 8*(m/4) + 4*(kb%2) + m%4.
-        f32x4 sacc[4][2];
+        // S^T = K Q^T over the needed chunks.  Row m of 16-key block (kc, h) holds key
+        // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
+        f32x4 sacc[2][2][2];  // [kc][h][qb]
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sacc[kb][0] = sacc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int krow = 32 * (kb >> 1) + 8 * (c16 >> 2) + 4 * (kb & 1) + (c16 & 3);
+        for (int kc = 0; kc < 2; ++kc) {
+            if (kc < c_lo || kc > c_hi)
+                continue;
 #pragma unroll
-            for (int kk = 0; kk < kKSteps; ++kk) {
-                const bf16x8 af =
-                    *reinterpret_cast<const bf16x8 *>(&lds_k[buf][krow * kKStride + kk * 32 + g16 * 8]);
+            for (int h = 0; h < 2; ++h) {
+                sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sacc[kb][qb], 0, 0, 0);
+                for (int kk = 0; kk < kKSteps; ++kk) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(kt + k_off[kc][h][kk]);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        sacc[kc][h][qb] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sacc[kc][h][qb], 0, 0, 0);
+                }
             }
         }
 
-        // Element mask on edge tiles only, then the online softmax update per query column.
-        const bool mask_free = tile_mask_free(j0, kTileN, t0, t1, a.w_loc, a.s);
-        bf16x8 pf[2][2];  // [kc][qb]: P^T B-operand fragments
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float sv[4][4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float x = sacc[kb][qb][j] * a.scale_log2;
-                    if (!mask_free) {
-                        const int key = j0 + 32 * (kb >> 1) + 8 * g16 + 4 * (kb & 1) + j;
-                        if (!key_allowed(tok[qb], key, a.w_loc, a.s))
-                            x = -INFINITY;
-                    }
-                    sv[kb][j] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[qb], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-            m_run[qb] = m_new;
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(sv[kb][j] - m_use);
-                    psum += p;
-                    pf[kb >> 1][qb][4 * (kb & 1) + j] = static_cast<__bf16>(p);
-                }
-            l_run[qb] = l_run[qb] * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db)
-                o[db][qb] *= alpha;
-        }
-
-        // O^T += V^T P^T.
-#pragma unroll
-        for (int db = 0; db < kDBlocks; ++db)
+        // Element mask, only when some visited (query, key) pair is outside A(t).
+        const bool mask_free =
+            range_mask_free(j0 + c_lo * kChunkN, j0 + c_hi * kChunkN + kChunkN - 1, t0, t1, a.w_loc, a.s);
+        if (!mask_free) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(
-                    &lds_v[buf][(db * 16 + c16) * kVStride + 32 * kc + 8 * g16]);
+                if (kc < c_lo || kc > c_hi)
+                    continue;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int key = j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
+                            const int t = tok[qb];
+                            const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
+                            sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
+                        }
+            }
+        }
+
+        // Online softmax with lazy rescaling: the reference maximum only moves (and O and the
+        // sums are rescaled) when the column maximum exceeds it by more than 8 in log2 units,
+        // so the probabilities stay below 256 and most tiles skip the rescale.
+        bf16x8 pf[2][2];  // [kc][qb]: P^T B-operand fragments
+        float alpha[2];
+        bool grow_any = false;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                if (kc < c_lo || kc > c_hi)
+                    continue;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    mx = fmaxf(mx, fmaxf(fmaxf(sacc[kc][h][qb][0], sacc[kc][h][qb][1]),
+                                         fmaxf(sacc[kc][h][qb][2], sacc[kc][h][qb][3])));
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_tile = mx * c;
+            const bool grow = m_tile > m_ref[qb] + 8.f;
+            alpha[qb] = 1.f;
+            if (grow) {
+                alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - m_tile);
+                m_ref[qb] = m_tile;
+            }
+            grow_any |= grow;
+            const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                if (kc < c_lo || kc > c_hi)
+                    continue;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pf[kc][qb][4 * h + j] =
+                            static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc][h][qb][j], c, -m_use)));
+            }
+        }
+        if (__any(grow_any)) {
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                o[db][0] *= alpha[0];
+                o[db][1] *= alpha[1];
+            }
+            lsum[0] *= alpha[0];
+            lsum[1] *= alpha[1];
+        }
+
+        // O^T += V^T P^T over the needed chunks, and the probability sums.
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            if (kc < c_lo || kc > c_hi)
+                continue;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[kc][qb], lsum[qb], 0, 0, 0);
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                bf16x8 af;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = kc * kChunkN + 4 * h + vt_row0;
+                    const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ swz_v(row)) + vt_half;
+                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vt + off));
+                    const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+                    af[4 * h + 0] = y[0];
+                    af[4 * h + 1] = y[1];
+                    af[4 * h + 2] = y[2];
+                    af[4 * h + 3] = y[3];
+                }
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
                     o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[kc][qb], o[db][qb], 0, 0, 0);
             }
+        }
 
-        if (n + 1 < ntiles)
-            commit(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
         __syncthreads();
+        j0 = nj0;
+        c_lo = nc_lo;
+        c_hi = nc_hi;
     }
 
     // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        float l = l_run[qb];
+        float l = lsum[qb][0];  // non-zero in lane group 0 only
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         const float inv = 1.f / l;
@@ -299,13 +389,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             float *orow = a.out + (((size_t)bc.b * a.L + tok[qb]) * a.Hq + head[qb]) * D;
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db)
-                *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db][qb] * inv;
+                __builtin_nontemporal_store(o[db][qb] * inv, reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4));
         }
     }
 }
 
 // Debug: the set of (query, key) pairs the prefill kernel admits, from the same tile walk,
-// tile classification and element predicate.  One workgroup per q-tile.
+// chunk selection, mask-free classification and element predicate.  One workgroup per q-tile.
 __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int w_loc, int s)
 {
     const int t0 = blockIdx.x * Tm;
@@ -313,10 +403,14 @@ __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int w_lo
     const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
     for (int n = 0; n < tw.count(); ++n) {
         const int j0 = tw.tile(n) * kTileN;
-        const bool mask_free = tile_mask_free(j0, kTileN, t0, t1, w_loc, s);
-        for (int idx = threadIdx.x; idx < Tm * kTileN; idx += blockDim.x) {
-            const int t = t0 + idx / kTileN;
-            const int key = j0 + idx % kTileN;
+        int c_lo, c_hi;
+        tile_chunks(j0, kTileN / kChunkN, t0, t1, w_loc, s, c_lo, c_hi);
+        const int k_lo = j0 + c_lo * kChunkN, k_hi = j0 + c_hi * kChunkN + kChunkN - 1;
+        const bool mask_free = range_mask_free(k_lo, k_hi, t0, t1, w_loc, s);
+        const int width = k_hi - k_lo + 1;
+        for (int idx = threadIdx.x; idx < Tm * width; idx += blockDim.x) {
+            const int t = t0 + idx / width;
+            const int key = k_lo + idx % width;
             if (t > t1 || key >= L)
                 continue;
             if (mask_free || key_allowed(t, key, w_loc, s))
