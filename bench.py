@@ -7,11 +7,12 @@ One step = one pass of the whole hot path over one batch of synthetic input:
     d=128), each token one swa_kv_append + swa_decode_step, positions 2^18 .. 2^18+255,
     captured once in a HIP graph and replayed.
 Inputs are resident in HBM before the timed region.  The timed region is bracketed by
-torch.cuda.synchronize(); HIP events on the launch stream time every prefill launch and
-every decode replay inside it.
+torch.cuda.synchronize(); inside it, each prefill kernel stamps a pair of HIP events with
+its own start and end (swa_prefill_timed), and HIP events on the stream bracket every
+decode replay.
 
 Printed JSON line (one):
-  value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill launch time
+  value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time
   decode           tokens/s of the decode leg and its HBM figures
   roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
                    launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
@@ -185,10 +186,10 @@ def main():
         graph.replay()
         if evs is not None:
             evs[3][i].record()
-            evs[0][i].record()
-        swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out)
-        if evs is not None:
-            evs[1][i].record()
+            # The prefill kernel's dispatch stamps its own start/end into these events.
+            swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out, events=(evs[0][i], evs[1][i]))
+        else:
+            swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -196,6 +197,8 @@ def main():
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(4)]
+    for e in evs[0] + evs[1]:
+        e.record()  # creates the underlying HIP events, which the timed launches then stamp
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):

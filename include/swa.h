@@ -74,6 +74,17 @@ int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, 
                 int L, int d, int w, int s, float scale, int conv, void *stream);
 
 /*
+ * swa_prefill_timed -- swa_prefill that also stamps two caller-created HIP events
+ * (hipEvent_t, created with timing enabled) with the start and the end of the prefill
+ * kernel itself (hipExtLaunchKernel), for callers that time the kernel rather than the
+ * stream interval around it.  Same arguments, layout and errors as swa_prefill, plus
+ * SWA_EINVAL if either event is null.
+ */
+int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv,
+                      int L, int d, int w, int s, float scale, int conv, void *stream,
+                      void *start_event, void *stop_event);
+
+/*
  * swa_kv_append -- write new tokens' keys and values into the bounded decode cache.
  *
  * Cache layout (per batch b and kv-head): s pinned sink slots followed by a ring of

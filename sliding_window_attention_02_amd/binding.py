@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 EXPORTS = (
     "swa_prefill",
+    "swa_prefill_timed",
     "swa_kv_append",
     "swa_decode_workspace_bytes",
     "swa_decode_step",
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
     i32, vp, f32, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     L.swa_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.swa_prefill.restype = i32
+    L.swa_prefill_timed.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+    L.swa_prefill_timed.restype = i32
     L.swa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.swa_kv_append.restype = i32
     L.swa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -103,8 +106,13 @@ def local_window(w: int, s: int, conv: int = ADDITIVE) -> int:
     return wl
 
 
-def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADDITIVE, out=None):
-    """SWA(w,s) prefill.  q bf16 [B][L][Hq][d], k/v bf16 [B][L][Hkv][d] -> fp32 [B][L][Hq][d]."""
+def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADDITIVE, out=None,
+            events=None):
+    """SWA(w,s) prefill.  q bf16 [B][L][Hq][d], k/v bf16 [B][L][Hkv][d] -> fp32 [B][L][Hq][d].
+
+    events: optional (start, stop) torch.cuda.Event pair (timing enabled, already recorded
+    once so the underlying HIP events exist); the kernel dispatch stamps them with its own
+    start and end (swa_prefill_timed)."""
     if q.dim() != 4:
         raise ValueError("q must be [B][L][Hq][d]")
     B, L, Hq, d = q.shape
@@ -116,8 +124,13 @@ def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADD
         out = torch.empty((B, L, Hq, d), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (B, L, Hq, d))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib().swa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, d,
-                             w, s, scale, conv, _stream(q)))
+    if events is None:
+        _check(lib().swa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, d,
+                                 w, s, scale, conv, _stream(q)))
+    else:
+        start, stop = events
+        _check(lib().swa_prefill_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, L,
+                                       d, w, s, scale, conv, _stream(q), start.cuda_event, stop.cuda_event))
     return out
 
 

@@ -3,7 +3,7 @@
 // Every entry point validates its arguments on the host before touching HIP, resolves
 // the window convention to the local window w_loc, and enqueues kernels on the caller's
 // stream.  Nothing here allocates, frees or synchronises device memory.
-#include "../../include/swa.h"
+#include "swa.h"
 #include "swa_launch.h"
 
 #include <hip/hip_runtime.h>
@@ -90,14 +90,11 @@ int hip_status(const char *fn, hipError_t e)
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char *swa_last_error(void) { return g_last_error.c_str(); }
-
-int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv, int L,
-                int d, int w, int s, float scale, int conv, void *stream)
+int prefill_impl(const char *fn, const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv,
+                 int L, int d, int w, int s, float scale, int conv, void *stream, void *start, void *stop)
 {
-    const char *fn = "swa_prefill";
     CHECK_PTR(q);
     CHECK_PTR(k);
     CHECK_PTR(v);
@@ -115,7 +112,32 @@ int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, 
     if ((long long)L * Hq * d > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: one sequence of q holds more than 2^31-1 elements", fn);
     return hip_status(fn, swa::launch_prefill(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale,
-                                              static_cast<hipStream_t>(stream)));
+                                              static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start),
+                                              static_cast<hipEvent_t>(stop)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *swa_last_error(void) { return g_last_error.c_str(); }
+
+
+int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv, int L,
+                int d, int w, int s, float scale, int conv, void *stream)
+{
+    return prefill_impl("swa_prefill", q, k, v, out, B, Hq, Hkv, L, d, w, s, scale, conv, stream, nullptr,
+                        nullptr);
+}
+
+int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv, int L,
+                      int d, int w, int s, float scale, int conv, void *stream, void *start_event,
+                      void *stop_event)
+{
+    if (start_event == nullptr || stop_event == nullptr)
+        return fail(SWA_EINVAL, "swa_prefill_timed: start_event and stop_event must not be null");
+    return prefill_impl("swa_prefill_timed", q, k, v, out, B, Hq, Hkv, L, d, w, s, scale, conv, stream,
+                        start_event, stop_event);
 }
 
 int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int64_t *pos,

@@ -20,8 +20,10 @@ struct PrefillGeometry {
 };
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
 
+// start/stop: optional events stamped by the kernel dispatch itself (null: plain launch).
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
-                          int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream);
+                          int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w_loc, int s,
                                      hipStream_t stream);

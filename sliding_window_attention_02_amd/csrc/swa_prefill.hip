@@ -32,6 +32,7 @@
 #include "swa_device.h"
 #include "swa_launch.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace swa {
@@ -389,7 +390,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             float *orow = a.out + (((size_t)bc.b * a.L + tok[qb]) * a.Hq + head[qb]) * D;
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db)
-                __builtin_nontemporal_store(o[db][qb] * inv, reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4));
+                // Plain stores: L2 merges the 64-byte pieces of a row into whole lines
+                // (non-temporal stores here cost 1.5x the output bytes in HBM writes).
+                *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db][qb] * inv;
         }
     }
 }
@@ -444,7 +447,8 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
 }
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
-                          int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream)
+                          int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop)
 {
     const PrefillGeometry g = prefill_geometry(L, Hq, Hkv);
     PrefillArgs a;
@@ -467,10 +471,16 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    if (d == 128)
+    if (start != nullptr || stop != nullptr) {
+        if (d == 128)
+            hipExtLaunchKernelGGL(prefill_kernel<128>, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL(prefill_kernel<64>, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
+    } else if (d == 128) {
         hipLaunchKernelGGL(prefill_kernel<128>, dim3(a.nblocks), dim3(kThreads), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL(prefill_kernel<64>, dim3(a.nblocks), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -124,3 +124,10 @@ def test_local_window_matches_convention():
     assert binding.local_window(64, 4, binding.TOTAL) == 60
     with pytest.raises(ValueError):
         binding.local_window(4, 4, binding.TOTAL)
+
+
+def test_prefill_timed_requires_events(lib):
+    f = lib.swa_prefill_timed
+    assert f(A, A, A, A, 1, 4, 2, 16, 128, 8, 4, 0.1, 0, None, None, A) == binding.SWA_EINVAL
+    assert "event" in err(lib)
+    assert f(A, A, A, A, 0, 4, 2, 16, 128, 8, 4, 0.1, 0, None, A, A) == binding.SWA_EINVAL

@@ -176,3 +176,15 @@ def test_prefill_on_a_side_stream():
         out = swa.prefill(q, k, v, 32, 4)
     s.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_timed_prefill_matches_and_stamps_kernel_time():
+    q, k, v = [t.cuda() for t in inputs.random_qkv(1, 1024, 32, 8, 128, seed=12, sink_boost_n=4, sink_boost=4.0)]
+    ref = swa.prefill(q, k, v, 64, 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    out = swa.prefill(q, k, v, 64, 4, events=(e0, e1))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert e0.elapsed_time(e1) > 0
