@@ -4,7 +4,8 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * prefill of the Llama-3.1-8B-shaped SWA(64,4) workload (B=1, L=4096, Hq=32, Hkv=8,
     d=128, bf16 inputs N(0,1)*0.5, sink keys x4, fp32 output), one swa_prefill launch;
   * 256 decode tokens of the SWA(64,4) ring-cache workload at batch 64 (Hq=32, Hkv=8,
-    d=128), each token one swa_kv_append + swa_decode_step, positions 2^18 .. 2^18+255,
+    d=128), each token one swa_append_decode_step (append + attend in one launch), positions
+    2^18 .. 2^18+255,
     captured once in a HIP graph and replayed.
 Inputs are resident in HBM before the timed region.  The timed region is bracketed by
 torch.cuda.synchronize(); inside it, each prefill kernel stamps a pair of HIP events with
@@ -150,8 +151,8 @@ def main():
                   torch.full((DB,), P - dw_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
     dq = torch.stack([inputs.q_at(dw.seed, P + i, DB, dw.Hq, dw.d, dw.std) for i in range(T)]).to(dev)
     kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(T)]
-    dk = torch.stack([x[0][:, None] for x in kvs]).to(dev)  # [T][B][1][Hkv][d]
-    dv = torch.stack([x[1][:, None] for x in kvs]).to(dev)
+    dk = torch.stack([x[0] for x in kvs]).to(dev)  # [T][B][Hkv][d]
+    dv = torch.stack([x[1] for x in kvs]).to(dev)
     dpos = (P + torch.arange(T, dtype=torch.int64)).repeat_interleave(DB).view(T, DB).to(dev)
     dout = torch.empty((T, DB, dw.Hq, dw.d), dtype=torch.float32, device=dev)
     # The graph replays T append+attend steps.  The cache is restored to the state after
@@ -159,9 +160,10 @@ def main():
     snap_k, snap_v = kc.clone(), vc.clone()
 
     def decode_steps():
+        # One launch per token: append the new K/V to its slot and attend (swa_append_decode_step).
         for i in range(T):
-            swa.kv_append(kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.conv)
-            swa.decode_step(dq[i], kc, vc, dpos[i], dw.w, dw.s, dw.scale, dw.conv, out=dout[i], workspace=ws)
+            swa.append_decode_step(dq[i], kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.scale, dw.conv,
+                                   out=dout[i], workspace=ws)
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())

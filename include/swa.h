@@ -136,6 +136,19 @@ int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, flo
                     const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s, float scale,
                     int conv, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * swa_append_decode_step -- swa_kv_append of one token per sequence followed by
+ * swa_decode_step, in one launch.  The new token k_new[b], v_new[b] (bf16 [B][Hkv][d], the
+ * token at position pos[b]) is written to its slot and attended directly from k_new/v_new;
+ * every other slot is read from the cache.  Results, and the cache contents afterwards, are
+ * identical to the two-call sequence.  Same arguments and errors as swa_decode_step, plus
+ * SWA_EINVAL for null or misaligned k_new / v_new.  The caches are written.
+ */
+int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const void *k_new,
+                           const void *v_new, float *out, const int64_t *pos, int B, int Hq,
+                           int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char *swa_last_error(void);
 

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SwaError,
     alloc_cache,
     alloc_workspace,
+    append_decode_step,
     debug_decode_slots,
     debug_prefill_mask,
     decode_step,

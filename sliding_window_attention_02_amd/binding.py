@@ -29,6 +29,7 @@ EXPORTS = (
     "swa_kv_append",
     "swa_decode_workspace_bytes",
     "swa_decode_step",
+    "swa_append_decode_step",
     "swa_last_error",
     "swa_debug_prefill_mask",
     "swa_debug_decode_slots",
@@ -62,6 +63,9 @@ def lib() -> ctypes.CDLL:
     L.swa_decode_workspace_bytes.restype = sz
     L.swa_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.swa_decode_step.restype = i32
+    L.swa_append_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz,
+                                         vp]
+    L.swa_append_decode_step.restype = i32
     L.swa_last_error.argtypes = []
     L.swa_last_error.restype = ctypes.c_char_p
     L.swa_debug_prefill_mask.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
@@ -185,6 +189,32 @@ def decode_step(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = 
     _check(lib().swa_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                  pos.data_ptr(), B, Hq, Hkv, d, w, s, scale, conv, ws_ptr or None, ws_bytes,
                                  _stream(q)))
+    return out
+
+
+def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, scale: float | None = None,
+                       conv: int = ADDITIVE, out=None, workspace=None):
+    """kv_append of one token per sequence (k_new/v_new bf16 [B][Hkv][d] at positions pos[b])
+    and decode_step for the query at that position, in one launch -> fp32 [B][Hq][d]."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, d))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, d))
+    _need(pos, "pos", torch.int64, (B,))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, d))
+    need = decode_workspace_bytes(B, Hq, Hkv, d, w, s, conv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_append_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                                        v_new.data_ptr(), out.data_ptr(), pos.data_ptr(), B, Hq, Hkv, d, w, s, scale,
+                                        conv, ws_ptr or None, ws_bytes, _stream(q)))
     return out
 
 

@@ -118,6 +118,43 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
 
 }  // namespace
 
+namespace {
+
+int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache, const void *k_new,
+                const void *v_new, float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,
+                float scale, int conv, void *workspace, size_t workspace_bytes, void *stream)
+{
+    CHECK_PTR(q);
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    CHECK_PTR(out);
+    if (pos == nullptr)
+        return fail(SWA_EINVAL, "%s: pos is null", fn);
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((rc = check_scale(fn, scale)))
+        return rc;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    if (plan.workspace_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+            return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, plan.workspace_bytes,
+                        workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if (!aligned16(workspace))
+            return fail(SWA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, swa::launch_decode(q, const_cast<void *>(k_cache), const_cast<void *>(v_cache), k_new,
+                                             v_new, out, pos, B, Hq, Hkv, d, w_loc, s, scale, workspace, plan,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *swa_last_error(void) { return g_last_error.c_str(); }
@@ -177,37 +214,24 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, i
     return swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes;
 }
 
+
 int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, float *out, const int64_t *pos,
                     int B, int Hq, int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
                     size_t workspace_bytes, void *stream)
 {
-    const char *fn = "swa_decode_step";
-    CHECK_PTR(q);
-    CHECK_PTR(k_cache);
-    CHECK_PTR(v_cache);
-    CHECK_PTR(out);
-    if (pos == nullptr)
-        return fail(SWA_EINVAL, "%s: pos is null", fn);
-    int rc = check_heads(fn, B, Hq, Hkv, d);
-    if (rc)
-        return rc;
-    int w_loc = 0;
-    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
-        return rc;
-    if ((rc = check_scale(fn, scale)))
-        return rc;
-    if ((long long)s + w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
-    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
-    if (plan.workspace_bytes > 0) {
-        if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
-            return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, plan.workspace_bytes,
-                        workspace == nullptr ? (size_t)0 : workspace_bytes);
-        if (!aligned16(workspace))
-            return fail(SWA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
-    }
-    return hip_status(fn, swa::launch_decode(q, k_cache, v_cache, out, pos, B, Hq, Hkv, d, w_loc, s, scale,
-                                             workspace, plan, static_cast<hipStream_t>(stream)));
+    return decode_impl("swa_decode_step", q, k_cache, v_cache, nullptr, nullptr, out, pos, B, Hq, Hkv, d, w, s,
+                       scale, conv, workspace, workspace_bytes, stream);
+}
+
+int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                           float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,
+                           float scale, int conv, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "swa_append_decode_step";
+    CHECK_PTR(k_new);
+    CHECK_PTR(v_new);
+    return decode_impl(fn, q, k_cache, v_cache, k_new, v_new, out, pos, B, Hq, Hkv, d, w, s, scale, conv,
+                       workspace, workspace_bytes, stream);
 }
 
 int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, int conv, void *stream)

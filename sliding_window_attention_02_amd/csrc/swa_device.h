@@ -91,19 +91,32 @@ __device__ __forceinline__ int64_t append_slot(int64_t p, int s, int w_loc)
     return p < s ? p : s + (p % w_loc);
 }
 
-// Position held by slot j when the latest appended position is t, or -1 when the slot
-// holds nothing in A(t) (a sink slot beyond t, or a ring slot whose latest position
-// would be a sink or negative).
-__device__ __forceinline__ int64_t slot_position(int j, int64_t t, int s, int w_loc)
-{
-    if (j < s)
-        return (int64_t)j <= t ? (int64_t)j : -1;
-    const int64_t r = j - s;
-    int64_t back = (t - r) % w_loc;
-    if (back < 0)
-        back += w_loc;
-    const int64_t p = t - back;
-    return (p >= s && p >= 0) ? p : -1;
-}
+// Slot -> position map for a query at position t (the latest appended position): slot j
+// holds position(j), or -1 when the slot holds nothing in A(t) (a sink slot beyond t, or a
+// ring slot whose latest position would be a sink or negative).  The one 64-bit modulo is
+// taken at construction; position() is 32-bit arithmetic plus one 64-bit subtraction.
+struct SlotMap {
+    int64_t t;
+    int s, w_loc, t_mod;
+    __device__ __forceinline__ SlotMap(int64_t t_, int s_, int w_loc_)
+        : t(t_), s(s_), w_loc(w_loc_), t_mod(t_ >= 0 ? (int)(t_ % w_loc_) : 0)
+    {
+    }
+    __device__ __forceinline__ int64_t position(int j) const
+    {
+        if (j < s)
+            return (int64_t)j <= t ? (int64_t)j : -1;
+        // ring slot r = j - s holds the latest p <= t with p = r (mod w_loc):
+        // p = t - ((t - r) mod w_loc) and (t - r) mod w_loc = (t_mod - r) mod w_loc
+        int back = t_mod - (j - s);
+        if (back < 0)
+            back += w_loc;
+        const int64_t p = t - back;
+        return (p >= s && p >= 0) ? p : -1;
+    }
+    __device__ __forceinline__ bool valid(int j) const { return position(j) >= 0; }
+    // slot of position t itself (t >= 0)
+    __device__ __forceinline__ int slot_of_t() const { return t < s ? (int)t : s + t_mod; }
+};
 
 }  // namespace swa

@@ -31,7 +31,7 @@ hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int 
 // ------------------------------------------------------------------------------ decode
 struct DecodePlan {
     int n_slots;          // s + w_loc
-    int Gb;               // q-heads per workgroup (largest divisor of G that is <= 8)
+    int Gb;               // q-heads per workgroup (largest divisor of G that is <= 16)
     int n_hslices;        // G / Gb
     int n_split;          // workgroups over the slot range of one (b, kv-head, head slice)
     int slots_per_split;  // slots per split
@@ -43,8 +43,10 @@ hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, con
                             const int64_t *pos, int B, int Hkv, int d, int w_loc, int s, int n_new,
                             hipStream_t stream);
 
-hipError_t launch_decode(const void *q, const void *k_cache, const void *v_cache, float *out,
-                         const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
+// k_new / v_new: null for a plain decode step; otherwise the new token of each sequence
+// ([B][Hkv][d]) is written to its slot and attended in the same launch.
+hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                         float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
                          float scale, void *workspace, const DecodePlan &plan, hipStream_t stream);
 
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,

@@ -131,3 +131,11 @@ def test_prefill_timed_requires_events(lib):
     assert f(A, A, A, A, 1, 4, 2, 16, 128, 8, 4, 0.1, 0, None, None, A) == binding.SWA_EINVAL
     assert "event" in err(lib)
     assert f(A, A, A, A, 0, 4, 2, 16, 128, 8, 4, 0.1, 0, None, A, A) == binding.SWA_EINVAL
+
+
+def test_append_decode_step_rejects_on_host(lib):
+    f = lib.swa_append_decode_step
+    assert f(A, A, A, None, A, A, A, 64, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EINVAL
+    assert "k_new is null" in err(lib)
+    assert f(A, A, A, A, MIS, A, A, 64, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EINVAL
+    assert f(A, A, A, A, A, A, A, 64, 32, 8, 96, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EUNSUPPORTED

@@ -190,3 +190,27 @@ def test_decode_is_deterministic(B, Hq, Hkv, d, w, s):
     a = swa.decode_step(q, kc, vc, pos, w, s)
     b = swa.decode_step(q, kc, vc, pos, w, s)
     assert torch.equal(a, b) and torch.isfinite(a).all()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv", [(64, 32, 8, 128, 64, 4, 0), (1, 32, 8, 128, 64, 4, 0),
+                                                 (3, 8, 2, 64, 9, 3, 1), (2, 16, 1, 128, 300, 4, 0)])
+def test_fused_append_decode_equals_two_calls(B, Hq, Hkv, d, w, s, conv):
+    """swa_append_decode_step = swa_kv_append + swa_decode_step, outputs and cache bit for bit,
+    from an empty cache through ring wrap-around."""
+    say("fused", B, Hq, Hkv, d, w, s, conv)
+    w_loc = orc.local_window(w, s, conv)
+    T = w_loc + s + 40
+    g = torch.Generator().manual_seed(17)
+    qs = torch.randn(T, B, Hq, d, generator=g).to(torch.bfloat16).cuda()
+    ks = torch.randn(T, B, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    vs = torch.randn(T, B, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    kc1, vc1 = swa.alloc_cache(B, Hkv, d, w, s, conv)
+    kc2, vc2 = swa.alloc_cache(B, Hkv, d, w, s, conv)
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s, conv)
+    for t in range(T):
+        pos = gpos([t] * B)
+        swa.kv_append(kc1, vc1, ks[t][:, None].contiguous(), vs[t][:, None].contiguous(), pos, w, s, conv)
+        a = swa.decode_step(qs[t], kc1, vc1, pos, w, s, None, conv, workspace=ws)
+        b = swa.append_decode_step(qs[t], kc2, vc2, ks[t], vs[t], pos, w, s, None, conv, workspace=ws)
+        assert torch.equal(a, b), t
+    assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
