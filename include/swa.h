@@ -157,15 +157,15 @@ const char *swa_last_error(void);
  * same device functions as the hot kernels.
  *
  * swa_debug_prefill_mask: mask uint8 [L][L] device (out).  mask[t][i] = 1 iff the
- * prefill kernel's tile walk for the tile holding query t visits key i and either
- * classifies the tile as mask-free or its element predicate admits (t, i).  Requires
- * L <= 8192.
+ * prefill kernel that swa_prefill would launch for (L, Hq, Hkv, d, w, s, conv) visits key i
+ * for the tile holding query t and either classifies those keys as mask-free or its element
+ * predicate admits (t, i).  Requires L <= 8192.
  *
  * swa_debug_decode_slots: slot_pos int64 [B][s + w_loc] device (out): the position the
  * decode kernel reads from each slot for query position pos[b], or -1 if the slot is
  * skipped.
  */
-int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, int conv,
+int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w, int s, int conv,
                            void *stream);
 int swa_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w, int s, int conv,
                            void *stream);

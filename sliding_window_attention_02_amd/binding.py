@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
     L.swa_append_decode_step.restype = i32
     L.swa_last_error.argtypes = []
     L.swa_last_error.restype = ctypes.c_char_p
-    L.swa_debug_prefill_mask.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
+    L.swa_debug_prefill_mask.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.swa_debug_prefill_mask.restype = i32
     L.swa_debug_decode_slots.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     L.swa_debug_decode_slots.restype = i32
@@ -218,10 +218,10 @@ def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, s
     return out
 
 
-def debug_prefill_mask(L: int, Hq: int, Hkv: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
-    """uint8 [L][L]: the (query, key) pairs the prefill kernel's tile walk admits."""
+def debug_prefill_mask(L: int, Hq: int, Hkv: int, w: int, s: int, conv: int = ADDITIVE, device="cuda", d: int = 128):
+    """uint8 [L][L]: the (query, key) pairs the prefill kernel for these arguments admits."""
     m = torch.empty((L, L), dtype=torch.uint8, device=device)
-    _check(lib().swa_debug_prefill_mask(m.data_ptr(), L, Hq, Hkv, w, s, conv, _stream(m)))
+    _check(lib().swa_debug_prefill_mask(m.data_ptr(), L, Hq, Hkv, d, w, s, conv, _stream(m)))
     return m
 
 

@@ -234,12 +234,12 @@ int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const vo
                        workspace, workspace_bytes, stream);
 }
 
-int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, int conv, void *stream)
+int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w, int s, int conv, void *stream)
 {
     const char *fn = "swa_debug_prefill_mask";
     if (mask == nullptr)
         return fail(SWA_EINVAL, "%s: mask is null", fn);
-    int rc = check_heads(fn, 1, Hq, Hkv, 64);
+    int rc = check_heads(fn, 1, Hq, Hkv, d);
     if (rc)
         return rc;
     if (L < 1 || L > 8192)
@@ -247,7 +247,7 @@ int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w, int s, 
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
         return rc;
-    return hip_status(fn, swa::launch_debug_prefill_mask(mask, L, Hq, Hkv, w_loc, s,
+    return hip_status(fn, swa::launch_debug_prefill_mask(mask, L, Hq, Hkv, d, w_loc, s,
                                                          static_cast<hipStream_t>(stream)));
 }
 

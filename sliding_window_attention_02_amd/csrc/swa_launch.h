@@ -14,7 +14,7 @@ namespace swa {
 struct PrefillGeometry {
     int G;          // q-heads per kv-head
     int Gw;         // q-heads per workgroup (largest divisor of G that is <= 4)
-    int Tm;         // tokens per workgroup (128 / Gw)
+    int Tm;         // tokens per workgroup (rows / Gw)
     int n_hslices;  // G / Gw
     int n_qtiles;   // ceil(L / Tm)
 };
@@ -25,7 +25,7 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
-hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w_loc, int s,
+hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w_loc, int s,
                                      hipStream_t stream);
 
 // ------------------------------------------------------------------------------ decode

@@ -17,23 +17,27 @@
 // so each lane ends up with the scores of ONE query column for a few keys; the
 // probabilities P^T then already sit in the B-operand layout of
 //     O^T (d x queries) += V^T (d x keys) . P^T (keys x queries)
-// and the per-query softmax statistics (max, sum) never leave the lane group.  The
-// 16-key row blocks of S^T are assigned keys so that lane group g of the PV product
-// sees the 8 consecutive keys 32*kc + 8g .. 32*kc + 8g + 7, which V^T in LDS serves
-// with one 16-byte read.  Any k-ordering the hardware uses inside the 8-value groups
-// is the same for A and B, so the contraction is exact regardless.
+// and the per-query softmax statistics (max, sum) only combine the four lanes
+// l % 16 + 16g that share a column.  The 16-key row blocks of S^T are assigned keys so
+// that lane group g of the PV product sees the 8 consecutive keys 32*kc + 8g .. +7, which
+// two transposed 8-byte LDS reads of row-major V deliver as the V^T A operand.  Any
+// k-ordering the hardware uses inside the 8-value groups is the same for A and B, so the
+// contraction is exact regardless.
 //
-// Memory: K and V tiles of 64 keys are staged global -> registers -> LDS with double
-// buffering (one barrier per tile).  K is stored row-major with a 16-byte row pad
-// (conflict-free 16-byte reads of 16 rows); V is stored transposed (V^T, row = d) with
-// a 16-byte pad.  Q stays in registers for the whole key loop.  Workgroups are ordered
-// heavy-first (last q-tile first) and mapped so that consecutive logical workgroups share
-// an XCD and its L2, where neighbouring q-tiles re-read the same K/V tiles.
+// Memory: K and V tiles of 64 keys go from global memory straight into LDS (direct
+// global -> LDS loads, double-buffered, one barrier per tile), both row-major with the
+// 16-byte pieces of each row XOR-swizzled so that the K fragment reads and the transposed
+// V reads (ds_read_b64_tr_b16) are free of bank conflicts.  Q stays in registers for the
+// whole key loop.  Workgroups are ordered heavy-first (last q-tile first) and mapped so
+// that consecutive logical workgroups share an XCD and its L2, where neighbouring q-tiles
+// re-read the same K/V tiles.
 #include "swa_device.h"
 #include "swa_launch.h"
 
 #include <hip/hip_ext.h>
 #include <math.h>
+
+#include <type_traits>
 
 namespace swa {
 namespace {
@@ -80,7 +84,23 @@ __device__ __forceinline__ int swz_k(int r)
 }
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
+// Maximum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one query column,
+// with the gfx950 cross-row swaps (VALU only, no LDS round trip).  permlane32_swap on (x, x)
+// hands each lane the value of lane l^32 in one of its two results and its own in the other;
+// permlane16_swap does the same for lane l^16.
+__device__ __forceinline__ float max_over_groups(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory operations and
+// nothing else (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
 // LDS pointer in the local address space, as the direct global -> LDS load takes it.  The
 // cast is written inline: an implicit conversion (or a helper function) there makes the host
@@ -235,11 +255,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     int j0 = tw.tile(0) * kTileN, c_lo, c_hi;
     tile_chunks(j0, 2, t0, t1, a.w_loc, a.s, c_lo, c_hi);
     issue_tile(j0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
 
-    for (int n = 0; n < ntiles; ++n) {
-        const int buf = n & 1;
+    // One tile step; the LDS buffer index is a compile-time constant (the loop below is
+    // unrolled by two), so every LDS address is a per-lane base plus an immediate offset.
+    auto tile_step = [&](const int n, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const unsigned char *kt = lds[buf][0];
         const unsigned char *vt = lds[buf][1];
         int nj0 = 0, nc_lo = 2, nc_hi = -1;
@@ -310,8 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     mx = fmaxf(mx, fmaxf(fmaxf(sacc[kc][h][qb][0], sacc[kc][h][qb][1]),
                                          fmaxf(sacc[kc][h][qb][2], sacc[kc][h][qb][3])));
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_over_groups(mx);
             const float m_tile = mx * c;
             const bool grow = m_tile > m_ref[qb] + 8.f;
             alpha[qb] = 1.f;
@@ -372,11 +393,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
         __syncthreads();
         j0 = nj0;
         c_lo = nc_lo;
         c_hi = nc_hi;
+    };
+    for (int n = 0; n < ntiles; n += 2) {
+        tile_step(n, std::integral_constant<int, 0>());
+        if (n + 1 < ntiles)
+            tile_step(n + 1, std::integral_constant<int, 1>());
     }
 
     // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
@@ -471,30 +497,25 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    if (start != nullptr || stop != nullptr) {
-        if (d == 128)
-            hipExtLaunchKernelGGL(prefill_kernel<128>, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
-        else
-            hipExtLaunchKernelGGL(prefill_kernel<64>, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
-    } else if (d == 128) {
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3(a.nblocks), dim3(kThreads), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3(a.nblocks), dim3(kThreads), 0, stream, a);
-    }
+    void (*kern)(PrefillArgs) = d == 128 ? prefill_kernel<128> : prefill_kernel<64>;
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int w_loc, int s,
+hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w_loc, int s,
                                      hipStream_t stream)
 {
+    (void)d;  // one tile geometry serves both head sizes
     const PrefillGeometry g = prefill_geometry(L, Hq, Hkv);
     const size_t n = (size_t)L * L;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, mask, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(256), 0, stream, mask, L, g.Tm,
-                       w_loc, s);
+    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(256), 0, stream, mask, L, g.Tm, w_loc, s);
     return hipGetLastError();
 }
 

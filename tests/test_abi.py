@@ -99,8 +99,9 @@ def test_decode_workspace_query_and_rejection(lib):
 
 
 def test_debug_hooks_reject_on_host(lib):
-    assert lib.swa_debug_prefill_mask(None, 16, 4, 4, 8, 2, 0, None) == binding.SWA_EINVAL
-    assert lib.swa_debug_prefill_mask(A, 9000, 4, 4, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_prefill_mask(None, 16, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_prefill_mask(A, 9000, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_debug_prefill_mask(A, 16, 4, 4, 96, 8, 2, 0, None) == binding.SWA_EUNSUPPORTED
     assert lib.swa_debug_decode_slots(A, None, 1, 8, 2, 0, None) == binding.SWA_EINVAL
     assert lib.swa_debug_decode_slots(A, A, 1, 2, 2, 1, None) == binding.SWA_EINVAL
 
