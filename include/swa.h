@@ -117,10 +117,11 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, i
  * For each batch b with query position t = pos[b] (already appended with
  * swa_kv_append), out[b][h] is the SWA(w,s) attention row t of q[b][h] over the cache:
  * the sinks 0 .. min(s, t+1)-1 and the ring slots holding positions
- * max(s, t-w_loc+1) .. t.  Slot validity is derived from t alone, so stale slots from
- * earlier use of the cache are never read.  The cache is read in storage order; the
- * softmax sum does not depend on order.  The slot range is split over workgroups and
- * the partial (max, sum, weighted values) are merged in a fixed order.
+ * max(s, t-w_loc+1) .. t.  Slot validity is derived from t alone: a slot that holds no
+ * position of A(t) (never written yet, or stale from earlier use of the cache) contributes
+ * nothing, whatever bytes it holds.  The cache is read in storage order; the softmax sum
+ * does not depend on order.  When s + w_loc exceeds 96 slots the slot range is split over
+ * workgroups and the partial (max, sum, weighted values) are merged in a fixed order.
  *
  *   q          bf16 [B][Hq][d]   (in)
  *   k_cache,   bf16 [B][Hkv][s + w_loc][d] (in)

@@ -10,9 +10,9 @@
 // and q-head: with 4 q-heads per kv-head that is 8 flops per byte, more than the fp32 vector
 // units sustain at HBM speed, so the products run on bf16 MFMA (the q-heads of a kv-head
 // are the MFMA columns) and the kernel stays bound by the bytes it reads.  The slot range
-// of a (b, kv-head) is split over workgroups (split-K) when there are too few (b, kv-head)
-// pairs to fill the GPU; partial (max, sum, weighted values) merge in a separate kernel
-// that visits splits in a fixed order, so results do not depend on scheduling.
+// of a (b, kv-head) is split over workgroups (split-K) only when it exceeds what one
+// workgroup holds (96 slots); partial (max, sum, weighted values) then merge in a separate
+// kernel that visits splits in a fixed order, so results do not depend on scheduling.
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -35,9 +35,26 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // r..r+3 (r = 0 mod 4) at pieces P, P+1 hit 8 distinct pieces.
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kChunk = 32;      // slots per MFMA step
+constexpr int kMaxChunks = 3;   // slots per workgroup <= 96
 
+// Sum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one MFMA column, with
+// the gfx950 cross-row swaps: permlane32_swap(x, x) hands each lane its own value and the
+// value of lane l^32 (one in each result), permlane16_swap likewise for lane l^16.
+__device__ __forceinline__ float sum_over_groups(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float max_over_groups(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -53,37 +70,34 @@ struct DecodeArgs {
     float scale_log2;
 };
 
-// grid: (n_split, Hkv * n_hslices, B); 4 waves.  The GB <= 16 q-heads of a kv-head are the
-// 16 columns of a bf16 MFMA (unused columns are zero), so the per-key work runs on the
-// matrix cores and the kernel stays bound by the cache bytes it reads:
+// grid: (n_split, Hkv * n_hslices, B); one wave per workgroup, which owns the slot segment
+// [seg_lo, seg_hi) (at most NCH chunks of 32 slots) of one (b, kv-head, head slice).  The
+// GB <= 16 q-heads of the kv-head are the 16 columns of a bf16 MFMA (unused columns are zero),
+// so the per-key work runs on the matrix cores:
 //     S^T (32 keys x heads) = K (32 keys x d) . Q^T (d x heads)
 //     O^T (d x heads)     += V^T (d x 32 keys) . P^T (32 keys x heads)
-// exactly the prefill kernel's layout (lane l holds column l % 16 of S^T for keys
-// 8(l/16) .. +7 of the chunk, which is the B-operand layout of P^T).  K fragments come
-// straight from global memory; V rows go to a per-wave LDS buffer and come back transposed
-// through ds_read_b64_tr_b16.  Each wave walks 32-slot chunks of the workgroup's segment
-// with its own online-softmax state; the four states merge through LDS at the end.
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
+// the prefill kernel's layout (lane l holds column l % 16 of S^T for keys 8(l/16) .. +7 of
+// the chunk, which is the B-operand layout of P^T).
+//
+// Latency: every load of the workgroup (Q, the K fragments of all chunks into registers, the
+// V rows of all chunks straight into LDS, the new token) is issued before anything waits on
+// the position, so a step costs one memory round trip.  The addresses do not depend on the
+// position: once the ring has wrapped (t >= s + w_loc - 1) every slot holds a position of
+// A(t).  Before that, the V rows of empty slots are zeroed in LDS after they land and their
+// scores are masked, so whatever bytes such a slot holds never reach the result.  The fused
+// path takes the new token's K (registers) and V (written over its LDS row) from the input.
+template <int D, int NCH>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
 {
-    constexpr int kChunk = 32;             // slots per wave iteration
-    constexpr int kKSteps = D / 32;        // MFMA k-steps for S
-    constexpr int kDBlocks = D / 16;       // 16-row blocks of O^T
-    constexpr int kPieces = D / 8;         // 16-byte pieces per row
+    constexpr int kKSteps = D / 32;   // MFMA k-steps for S
+    constexpr int kDBlocks = D / 16;  // 16-row blocks of O^T
+    constexpr int kPieces = D / 8;    // 16-byte pieces per row
     constexpr int kRowBytes = D * 2;
     constexpr int kRowsPerLoad = 1024 / kRowBytes;
-    constexpr int kLoads = kChunk / kRowsPerLoad;  // 1 KiB direct loads per chunk
+    constexpr int kLoads = kChunk / kRowsPerLoad;  // 1 KiB direct loads per chunk of V
+    __shared__ __attribute__((aligned(1024))) unsigned char vlds[NCH][kChunk * kRowBytes];
 
-    // V staging (per wave), reused after the slot loop for the wave merge of O.
-    static_assert(kWaves * kChunk * kRowBytes == kWaves * 16 * D * 4, "merge buffer size");
-    __shared__ __attribute__((aligned(1024))) unsigned char vlds[kWaves][kChunk * kRowBytes];
-    __shared__ float red_m[kWaves][16];
-    __shared__ float red_l[kWaves][16];
-    float(*red_o)[16][D] = reinterpret_cast<float(*)[16][D]>(&vlds[0][0]);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x;
     const int g16 = lane >> 4;
     const int c16 = lane & 15;
     const int split = blockIdx.x;
@@ -92,44 +106,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
     const int b = blockIdx.z;
     const int GB = a.Gb;                 // heads of this workgroup (<= 16)
     const int h0 = hkv * a.G + hs * GB;  // first q-head of this workgroup
-
-    const int64_t t = a.pos[b];
-    const SlotMap sm(t, a.s, a.w_loc);
     const size_t cache_base = ((size_t)b * a.Hkv + hkv) * a.n_slots * D;
     const uint16_t *kcache = a.kc + cache_base;
     const uint16_t *vcache = a.vc + cache_base;
     const int seg_lo = split * a.slots_per_split;
     const int seg_hi = min(seg_lo + a.slots_per_split, a.n_slots);
-
-    // The slot of position t.  Fused append: that slot's K/V come from the input (never from
-    // the cache) in every workgroup, and one workgroup writes them to the cache.
+    const int nch = (seg_hi - seg_lo + kChunk - 1) / kChunk;  // <= NCH
     const bool fused = a.kn != nullptr;
-    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
-    const uint16_t *knew = fused ? a.kn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
-    const uint16_t *vnew = fused ? a.vn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
-    if (fused && hs == 0 && slot_t >= seg_lo && slot_t < seg_hi && tid < kPieces) {
-        *reinterpret_cast<u32x4 *>(a.kc + cache_base + (size_t)slot_t * D + tid * 8) =
-            *reinterpret_cast<const u32x4 *>(knew + tid * 8);
-        *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + tid * 8) =
-            *reinterpret_cast<const u32x4 *>(vnew + tid * 8);
-    }
-    // Row pointer for a slot; slots that hold nothing of A(t) read the row of position t
-    // instead (finite data, masked out), so no lane ever touches an unwritten row.
-    auto krow = [&](int slot, bool valid) -> const uint16_t * {
-        const int sl = valid ? slot : slot_t;
-        if (sl < 0)
-            return kcache;
-        return (fused && sl == slot_t) ? knew : kcache + (size_t)sl * D;
-    };
-    auto vrow = [&](int slot, bool valid) -> const uint16_t * {
-        const int sl = valid ? slot : slot_t;
-        if (sl < 0)
-            return vcache;
-        return (fused && sl == slot_t) ? vnew : vcache + (size_t)sl * D;
-    };
 
-    // Q^T B-operand fragments: column c16 = q-head h0 + c16 (zero beyond GB).
-    bf16x8 qf[kKSteps];
+    // ---- every load, none of which depends on the position.
+    const int64_t t = a.pos[b];
+    bf16x8 qf[kKSteps];  // Q^T B operand: column c16 = q-head h0 + c16 (zero beyond GB)
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
         u32x4 x = {0u, 0u, 0u, 0u};
@@ -137,50 +124,79 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
             x = *reinterpret_cast<const u32x4 *>(a.q + ((size_t)b * a.Hq + h0 + c16) * D + kk * 32 + g16 * 8);
         qf[kk] = __builtin_bit_cast(bf16x8, x);
     }
+    const uint16_t *knew = fused ? a.kn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
+    const uint16_t *vnew = fused ? a.vn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
+    bf16x8 knf[kKSteps];  // the new token's K at this lane's fragment pieces
+    u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
+    if (fused) {
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk)
+            knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
+        if (lane < kPieces) {
+            kn_piece = *reinterpret_cast<const u32x4 *>(knew + lane * 8);
+            vn_piece = *reinterpret_cast<const u32x4 *>(vnew + lane * 8);
+        }
+    }
+    // Rows past the segment repeat its last slot (in-bounds; their scores are masked).
+    const int last = seg_hi - 1;
+    bf16x8 kf[NCH][2][kKSteps];  // K fragment (chunk, kb, kk): row 8(c16/4) + 4kb + c16%4
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch < nch) {
+            const int c0 = seg_lo + ch * kChunk;
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int r = kRowsPerLoad * i + lane / kPieces;
+                const int slot = min(c0 + r, last);
+                const int piece = (lane % kPieces) ^ swz_v(r);
+                __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vcache + (size_t)slot * D + piece * 8),
+                                                 SWA_LDS_PTR(&vlds[ch][1024 * i]), 16, 0, 0);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int slot = min(c0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), last);
+#pragma unroll
+                for (int kk = 0; kk < kKSteps; ++kk)
+                    kf[ch][kb][kk] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(kcache + (size_t)slot * D + kk * 32 + g16 * 8));
+            }
+        }
+    }
+
+    // ---- the position.
+    const SlotMap sm(t, a.s, a.w_loc);
+    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
+    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
+    if (fused && hs == 0 && slot_t >= seg_lo && slot_t < seg_hi && lane < kPieces) {
+        *reinterpret_cast<u32x4 *>(a.kc + cache_base + (size_t)slot_t * D + lane * 8) = kn_piece;
+        *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + lane * 8) = vn_piece;
+    }
+
     const __bf16 one_or_zero = static_cast<__bf16>(c16 == 0 ? 1.f : 0.f);
     const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
-
     f32x4 o[kDBlocks];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
         o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY;  // log2 units, per column; probabilities stay below 2^8
-
-    unsigned char *vbuf = vlds[wave];
     const int vt_row0 = 8 * g16 + (c16 >> 2);
     const int vt_half = 8 * (c16 & 1);
     const int vt_pbit = (c16 >> 1) & 1;
 
-    for (int c0 = seg_lo + wave * kChunk; c0 < seg_hi; c0 += kWaves * kChunk) {
-        // V rows of the chunk -> this wave's LDS buffer (row-major, swizzled pieces).
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int r = kRowsPerLoad * i + lane / kPieces;
-            const int slot = c0 + r;
-            const bool valid = slot < seg_hi && sm.valid(slot);
-            const int piece = (lane % kPieces) ^ swz_v(r);
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vrow(slot, valid) + piece * 8),
-                                             SWA_LDS_PTR(vbuf + 1024 * i), 16, 0, 0);
-        }
-        // K fragments straight from global: row 8(c16/4) + 4kb + c16%4 of the chunk.
-        bf16x8 kf[2][kKSteps];
-        bool kvalid[2][4];
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch >= nch)
+            break;
+        const int c0 = seg_lo + ch * kChunk;
+        if (fused && slot_t >= c0 && slot_t < c0 + kChunk) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int r = 8 * (c16 >> 2) + 4 * kb + (c16 & 3);
-            const int slot = c0 + r;
-            const bool valid = slot < seg_hi && sm.valid(slot);
-            const uint16_t *kr = krow(slot, valid);
+            for (int kb = 0; kb < 2; ++kb) {
+                const bool mine = c0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3) == slot_t;
 #pragma unroll
-            for (int kk = 0; kk < kKSteps; ++kk)
-                kf[kb][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + kk * 32 + g16 * 8));
-            // validity of the keys this lane will hold in S^T: 8*g16 + 4kb + j
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sj = c0 + 8 * g16 + 4 * kb + j;
-                kvalid[kb][j] = sj < seg_hi && sm.valid(sj);
+                for (int kk = 0; kk < kKSteps; ++kk)
+                    kf[ch][kb][kk] = mine ? knf[kk] : kf[ch][kb][kk];
             }
         }
         f32x4 sacc[2];
@@ -189,19 +205,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
             sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < kKSteps; ++kk)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][kk], qf[kk], sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ch][kb][kk], qf[kk], sacc[kb], 0, 0, 0);
         }
-        // Mask, then the online softmax of the column (lazy rescale, threshold 8 in log2).
+        // Mask: slots past the segment, and before the ring wraps the slots outside A(t).
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sacc[kb][j] = kvalid[kb][j] ? sacc[kb][j] : -INFINITY;
+                const int sj = c0 + 8 * g16 + 4 * kb + j;
+                const bool ok = sj < seg_hi && (wrapped || sm.valid(sj));
+                sacc[kb][j] = ok ? sacc[kb][j] : -INFINITY;
                 mx = fmaxf(mx, sacc[kb][j]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_groups(mx);
+        // Online softmax of the column with lazy rescaling (threshold 8 in log2 units).
         const float m_tile = mx * a.scale_log2;
         if (__any(m_tile > m_ref + 8.f)) {
             const float m_new = fmaxf(m_ref, m_tile);
@@ -221,7 +239,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
                 pf[4 * kb + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], a.scale_log2, -m_use)));
         lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf, lsum, 0, 0, 0);
 
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's V rows are in LDS
+        unsigned char *vbuf = vlds[ch];
+        if (ch == 0)
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): every V row is in LDS
+        // V fix-ups in LDS (LDS operations of a wave complete in order, so the transposed
+        // reads below see them): zero the rows of slots outside A(t) (before the ring wraps,
+        // and the padding past the segment), and put the new token's row over its slot.
+        if (!wrapped || c0 + kChunk > seg_hi) {
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int r = kRowsPerLoad * i + lane / kPieces;
+                const int sj = c0 + r;
+                if (!(sj < seg_hi && (wrapped || sm.valid(sj))))
+                    *reinterpret_cast<u32x4 *>(vbuf + 1024 * i + 16 * lane) = u32x4{0u, 0u, 0u, 0u};  // row r
+            }
+        }
+        if (fused && slot_t >= c0 && slot_t < c0 + kChunk && lane < kPieces) {
+            const int r = slot_t - c0;
+            *reinterpret_cast<u32x4 *>(vbuf + r * kRowBytes + 16 * (lane ^ swz_v(r))) = vn_piece;
+        }
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
             bf16x8 af;
@@ -238,48 +274,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
             }
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[db], 0, 0, 0);
         }
-        // The next iteration's loads overwrite vbuf: the transposed reads above must have
-        // returned (they have: the MFMAs consumed them) before the loads are issued.
     }
 
-    // Per-wave states -> LDS, then merge the waves: thread -> (head g, element d).
-    __syncthreads();  // every wave is done with its V buffer, which now holds red_o
-    if (g16 == 0 && c16 < GB) {
-        red_m[wave][c16] = m_ref;
-        red_l[wave][c16] = lsum[0];
-    }
-    if (c16 < GB) {
+    // ---- output (one split) or the partial (m, l, o) of this split.
+    const float ll = sum_over_groups(lsum[0]);  // non-zero in lane group 0 only
+    if (c16 >= GB)
+        return;
+    const int h = h0 + c16;
+    if (a.n_split == 1) {
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        float *orow = a.out + ((size_t)b * a.Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+            *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db] * inv;
+    } else {
+        float *part = a.ws + (((size_t)b * a.Hq + h) * a.n_split + split) * (D + 2);
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                red_o[wave][c16][db * 16 + 4 * g16 + j] = o[db][j];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GB * D; idx += kThreads) {
-        const int g = idx / D, dd = idx % D;
-        float mm = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            mm = fmaxf(mm, red_m[w][g]);
-        const float m_use = mm == -INFINITY ? 0.f : mm;
-        float ll = 0.f, oo = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = __builtin_amdgcn_exp2f(red_m[w][g] - m_use);
-            ll += red_l[w][g] * sc;
-            oo += red_o[w][g][dd] * sc;
-        }
-        const int h = h0 + g;
-        if (a.n_split == 1) {
-            a.out[((size_t)b * a.Hq + h) * D + dd] = ll > 0.f ? oo / ll : 0.f;
-        } else {
-            float *part = a.ws + (((size_t)b * a.Hq + h) * a.n_split + split) * (D + 2);
-            part[2 + dd] = oo;
-            if (dd == 0) {
-                part[0] = mm;
-                part[1] = ll;
-            }
+                part[2 + db * 16 + g16 * 4 + j] = o[db][j];
+        if (g16 == 0) {
+            part[0] = m_ref;
+            part[1] = ll;
         }
     }
 }
@@ -348,7 +365,14 @@ __global__ void debug_decode_slots_kernel(int64_t *slot_pos, const int64_t *pos,
 template <int D>
 void launch_decode_d(const DecodeArgs &a, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL(decode_kernel<D>, dim3(a.n_split, a.Hkv * a.n_hslices, B), dim3(kThreads), 0, stream, a);
+    const dim3 grid(a.n_split, a.Hkv * a.n_hslices, B);
+    const int nch = (a.slots_per_split + kChunk - 1) / kChunk;
+    if (nch <= 1)
+        hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(64), 0, stream, a);
+    else if (nch == 2)
+        hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, 3>), grid, dim3(64), 0, stream, a);
 }
 
 }  // namespace
@@ -365,14 +389,12 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s)
             break;
         }
     p.n_hslices = G / p.Gb;
-    // Enough workgroups to cover the 256 CUs twice, but at least 32 slots per split.
-    const long long pairs = (long long)B * Hkv * p.n_hslices;
-    long long want = (512 + pairs - 1) / pairs;
-    const long long max_split = (p.n_slots + 31) / 32;
-    if (want > max_split)
-        want = max_split;
-    if (want < 1)
-        want = 1;
+    // As few splits as the kernel's register and LDS budget (kMaxChunks * 32 slots per
+    // workgroup) allows: a step costs one memory round trip either way, and a second kernel
+    // (the merge) costs more than the parallelism it buys, even at batch 1.
+    (void)B;
+    (void)d;
+    const long long want = (p.n_slots + kMaxChunks * kChunk - 1) / (kMaxChunks * kChunk);
     p.slots_per_split = (int)((p.n_slots + want - 1) / want);
     p.n_split = (p.n_slots + p.slots_per_split - 1) / p.slots_per_split;
     p.workspace_bytes = p.n_split > 1 ? (size_t)B * Hq * p.n_split * (d + 2) * sizeof(float) : 0;

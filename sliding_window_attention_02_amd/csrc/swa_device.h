@@ -93,14 +93,20 @@ __device__ __forceinline__ int64_t append_slot(int64_t p, int s, int w_loc)
 
 // Slot -> position map for a query at position t (the latest appended position): slot j
 // holds position(j), or -1 when the slot holds nothing in A(t) (a sink slot beyond t, or a
-// ring slot whose latest position would be a sink or negative).  The one 64-bit modulo is
-// taken at construction; position() is 32-bit arithmetic plus one 64-bit subtraction.
+// ring slot whose latest position would be a sink or negative).  The one modulo is taken at
+// construction (32-bit unless t needs 64); position() is 32-bit arithmetic plus one 64-bit
+// subtraction.
 struct SlotMap {
     int64_t t;
     int s, w_loc, t_mod;
-    __device__ __forceinline__ SlotMap(int64_t t_, int s_, int w_loc_)
-        : t(t_), s(s_), w_loc(w_loc_), t_mod(t_ >= 0 ? (int)(t_ % w_loc_) : 0)
+    __device__ __forceinline__ SlotMap(int64_t t_, int s_, int w_loc_) : t(t_), s(s_), w_loc(w_loc_)
     {
+        if (t_ < 0)
+            t_mod = 0;
+        else if (t_ <= 0x7fffffffLL)
+            t_mod = (int)((uint32_t)t_ % (uint32_t)w_loc_);
+        else
+            t_mod = (int)(t_ % w_loc_);
     }
     __device__ __forceinline__ int64_t position(int j) const
     {

@@ -81,21 +81,22 @@ def test_kv_append_rejects_on_host(lib):
 
 
 def test_decode_workspace_query_and_rejection(lib):
-    # 512 (b, kv-head) pairs fill the chip: no split, no workspace.
+    # 68 slots fit one workgroup at any batch: no split, no workspace.
     assert lib.swa_decode_workspace_bytes(64, 32, 8, 128, 64, 4, 0) == 0
-    # One sequence: the 68 slots are split; partials are (max, sum, d values) per q-head and split.
-    ws = lib.swa_decode_workspace_bytes(1, 32, 8, 128, 64, 4, 0)
+    assert lib.swa_decode_workspace_bytes(1, 32, 8, 128, 64, 4, 0) == 0
+    # 204 slots are split; partials are (max, sum, d values) per q-head and split.
+    ws = lib.swa_decode_workspace_bytes(1, 32, 8, 128, 200, 4, 0)
     assert ws > 0 and ws % (32 * (128 + 2) * 4) == 0
-    assert lib.swa_decode_workspace_bytes(1, 32, 8, 96, 64, 4, 0) == 0
+    assert lib.swa_decode_workspace_bytes(1, 32, 8, 96, 200, 4, 0) == 0
     f = lib.swa_decode_step
-    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None)
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 200, 4, 0.1, 0, None, 0, None)
     assert rc == binding.SWA_EINVAL and "workspace" in err(lib)
-    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, A, ws - 4, None)
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 200, 4, 0.1, 0, A, ws - 4, None)
     assert rc == binding.SWA_EINVAL and "workspace" in err(lib)
-    rc = f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.1, 0, MIS, ws, None)
+    rc = f(A, A, A, A, A, 1, 32, 8, 128, 200, 4, 0.1, 0, MIS, ws, None)
     assert rc == binding.SWA_EINVAL and "aligned" in err(lib)
-    assert f(A, A, A, A, None, 1, 32, 8, 128, 64, 4, 0.1, 0, A, ws, None) == binding.SWA_EINVAL
-    assert f(A, A, A, A, A, 1, 32, 8, 128, 64, 4, 0.0, 0, A, ws, None) == binding.SWA_EINVAL
+    assert f(A, A, A, A, None, 1, 32, 8, 128, 200, 4, 0.1, 0, A, ws, None) == binding.SWA_EINVAL
+    assert f(A, A, A, A, A, 1, 32, 8, 128, 200, 4, 0.0, 0, A, ws, None) == binding.SWA_EINVAL
 
 
 def test_debug_hooks_reject_on_host(lib):

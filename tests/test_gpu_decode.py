@@ -115,7 +115,9 @@ def history(seed, T, B, Hq, Hkv, d, std=1.0, boost_n=4):
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv", [(3, 8, 2, 128, 16, 4, 0), (2, 32, 8, 128, 64, 4, 0),
                                                  (2, 4, 4, 64, 8, 0, 0), (1, 12, 4, 128, 20, 4, 1),
-                                                 (5, 16, 1, 64, 5, 9, 0), (1, 32, 2, 128, 40, 2, 0)])
+                                                 (5, 16, 1, 64, 5, 9, 0), (1, 32, 2, 128, 40, 2, 0),
+                                                 # more slots than one workgroup holds: split + merge
+                                                 (1, 8, 2, 128, 150, 4, 0), (2, 8, 4, 64, 200, 2, 0)])
 def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv):
     say("decode-empty", B, Hq, Hkv, d, w, s, conv)
     T = 300
@@ -123,6 +125,8 @@ def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv):
     scale = 1.0 / np.sqrt(d)
     ref = orc.prefill(f64(qs), f64(ks), f64(vs), w, s, scale, conv)
     kc, vc = swa.alloc_cache(B, Hkv, d, w, s, conv)
+    kc.fill_(float("nan"))  # slots not yet written must never reach the result
+    vc.fill_(float("nan"))
     ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s, conv)
     qg, kg, vg = qs.cuda(), ks.cuda(), vs.cuda()
     outs = []
