@@ -14,11 +14,13 @@ decode replay.
 
 Printed JSON line (one):
   value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time
-  decode           tokens/s of the decode leg and its HBM figures
+  decode           tokens/s of the decode leg and its HBM figures; other_batches: the same
+                   decode graph timed alone at batch 1 and batch 1024 (outside the steps)
   roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
                    launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
                    38.5 useful flop per algorithmic byte, far below the 315 flop/byte ridge)
   cpu_baseline     the fp64 oracle timed on host cores on the same prefill workload
+                   (whole passes, repeated for at least 10 s)
 """
 from __future__ import annotations
 
@@ -71,6 +73,7 @@ def parse():
     ap.add_argument("--decode-tokens", type=int, default=256)
     ap.add_argument("--decode-start", type=int, default=2 ** 18)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-points", action="store_true", help="skip the batch 1 and 1024 decode points")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cores))")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -88,20 +91,97 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 3}))
 
 
-def cpu_baseline(wl, q, k, v, threads: int):
-    """The oracle as it stands on the host cores: the whole prefill workload, timed once."""
+def cpu_baseline(wl, q, k, v, threads: int, min_seconds: float = 10.0):
+    """The oracle as it stands on the host cores: whole passes of the prefill workload,
+    repeated until at least min_seconds of CPU work."""
     from oracle import oracle as orc
     from sliding_window_attention_02_amd import accounting as acc
 
     qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    passes = 0
     t0 = time.perf_counter()
-    orc.prefill(qd, kd, vd, wl.w, wl.s, wl.scale, wl.conv, nthreads=threads)
-    dt = time.perf_counter() - t0
+    while True:
+        orc.prefill(qd, kd, vd, wl.w, wl.s, wl.scale, wl.conv, nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
-    flops = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    flops = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s) * passes
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {wl.name} prefill (B={wl.B}, L={wl.L}, Hq={wl.Hq}, Hkv={wl.Hkv}, d={wl.d}, "
-                      f"SWA({wl.w},{wl.s})) once in fp64, {dt:.2f} s"}
+            "sample": f"{passes} whole passes of the {wl.name} prefill (B={wl.B}, L={wl.L}, Hq={wl.Hq}, "
+                      f"Hkv={wl.Hkv}, d={wl.d}, SWA({wl.w},{wl.s})) in fp64, {dt:.1f} s"}
+
+
+def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev):
+    """A HIP graph of T decode steps of workload dw at batch B (positions P .. P+T-1), each step
+    one swa_append_decode_step (append the token's K/V to its slot and attend), and a function
+    that restores the cache to its state after position P-1 (run it before every replay, so
+    each replay decodes the same tokens).  Every input is seeded: the cache holds the sinks and
+    positions P-w_loc .. P-1."""
+    import torch
+
+    w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
+    gen = dict(B=B, Hkv=dw.Hkv, d=dw.d, std=dw.std, sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost)
+    kc, vc = swa.alloc_cache(B, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    ws = swa.alloc_workspace(B, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    seed_pos = list(range(dw.s)) + list(range(P - w_loc, P))
+    sk, sv = inputs.kv_span(dw.seed, seed_pos, **gen)
+    swa.kv_append(kc, vc, sk[:, :dw.s].contiguous().to(dev), sv[:, :dw.s].contiguous().to(dev),
+                  torch.zeros(B, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    swa.kv_append(kc, vc, sk[:, dw.s:].contiguous().to(dev), sv[:, dw.s:].contiguous().to(dev),
+                  torch.full((B,), P - w_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    dq = torch.stack([inputs.q_at(dw.seed, P + i, B, dw.Hq, dw.d, dw.std) for i in range(T)]).to(dev)
+    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(T)]
+    dk = torch.stack([x[0] for x in kvs]).to(dev)  # [T][B][Hkv][d]
+    dv = torch.stack([x[1] for x in kvs]).to(dev)
+    dpos = (P + torch.arange(T, dtype=torch.int64)).repeat_interleave(B).view(T, B).to(dev)
+    dout = torch.empty((T, B, dw.Hq, dw.d), dtype=torch.float32, device=dev)
+    snap_k, snap_v = kc.clone(), vc.clone()
+
+    def steps():
+        for i in range(T):
+            swa.append_decode_step(dq[i], kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.scale, dw.conv,
+                                   out=dout[i], workspace=ws)
+
+    def restore():
+        kc.copy_(snap_k)
+        vc.copy_(snap_v)
+
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        steps()  # eager warm-up on the capture stream
+    stream.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        steps()
+    torch.cuda.synchronize()
+    return graph, restore
+
+
+def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 5):
+    """Per-token step time of the decode graph at batch B (not part of the bench step)."""
+    import torch
+
+    graph, restore = decode_graph(swa, inputs, dw, B, T, P, dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(reps + 1):
+        restore()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    step_us = sum(ms[1:]) / reps * 1e3 / T
+    w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
+    kv = acc.decode_kv_bytes(B, dw.Hkv, dw.d, acc.decode_keys(P, w_loc, dw.s))
+    gbs = kv / (step_us * 1e-6) / 1e9
+    return {"B": B, "us_per_token_step": round(step_us, 3), "tokens_per_s": round(B / (step_us * 1e-6), 1),
+            "kv_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5)}
 
 
 def main():
@@ -140,49 +220,11 @@ def main():
     dw = inputs.decode_workloads()["decode_swa64_4_b64"]
     DB, T, P = args.decode_batch, args.decode_tokens, args.decode_start
     dw_loc = dw.w if dw.conv == 0 else dw.w - dw.s
-    gen = dict(B=DB, Hkv=dw.Hkv, d=dw.d, std=dw.std, sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost)
-    kc, vc = swa.alloc_cache(DB, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
-    ws = swa.alloc_workspace(DB, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
-    seed_pos = list(range(dw.s)) + list(range(P - dw_loc, P))
-    sk, sv = inputs.kv_span(dw.seed, seed_pos, **gen)
-    swa.kv_append(kc, vc, sk[:, :dw.s].contiguous().to(dev), sv[:, :dw.s].contiguous().to(dev),
-                  torch.zeros(DB, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
-    swa.kv_append(kc, vc, sk[:, dw.s:].contiguous().to(dev), sv[:, dw.s:].contiguous().to(dev),
-                  torch.full((DB,), P - dw_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
-    dq = torch.stack([inputs.q_at(dw.seed, P + i, DB, dw.Hq, dw.d, dw.std) for i in range(T)]).to(dev)
-    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(T)]
-    dk = torch.stack([x[0] for x in kvs]).to(dev)  # [T][B][Hkv][d]
-    dv = torch.stack([x[1] for x in kvs]).to(dev)
-    dpos = (P + torch.arange(T, dtype=torch.int64)).repeat_interleave(DB).view(T, DB).to(dev)
-    dout = torch.empty((T, DB, dw.Hq, dw.d), dtype=torch.float32, device=dev)
-    # The graph replays T append+attend steps.  The cache is restored to the state after
-    # position P-1 before every replay, so each replay decodes the same token sequence.
-    snap_k, snap_v = kc.clone(), vc.clone()
-
-    def decode_steps():
-        # One launch per token: append the new K/V to its slot and attend (swa_append_decode_step).
-        for i in range(T):
-            swa.append_decode_step(dq[i], kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.scale, dw.conv,
-                                   out=dout[i], workspace=ws)
-
-    stream = torch.cuda.Stream(device=dev)
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        decode_steps()  # eager warm-up on the capture stream
-    stream.synchronize()
-    kc.copy_(snap_k)
-    vc.copy_(snap_v)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        decode_steps()
-    torch.cuda.synchronize()
-
+    graph, restore = decode_graph(swa, inputs, dw, DB, T, P, dev)
     def step(evs=None, i=0):
         # Decode replay first, then the prefill: the prefill's start event is always queued
         # behind GPU work, so its interval never includes host launch latency.
-        kc.copy_(snap_k)
-        vc.copy_(snap_v)
+        restore()
         if evs is not None:
             evs[2][i].record()
         graph.replay()
@@ -222,6 +264,14 @@ def main():
     dec_kv_bytes = acc.decode_kv_bytes(DB, dw.Hkv, dw.d, n_keys)
     dec_step_us = dec_mean * 1e3 / T
     dec_gbs = dec_kv_bytes / (dec_step_us * 1e-6) / 1e9
+
+    # Other batch sizes of the same decode workload, outside the timed steps: batch 1 (the
+    # other configured batch) and batch 1024, where the cache (285 MB) no longer fits the
+    # Infinity Cache and the step is bound by HBM rather than by latency.
+    points = []
+    if not args.no_decode_points:
+        for b, t in ((1, 256), (1024, 32)):
+            points.append(decode_point(swa, inputs, acc, dw, b, t, P, dev))
 
     base = None
     if not args.no_cpu_baseline:
@@ -266,6 +316,7 @@ def main():
             "kv_gb_per_s": round(dec_gbs, 2),
             "frac_of_hbm_peak": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
             "note": "the 17.8 MB working set stays in the 256 MB Infinity Cache across steps",
+            "other_batches": points,
         },
         "roofline": {
             "kernel": "prefill_kernel<128>",
