@@ -17,6 +17,11 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["swa_api.cpp", "swa_prefill.hip", "swa_decode.hip"]
 
+# Per-source flags.  The decode kernel runs one wave per workgroup, so the compiler may give
+# it AGPRs; keeping MFMA results in arch VGPRs spares the AGPR -> VGPR copies before the
+# softmax reads the scores.
+EXTRA_FLAGS = {"swa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -43,7 +48,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"]
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)

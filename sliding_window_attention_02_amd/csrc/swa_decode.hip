@@ -117,12 +117,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
     // ---- every load, none of which depends on the position.
     const int64_t t = a.pos[b];
     bf16x8 qf[kKSteps];  // Q^T B operand: column c16 = q-head h0 + c16 (zero beyond GB)
+    {
+        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + h0 + min(c16, GB - 1)) * D + g16 * 8;
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (c16 < GB)
-            x = *reinterpret_cast<const u32x4 *>(a.q + ((size_t)b * a.Hq + h0 + c16) * D + kk * 32 + g16 * 8);
-        qf[kk] = __builtin_bit_cast(bf16x8, x);
+        for (int kk = 0; kk < kKSteps; ++kk) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(qrow + kk * 32);
+            qf[kk] = __builtin_bit_cast(bf16x8, c16 < GB ? x : u32x4{0u, 0u, 0u, 0u});
+        }
     }
     const uint16_t *knew = fused ? a.kn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
     const uint16_t *vnew = fused ? a.vn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
@@ -132,14 +133,28 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk)
             knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
-        if (lane < kPieces) {
-            kn_piece = *reinterpret_cast<const u32x4 *>(knew + lane * 8);
-            vn_piece = *reinterpret_cast<const u32x4 *>(vnew + lane * 8);
-        }
+        const int piece = min(lane, kPieces - 1);  // lanes past the row repeat its last piece
+        kn_piece = *reinterpret_cast<const u32x4 *>(knew + piece * 8);
+        vn_piece = *reinterpret_cast<const u32x4 *>(vnew + piece * 8);
     }
     // Rows past the segment repeat its last slot (in-bounds; their scores are masked).
     const int last = seg_hi - 1;
+    // K first (the scores need it first), then V, which is only needed after the softmax.
     bf16x8 kf[NCH][2][kKSteps];  // K fragment (chunk, kb, kk): row 8(c16/4) + 4kb + c16%4
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch < nch) {
+            const int c0 = seg_lo + ch * kChunk;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int slot = min(c0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), last);
+#pragma unroll
+                for (int kk = 0; kk < kKSteps; ++kk)
+                    kf[ch][kb][kk] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(kcache + (size_t)slot * D + kk * 32 + g16 * 8));
+            }
+        }
+    }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         if (ch < nch) {
@@ -151,14 +166,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
                 const int piece = (lane % kPieces) ^ swz_v(r);
                 __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vcache + (size_t)slot * D + piece * 8),
                                                  SWA_LDS_PTR(&vlds[ch][1024 * i]), 16, 0, 0);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int slot = min(c0 + 8 * (c16 >> 2) + 4 * kb + (c16 & 3), last);
-#pragma unroll
-                for (int kk = 0; kk < kKSteps; ++kk)
-                    kf[ch][kb][kk] = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(kcache + (size_t)slot * D + kk * 32 + g16 * 8));
             }
         }
     }
@@ -172,23 +179,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
         *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + lane * 8) = vn_piece;
     }
 
-    const __bf16 one_or_zero = static_cast<__bf16>(c16 == 0 ? 1.f : 0.f);
-    const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
-                             one_or_zero, one_or_zero, one_or_zero, one_or_zero};
-    f32x4 o[kDBlocks];
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;  // log2 units, per column; probabilities stay below 2^8
-    const int vt_row0 = 8 * g16 + (c16 >> 2);
-    const int vt_half = 8 * (c16 & 1);
-    const int vt_pbit = (c16 >> 1) & 1;
-
+    // ---- scores of the whole segment (at most 96 slots, all in registers at once, so the
+    // softmax takes the exact maximum in one pass: no running rescale).
+    f32x4 sacc[NCH][2];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        if (ch >= nch)
-            break;
         const int c0 = seg_lo + ch * kChunk;
         if (fused && slot_t >= c0 && slot_t < c0 + kChunk) {
 #pragma unroll
@@ -199,65 +194,100 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
                     kf[ch][kb][kk] = mine ? knf[kk] : kf[ch][kb][kk];
             }
         }
-        f32x4 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sacc[ch][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ch < nch) {
 #pragma unroll
-            for (int kk = 0; kk < kKSteps; ++kk)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ch][kb][kk], qf[kk], sacc[kb], 0, 0, 0);
+                for (int kk = 0; kk < kKSteps; ++kk)
+                    sacc[ch][kb] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ch][kb][kk], qf[kk], sacc[ch][kb], 0, 0, 0);
+            }
         }
-        // Mask: slots past the segment, and before the ring wraps the slots outside A(t).
-        float mx = -INFINITY;
+    }
+    // Mask: before the ring wraps, the slots outside A(t) and past the segment; after, only
+    // the slots past the segment (rows the loads filled with the segment's last slot).  Then
+    // the column maximum over the four lane groups.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int c0 = seg_lo + ch * kChunk;
+        if (!wrapped) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sj = c0 + 8 * g16 + 4 * kb + j;
+                    sacc[ch][kb][j] = ((sj < seg_hi) & sm.valid32(sj)) ? sacc[ch][kb][j] : -INFINITY;
+                }
+        } else if (c0 + kChunk > seg_hi) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sacc[ch][kb][j] = c0 + 8 * g16 + 4 * kb + j < seg_hi ? sacc[ch][kb][j] : -INFINITY;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
+            mx = fmaxf(mx, fmaxf(fmaxf(sacc[ch][kb][0], sacc[ch][kb][1]), fmaxf(sacc[ch][kb][2], sacc[ch][kb][3])));
+    }
+    mx = max_over_groups(mx);
+    const float m_ref = mx * a.scale_log2;  // log2 units; -inf when the column sees no key
+    const float m_use = mx == -INFINITY ? 0.f : m_ref;
+    // P^T (bf16, B operand of PV) and its column sums from the same rounded values: a
+    // constant A fragment whose row 0 is all ones makes one MFMA per chunk add the column
+    // sum into lane group 0.
+    const __bf16 one_or_zero = static_cast<__bf16>(c16 == 0 ? 1.f : 0.f);
+    const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
+                             one_or_zero, one_or_zero, one_or_zero, one_or_zero};
+    bf16x8 pf[NCH];
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sj = c0 + 8 * g16 + 4 * kb + j;
-                const bool ok = sj < seg_hi && (wrapped || sm.valid(sj));
-                sacc[kb][j] = ok ? sacc[kb][j] : -INFINITY;
-                mx = fmaxf(mx, sacc[kb][j]);
-            }
-        mx = max_over_groups(mx);
-        // Online softmax of the column with lazy rescaling (threshold 8 in log2 units).
-        const float m_tile = mx * a.scale_log2;
-        if (__any(m_tile > m_ref + 8.f)) {
-            const float m_new = fmaxf(m_ref, m_tile);
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db)
-                o[db] *= alpha;
-            lsum *= alpha;
-            m_ref = m_new;
-        }
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        bf16x8 pf;
+    for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                pf[4 * kb + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][j], a.scale_log2, -m_use)));
-        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf, lsum, 0, 0, 0);
+                pf[ch][4 * kb + j] =
+                    static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[ch][kb][j], a.scale_log2, -m_use)));
+        if (ch < nch)
+            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[ch], lsum, 0, 0, 0);
+    }
 
-        unsigned char *vbuf = vlds[ch];
-        if (ch == 0)
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): every V row is in LDS
-        // V fix-ups in LDS (LDS operations of a wave complete in order, so the transposed
-        // reads below see them): zero the rows of slots outside A(t) (before the ring wraps,
-        // and the padding past the segment), and put the new token's row over its slot.
-        if (!wrapped || c0 + kChunk > seg_hi) {
+    // ---- V: wait for the rows in LDS, fix them up, O^T += V^T P^T per chunk.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): every V row is in LDS
+    // Fix-ups (LDS operations of a wave complete in order, so the transposed reads below see
+    // them): before the ring wraps, zero the rows of slots outside A(t) and past the segment
+    // (after it wraps, every row holds finite cache data and the masked ones get weight 0);
+    // put the new token's row over its slot.
+    if (!wrapped) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            const int c0 = seg_lo + ch * kChunk;
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
-                const int r = kRowsPerLoad * i + lane / kPieces;
-                const int sj = c0 + r;
-                if (!(sj < seg_hi && (wrapped || sm.valid(sj))))
-                    *reinterpret_cast<u32x4 *>(vbuf + 1024 * i + 16 * lane) = u32x4{0u, 0u, 0u, 0u};  // row r
+                const int sj = c0 + kRowsPerLoad * i + lane / kPieces;
+                if (ch < nch && !((sj < seg_hi) & sm.valid32(sj)))
+                    *reinterpret_cast<u32x4 *>(&vlds[ch][1024 * i + 16 * lane]) = u32x4{0u, 0u, 0u, 0u};
             }
         }
-        if (fused && slot_t >= c0 && slot_t < c0 + kChunk && lane < kPieces) {
-            const int r = slot_t - c0;
-            *reinterpret_cast<u32x4 *>(vbuf + r * kRowBytes + 16 * (lane ^ swz_v(r))) = vn_piece;
-        }
+    }
+    if (fused && slot_t >= seg_lo && slot_t < seg_hi && lane < kPieces) {
+        const int ch = (slot_t - seg_lo) / kChunk, r = (slot_t - seg_lo) % kChunk;
+        *reinterpret_cast<u32x4 *>(&vlds[0][0] + ch * kChunk * kRowBytes + r * kRowBytes + 16 * (lane ^ swz_v(r))) =
+            vn_piece;
+    }
+    const int vt_row0 = 8 * g16 + (c16 >> 2);
+    const int vt_half = 8 * (c16 & 1);
+    const int vt_pbit = (c16 >> 1) & 1;
+    f32x4 o[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+        o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch >= nch)
+            break;
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
             bf16x8 af;
@@ -265,14 +295,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
             for (int h = 0; h < 2; ++h) {
                 const int row = 4 * h + vt_row0;
                 const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ swz_v(row)) + vt_half;
-                const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(vbuf + off));
+                const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(&vlds[ch][off]));
                 const bf16x4 y = __builtin_bit_cast(bf16x4, x);
                 af[4 * h + 0] = y[0];
                 af[4 * h + 1] = y[1];
                 af[4 * h + 2] = y[2];
                 af[4 * h + 3] = y[3];
             }
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[ch], o[db], 0, 0, 0);
         }
     }
 

@@ -99,6 +99,7 @@ __device__ __forceinline__ int64_t append_slot(int64_t p, int s, int w_loc)
 struct SlotMap {
     int64_t t;
     int s, w_loc, t_mod;
+    int t_clamp;  // min(t, 2^31 - 1), or -1 for t < 0: enough to decide validity in 32 bits
     __device__ __forceinline__ SlotMap(int64_t t_, int s_, int w_loc_) : t(t_), s(s_), w_loc(w_loc_)
     {
         if (t_ < 0)
@@ -107,6 +108,7 @@ struct SlotMap {
             t_mod = (int)((uint32_t)t_ % (uint32_t)w_loc_);
         else
             t_mod = (int)(t_ % w_loc_);
+        t_clamp = t_ < 0 ? -1 : (t_ > 0x7fffffffLL ? 0x7fffffff : (int)t_);
     }
     __device__ __forceinline__ int64_t position(int j) const
     {
@@ -121,6 +123,15 @@ struct SlotMap {
         return (p >= s && p >= 0) ? p : -1;
     }
     __device__ __forceinline__ bool valid(int j) const { return position(j) >= 0; }
+    // valid(j) in 32-bit arithmetic, branch-free: a sink slot j < s is valid iff j <= t; a
+    // ring slot holds p = t - back with back = (t_mod - (j - s)) mod w_loc < w_loc, valid iff
+    // p >= s, i.e. back <= t - s (t_clamp keeps that exact when t >= 2^31, as back < 2^31).
+    __device__ __forceinline__ bool valid32(int j) const
+    {
+        int back = t_mod - (j - s);
+        back += back < 0 ? w_loc : 0;
+        return ((j < s) & (j <= t_clamp)) | ((j >= s) & (back <= t_clamp - s));
+    }
     // slot of position t itself (t >= 0)
     __device__ __forceinline__ int slot_of_t() const { return t < s ? (int)t : s + t_mod; }
 };
