@@ -120,7 +120,7 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, i
  * max(s, t-w_loc+1) .. t.  Slot validity is derived from t alone: a slot that holds no
  * position of A(t) (never written yet, or stale from earlier use of the cache) contributes
  * nothing, whatever bytes it holds.  The cache is read in storage order; the softmax sum
- * does not depend on order.  When s + w_loc exceeds 128 slots the slot range is split over
+ * does not depend on order.  When s + w_loc exceeds 96 slots the slot range is split over
  * workgroups and the partial (max, sum, weighted values) are merged in a fixed order.
  *
  *   q          bf16 [B][Hq][d]   (in)
