@@ -15,7 +15,9 @@ decode replay.
 Printed JSON line (one):
   value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time
   decode           tokens/s of the decode leg and its HBM figures; other_batches: the same
-                   decode graph timed alone at batch 1 and batch 1024 (outside the steps)
+                   decode graph timed alone at batch 1, batch 1024, and batch 64 with the steps
+                   rotating over 32 caches (570 MB, so every step reads HBM), outside the steps
+  prefill.cold_*   the prefill with L2 and Infinity Cache evicted before each launch
   roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
                    launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
                    38.5 useful flop per algorithmic byte, far below the 315 flop/byte ridge)
@@ -73,10 +75,15 @@ def parse():
     ap.add_argument("--decode-tokens", type=int, default=256)
     ap.add_argument("--decode-start", type=int, default=2 ** 18)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode-points", action="store_true", help="skip the batch 1 and 1024 decode points")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the steps (other decode batches, cold prefill)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cores))")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--prefill-only", default="", help="only time this prefill workload (profiling)")
+    ap.add_argument("--cold", action="store_true", help="with --prefill-only: evict the caches before each launch")
+    ap.add_argument("--decode-only", type=int, default=0, help="only time the decode graph at this batch (profiling)")
+    ap.add_argument("--cache-sets", type=int, default=1, help="with --decode-only: caches the steps rotate over")
     return ap.parse_args()
 
 
@@ -113,12 +120,14 @@ def cpu_baseline(wl, q, k, v, threads: int, min_seconds: float = 10.0):
                       f"Hkv={wl.Hkv}, d={wl.d}, SWA({wl.w},{wl.s})) in fp64, {dt:.1f} s"}
 
 
-def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev):
-    """A HIP graph of T decode steps of workload dw at batch B (positions P .. P+T-1), each step
-    one swa_append_decode_step (append the token's K/V to its slot and attend), and a function
-    that restores the cache to its state after position P-1 (run it before every replay, so
-    each replay decodes the same tokens).  Every input is seeded: the cache holds the sinks and
-    positions P-w_loc .. P-1."""
+def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev, n_sets: int = 1):
+    """A HIP graph of T decode steps of workload dw at batch B, each step one
+    swa_append_decode_step (append the token's K/V to its slot and attend), and a function that
+    restores the caches to their state after position P-1 (run it before every replay, so each
+    replay decodes the same tokens).  Every input is seeded: a cache holds the sinks and
+    positions P-w_loc .. P-1.  With n_sets > 1 the steps rotate over that many independent
+    caches (step i uses cache i % n_sets at position P + i // n_sets), so that consecutive steps
+    never find their cache in the Infinity Cache once n_sets caches exceed it."""
     import torch
 
     w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
@@ -131,22 +140,27 @@ def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev):
                   torch.zeros(B, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
     swa.kv_append(kc, vc, sk[:, dw.s:].contiguous().to(dev), sv[:, dw.s:].contiguous().to(dev),
                   torch.full((B,), P - w_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
-    dq = torch.stack([inputs.q_at(dw.seed, P + i, B, dw.Hq, dw.d, dw.std) for i in range(T)]).to(dev)
-    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(T)]
-    dk = torch.stack([x[0] for x in kvs]).to(dev)  # [T][B][Hkv][d]
-    dv = torch.stack([x[1] for x in kvs]).to(dev)
-    dpos = (P + torch.arange(T, dtype=torch.int64)).repeat_interleave(B).view(T, B).to(dev)
-    dout = torch.empty((T, B, dw.Hq, dw.d), dtype=torch.float32, device=dev)
     snap_k, snap_v = kc.clone(), vc.clone()
+    caches = [(kc, vc)] + [(snap_k.clone(), snap_v.clone()) for _ in range(n_sets - 1)]
+    n_pos = (T + n_sets - 1) // n_sets
+    dq = torch.stack([inputs.q_at(dw.seed, P + i, B, dw.Hq, dw.d, dw.std) for i in range(n_pos)]).to(dev)
+    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(n_pos)]
+    dk = torch.stack([x[0] for x in kvs]).to(dev)  # [n_pos][B][Hkv][d]
+    dv = torch.stack([x[1] for x in kvs]).to(dev)
+    dpos = (P + torch.arange(n_pos, dtype=torch.int64)).repeat_interleave(B).view(n_pos, B).to(dev)
+    dout = torch.empty((T, B, dw.Hq, dw.d), dtype=torch.float32, device=dev)
 
     def steps():
         for i in range(T):
-            swa.append_decode_step(dq[i], kc, vc, dk[i], dv[i], dpos[i], dw.w, dw.s, dw.scale, dw.conv,
+            ck, cv = caches[i % n_sets]
+            j = i // n_sets
+            swa.append_decode_step(dq[j], ck, cv, dk[j], dv[j], dpos[j], dw.w, dw.s, dw.scale, dw.conv,
                                    out=dout[i], workspace=ws)
 
     def restore():
-        kc.copy_(snap_k)
-        vc.copy_(snap_v)
+        for ck, cv in caches:
+            ck.copy_(snap_k)
+            cv.copy_(snap_v)
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())
@@ -162,11 +176,11 @@ def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev):
     return graph, restore
 
 
-def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 5):
+def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 5, n_sets: int = 1):
     """Per-token step time of the decode graph at batch B (not part of the bench step)."""
     import torch
 
-    graph, restore = decode_graph(swa, inputs, dw, B, T, P, dev)
+    graph, restore = decode_graph(swa, inputs, dw, B, T, P, dev, n_sets)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ms = []
     for _ in range(reps + 1):
@@ -180,8 +194,77 @@ def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 
     w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
     kv = acc.decode_kv_bytes(B, dw.Hkv, dw.d, acc.decode_keys(P, w_loc, dw.s))
     gbs = kv / (step_us * 1e-6) / 1e9
-    return {"B": B, "us_per_token_step": round(step_us, 3), "tokens_per_s": round(B / (step_us * 1e-6), 1),
-            "kv_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5)}
+    rec = {"B": B, "us_per_token_step": round(step_us, 3), "tokens_per_s": round(B / (step_us * 1e-6), 1),
+           "kv_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5)}
+    if n_sets > 1:
+        rec["cache_sets"] = n_sets
+    return rec
+
+
+def flush_buffer(dev, mib: int = 512):
+    """A buffer whose fill evicts the 4 MB L2s and the 256 MB Infinity Cache."""
+    import torch
+
+    return torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+
+def prefill_timing(swa, wl, qg, kg, vg, out, reps: int, warmup: int, flush=None):
+    """Kernel-stamped launch times (ms) of `reps` prefills; with `flush`, the caches are
+    evicted (the buffer is overwritten) before every launch."""
+    import torch
+
+    for _ in range(warmup):
+        swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(reps)] for _ in range(2)]
+    for e in evs[0] + evs[1]:
+        e.record()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        if flush is not None:
+            flush.fill_(float(i))
+        swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out, events=(evs[0][i], evs[1][i]))
+    torch.cuda.synchronize()
+    return [evs[0][i].elapsed_time(evs[1][i]) for i in range(reps)]
+
+
+def prefill_only(args, dev):
+    """--prefill-only WORKLOAD: time that prefill alone (warm, and with --cold caches evicted
+    before every launch) and print one JSON line."""
+    import torch
+
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import accounting as acc
+    from sliding_window_attention_02_amd import inputs
+
+    wl = inputs.prefill_workloads()[args.prefill_only]
+    w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+    q, k, v = inputs.prefill_inputs(wl)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    flush = flush_buffer(dev) if args.cold else None
+    ms = prefill_timing(swa, wl, qg, kg, vg, out, args.steps, args.warmup, flush)
+    mean = sum(ms) / len(ms)
+    useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    algo = acc.prefill_bytes(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d)
+    tf = useful / (mean * 1e-3) / 1e12
+    gbs = algo / (mean * 1e-3) / 1e9
+    print(json.dumps({"workload": wl.name, "caches": "evicted before each launch" if args.cold else "warm",
+                      "launches": len(ms), "mean_launch_us": round(mean * 1e3, 3),
+                      "useful_tflops": round(tf, 3), "frac_of_bf16_mfma_peak": round(tf / acc.PEAK_BF16_TFLOPS, 5),
+                      "algorithmic_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5)}),
+          flush=True)
+
+
+def decode_only(args, dev):
+    """--decode-only B: time the decode graph at batch B and print one JSON line."""
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import accounting as acc
+    from sliding_window_attention_02_amd import inputs
+
+    dw = inputs.decode_workloads()["decode_swa64_4_b64"]
+    rec = decode_point(swa, inputs, acc, dw, args.decode_only, args.decode_tokens, args.decode_start, dev,
+                       reps=args.steps, n_sets=args.cache_sets)
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -205,6 +288,12 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.prefill_only:
+        prefill_only(args, dev)
+        return
+    if args.decode_only:
+        decode_only(args, dev)
+        return
 
     # ---------------------------------------------------------------- prefill inputs
     wl = inputs.prefill_workloads()[args.workload]
@@ -269,9 +358,17 @@ def main():
     # other configured batch) and batch 1024, where the cache (285 MB) no longer fits the
     # Infinity Cache and the step is bound by HBM rather than by latency.
     points = []
-    if not args.no_decode_points:
+    cold_mean = None
+    if not args.no_extras:
         for b, t in ((1, 256), (1024, 32)):
             points.append(decode_point(swa, inputs, acc, dw, b, t, P, dev))
+        # Batch 64 with the steps rotating over 32 caches (570 MB, over twice the Infinity
+        # Cache): every step reads its cache from HBM.
+        points.append(decode_point(swa, inputs, acc, dw, DB, T, P, dev, n_sets=32))
+        # The same prefill with the caches evicted (a 512 MiB buffer overwritten) before each
+        # launch, so its inputs come from HBM rather than from the Infinity Cache.
+        cold_ms = prefill_timing(swa, wl, qg, kg, vg, out, max(10, K // 2), 2, flush_buffer(dev))
+        cold_mean = sum(cold_ms) / len(cold_ms)
 
     base = None
     if not args.no_cpu_baseline:
@@ -306,6 +403,8 @@ def main():
             "useful_tflops": round(tflops, 3),
             "frac_of_bf16_mfma_peak": round(tflops / acc.PEAK_BF16_TFLOPS, 5),
             "executed_mfma_tflops": round(executed / (pre_mean * 1e-3) / 1e12, 3),
+            "cold_mean_launch_us": round(cold_mean * 1e3, 3) if cold_mean else None,
+            "cold_useful_tflops": round(useful / (cold_mean * 1e-3) / 1e12, 3) if cold_mean else None,
             "useful_gflop_per_launch": round(useful / 1e9, 4),
             "algorithmic_mb_per_launch": round(algo_bytes / 1e6, 3),
         },
