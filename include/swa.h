@@ -150,6 +150,39 @@ int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const vo
                            int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * swa_prefill_chunk -- prefill of one prompt chunk against the bounded cache, then the chunk
+ * appended to it: the long-prompt procedure of page "从长文档摘要说起" (wiblog.cn), section
+ * "长 Prompt 的分块处理与工程实现" and its flow description (a long input is processed in
+ * consecutive chunks, each attending within the window, with the cache rotating between chunks
+ * so that only the window's keys stay cached).
+ *
+ * The cache holds the state after position pos0 - 1 (every sequence at the same position).
+ * For each b and i < C, out[b][i][h] is the SWA(w,s) attention row pos0 + i of q[b][i][h] over
+ * the sinks and window keys in the cache and the chunk's own keys pos0 .. pos0 + i: the same
+ * row a whole-sequence swa_prefill gives.  Afterwards the cache holds the state after
+ * pos0 + C - 1 (as swa_kv_append of the chunk would leave it).  Any C >= 1 works (the pages
+ * keep chunks within the window; larger chunks are fine here).
+ *
+ *   q           bf16 [B][C][Hq][d]   (in)   the chunk's queries
+ *   k, v        bf16 [B][C][Hkv][d]  (in)   the chunk's keys and values
+ *   k_cache,    bf16 [B][Hkv][s + w_loc][d] (in/out), the layout swa_kv_append writes
+ *   v_cache
+ *   out         fp32 [B][C][Hq][d]   (out)
+ *   pos0        position of the chunk's first token, >= 0 (host value)
+ *   workspace   device scratch of at least swa_prefill_chunk_workspace_bytes(...) bytes
+ *               (the chunk's keys with the cached ones they see, gathered in position order);
+ *               contents on entry are ignored.
+ * Three launches on `stream` (gather, attend, append); no synchronisation.
+ * Errors: as swa_prefill, plus SWA_EINVAL for C < 1, pos0 < 0, or a missing, misaligned or
+ * too-small workspace; SWA_EUNSUPPORTED when s + w_loc - 1 + C rows of one sequence exceed
+ * 2^31-1 elements.
+ */
+size_t swa_prefill_chunk_workspace_bytes(int B, int Hkv, int C, int d, int w, int s, int conv);
+int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache,
+                      float *out, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s,
+                      float scale, int conv, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char *swa_last_error(void);
 

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     TOTAL,
     SwaError,
     alloc_cache,
+    alloc_chunk_workspace,
     alloc_workspace,
     append_decode_step,
     debug_decode_slots,
@@ -19,4 +20,6 @@ from .binding import (  # noqa: F401
     last_error,
     local_window,
     prefill,
+    prefill_chunk,
+    prefill_chunk_workspace_bytes,
 )

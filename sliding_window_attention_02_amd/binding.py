@@ -30,6 +30,8 @@ EXPORTS = (
     "swa_decode_workspace_bytes",
     "swa_decode_step",
     "swa_append_decode_step",
+    "swa_prefill_chunk_workspace_bytes",
+    "swa_prefill_chunk",
     "swa_last_error",
     "swa_debug_prefill_mask",
     "swa_debug_decode_slots",
@@ -66,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.swa_append_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                          vp]
     L.swa_append_decode_step.restype = i32
+    i64 = ctypes.c_int64
+    L.swa_prefill_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.swa_prefill_chunk_workspace_bytes.restype = sz
+    L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                    sz, vp]
+    L.swa_prefill_chunk.restype = i32
     L.swa_last_error.argtypes = []
     L.swa_last_error.restype = ctypes.c_char_p
     L.swa_debug_prefill_mask.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp]
@@ -215,6 +223,42 @@ def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, s
     _check(lib().swa_append_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
                                         v_new.data_ptr(), out.data_ptr(), pos.data_ptr(), B, Hq, Hkv, d, w, s, scale,
                                         conv, ws_ptr or None, ws_bytes, _stream(q)))
+    return out
+
+
+def prefill_chunk_workspace_bytes(B: int, Hkv: int, C: int, d: int, w: int, s: int, conv: int = ADDITIVE) -> int:
+    return int(lib().swa_prefill_chunk_workspace_bytes(B, Hkv, C, d, w, s, conv))
+
+
+def alloc_chunk_workspace(B: int, Hkv: int, C: int, d: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
+    n = prefill_chunk_workspace_bytes(B, Hkv, C, d, w, s, conv)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: float | None = None,
+                  conv: int = ADDITIVE, out=None, workspace=None):
+    """Prefill of a chunk at positions pos0 .. pos0+C-1 against the cache (state after pos0-1),
+    then the chunk appended.  q bf16 [B][C][Hq][d], k/v bf16 [B][C][Hkv][d] -> fp32 [B][C][Hq][d]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B][C][Hq][d] and k, v [B][C][Hkv][d]")
+    B, C, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, C, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, C, Hkv, d))
+    n_slots = s + local_window(w, s, conv)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, n_slots, d))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, n_slots, d))
+    if out is None:
+        out = torch.empty((B, C, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, C, Hq, d))
+    if workspace is None:
+        workspace = alloc_chunk_workspace(B, Hkv, C, d, w, s, conv, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   out.data_ptr(), int(pos0), B, Hq, Hkv, C, d, w, s, scale, conv,
+                                   workspace.data_ptr(), workspace.numel(), _stream(q)))
     return out
 
 

@@ -21,9 +21,11 @@ struct PrefillGeometry {
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
 
 // start/stop: optional events stamped by the kernel dispatch itself (null: plain launch).
+// Lq, q_lo: when Lq >= 0, only the queries at key positions q_lo .. q_lo + Lq - 1 are computed;
+// q and out then hold Lq rows per sequence (k and v hold L).  Lq < 0: every position.
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
-                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int Lq = -1, int q_lo = 0);
 
 hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w_loc, int s,
                                      hipStream_t stream);
@@ -39,15 +41,34 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s);
 
+// pos: device [B] first positions, or null to append every sequence at pos0.
 hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                             const int64_t *pos, int B, int Hkv, int d, int w_loc, int s, int n_new,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t pos0 = 0);
 
 // k_new / v_new: null for a plain decode step; otherwise the new token of each sequence
 // ([B][Hkv][d]) is written to its slot and attended in the same launch.
 hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                          float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
                          float scale, void *workspace, const DecodePlan &plan, hipStream_t stream);
+
+// ----------------------------------------------------------------------- chunked prefill
+//
+// A chunk of C tokens at positions pos0 .. pos0 + C - 1 against a cache that holds the state
+// after pos0 - 1.  Its keys, in position order, are ns cached sinks, nw cached window positions
+// (pos0 - nw .. pos0 - 1) and the chunk itself: a sequence of rows = ns + nw + C keys whose
+// queries are the last C, on which the SWA(w,s) predicate holds unchanged (the window rows
+// hold no sink positions and run contiguously into the chunk).
+struct ChunkPlan {
+    int ns;    // min(s, pos0)
+    int nw;    // min(w_loc - 1, pos0 - s) when pos0 > s, else 0
+    int rows;  // ns + nw + C
+};
+ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s);
+
+hipError_t launch_chunk_gather(void *k_scratch, void *v_scratch, const void *k_cache, const void *v_cache,
+                               const void *k_new, const void *v_new, int64_t pos0, const ChunkPlan &plan, int B,
+                               int Hkv, int d, int w_loc, int s, int C, hipStream_t stream);
 
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,
                                      hipStream_t stream);

@@ -58,6 +58,7 @@ struct PrefillArgs {
     const uint16_t *v;
     float *out;
     int L, Hq, Hkv, G, Gw, Tm, n_qtiles, n_hslices;
+    int Lq, q_lo;  // queries are key positions q_lo .. q_lo + Lq - 1 (rows 0 .. Lq-1 of q, out)
     int w_loc, s;
     float scale_log2;
     int nblocks;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const int c16 = lane & 15;  // column inside a 16-wide MFMA block
 
     const BlockCoord bc = block_coord(a);
-    const int t0 = bc.qt * a.Tm;
+    const int t0 = a.q_lo + bc.qt * a.Tm;
     const int t1 = min(t0 + a.Tm - 1, a.L - 1);
     const float c = a.scale_log2;
 
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     bf16x8 qf[2][kKSteps];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const uint16_t *qrow =
-            a.q + (((size_t)bc.b * a.L + (valid[qb] ? tok[qb] : 0)) * a.Hq + (valid[qb] ? head[qb] : 0)) * D;
+        const uint16_t *qrow = a.q + (((size_t)bc.b * a.Lq + (valid[qb] ? tok[qb] - a.q_lo : 0)) * a.Hq +
+                                      (valid[qb] ? head[qb] : 0)) * D;
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
             u32x4 x = {0u, 0u, 0u, 0u};
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         l += __shfl_xor(l, 32);
         const float inv = 1.f / l;
         if (valid[qb]) {
-            float *orow = a.out + (((size_t)bc.b * a.L + tok[qb]) * a.Hq + head[qb]) * D;
+            float *orow = a.out + (((size_t)bc.b * a.Lq + tok[qb] - a.q_lo) * a.Hq + head[qb]) * D;
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db)
                 // Plain stores: L2 merges the 64-byte pieces of a row into whole lines
@@ -474,15 +475,21 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
-                          hipEvent_t start, hipEvent_t stop)
+                          hipEvent_t start, hipEvent_t stop, int Lq, int q_lo)
 {
-    const PrefillGeometry g = prefill_geometry(L, Hq, Hkv);
+    if (Lq < 0) {
+        Lq = L;
+        q_lo = 0;
+    }
+    const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     a.out = out;
     a.L = L;
+    a.Lq = Lq;
+    a.q_lo = q_lo;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = g.G;

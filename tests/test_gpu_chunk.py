@@ -1,0 +1,141 @@
+"""GPU parity of swa_prefill_chunk (chunked prefill into the bounded cache) against the fp64
+oracle, through the C ABI.
+
+A sequence fed chunk by chunk must give, row for row, the whole-sequence SWA(w,s) prefill
+(max abs error <= 2e-2), from an empty cache (filled with NaN, which must never reach a
+result) through sink-fill, ring-fill and wrap-around, with chunks shorter and longer than
+the window; the cache afterwards must equal, bit for bit, the cache that appending every
+position one by one leaves.  Far from the start (positions past 2^31) each row is checked
+against the oracle's decode row over the explicit set of keys the row may see.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_attention_02_amd as swa
+from oracle import oracle as orc
+from sliding_window_attention_02_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def sequence(seed, B, L, Hq, Hkv, d, std=1.0):
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed, std=std, sink_boost_n=4, sink_boost=4.0)
+    return q, k, v  # bf16 [B][L][H][d] on the CPU
+
+
+def nan_cache(B, Hkv, d, w, s, conv):
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s, conv)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    return kc, vc
+
+
+CASES = [
+    # B, Hq, Hkv, d, w, s, conv, chunk sizes (their sum is L)
+    (2, 8, 2, 128, 16, 4, 0, [1, 3, 16, 40, 7, 100, 33]),
+    (1, 4, 4, 64, 8, 0, 0, [8] * 12 + [4]),
+    (3, 12, 4, 128, 20, 4, 1, [2, 2, 50, 96]),  # the first chunks end inside the sinks
+    (1, 32, 8, 128, 64, 4, 0, [64] * 9 + [24]),  # Llama-shaped heads, chunks of the window
+    (2, 8, 8, 128, 300, 2, 0, [100, 156]),  # window longer than the sequence: full causal
+    (1, 8, 2, 64, 33, 9, 0, [5, 61, 1, 1, 90]),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv,chunks", CASES)
+def test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks):
+    L = sum(chunks)
+    say("chunked", B, Hq, Hkv, d, w, s, conv, chunks)
+    q, k, v = sequence(2024, B, L, Hq, Hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    kc, vc = nan_cache(B, Hkv, d, w, s, conv)
+    outs, p0 = [], 0
+    for C in chunks:
+        ws = swa.alloc_chunk_workspace(B, Hkv, C, d, w, s, conv)
+        sl = slice(p0, p0 + C)
+        outs.append(swa.prefill_chunk(qg[:, sl].contiguous(), kg[:, sl].contiguous(), vg[:, sl].contiguous(),
+                                      kc, vc, p0, w, s, scale, conv, workspace=ws))
+        p0 += C
+    got = torch.cat(outs, dim=1).cpu().numpy()
+    err = np.abs(got - ref)
+    say(f"max {err.max():.3e}")
+    assert np.isfinite(got).all() and err.max() <= TOL
+    # The cache equals the one that appending every position one by one leaves (bitwise,
+    # NaN-filled slots included).
+    kc2, vc2 = nan_cache(B, Hkv, d, w, s, conv)
+    for t in range(L):
+        pos = torch.full((B,), t, dtype=torch.int64, device="cuda")
+        swa.kv_append(kc2, vc2, kg[:, t:t + 1].contiguous(), vg[:, t:t + 1].contiguous(), pos, w, s, conv)
+    assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
+
+
+@pytest.mark.parametrize("P", [2 ** 31 + 100, 2 ** 18])
+def test_chunk_far_from_start_matches_decode_rows(P):
+    """The cache holds the state after P-1 (sinks and the window before P); a chunk of 50
+    tokens at P; every row against the oracle's decode row over the keys it may see."""
+    B, Hq, Hkv, d, w, s, C = 2, 8, 2, 128, 24, 4, 50
+    w_loc = w
+    say("chunk-far", P)
+    seed = 77
+    gen = dict(B=B, Hkv=Hkv, d=d, std=1.0, sink_boost_n=4, sink_boost=4.0)
+    prev = list(range(s)) + list(range(P - w_loc, P))
+    pk, pv = inputs.kv_span(seed, prev, **gen)
+    ck, cv = inputs.kv_span(seed, list(range(P, P + C)), **gen)
+    cq = torch.stack([inputs.q_at(seed, P + i, B, Hq, d) for i in range(C)], dim=1)
+    kc, vc = nan_cache(B, Hkv, d, w, s, 0)
+    swa.kv_append(kc, vc, pk[:, :s].contiguous().cuda(), pv[:, :s].contiguous().cuda(),
+                  torch.zeros(B, dtype=torch.int64, device="cuda"), w, s)
+    swa.kv_append(kc, vc, pk[:, s:].contiguous().cuda(), pv[:, s:].contiguous().cuda(),
+                  torch.full((B,), P - w_loc, dtype=torch.int64, device="cuda"), w, s)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.prefill_chunk(cq.cuda(), ck.cuda(), cv.cuda(), kc, vc, P, w, s, scale).cpu().numpy()
+    pos_all = np.array(prev + list(range(P, P + C)), dtype=np.int64)
+    k_all = torch.cat([pk, ck], dim=1)
+    v_all = torch.cat([pv, cv], dim=1)
+    worst = 0.0
+    for b in range(B):
+        for i in range(C):
+            t = P + i
+            ref, kept = orc.decode_row(f64(cq[b, i]), pos_all, f64(k_all[b]), f64(v_all[b]), t, w, s, scale)
+            assert kept == min(t + 1, w_loc + s)
+            worst = max(worst, float(np.abs(out[b, i] - ref).max()))
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_chunk_of_one_token_equals_decode_step():
+    """A one-token chunk is a decode step: same row (to the tolerance; different kernels) and
+    the same cache afterwards."""
+    B, Hq, Hkv, d, w, s = 2, 32, 8, 128, 64, 4
+    L = 150
+    q, k, v = sequence(5, B, L, Hq, Hkv, d)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    kc1, vc1 = nan_cache(B, Hkv, d, w, s, 0)
+    kc2, vc2 = nan_cache(B, Hkv, d, w, s, 0)
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s)
+    worst = 0.0
+    for t in range(L):
+        sl = slice(t, t + 1)
+        a = swa.prefill_chunk(qg[:, sl].contiguous(), kg[:, sl].contiguous(), vg[:, sl].contiguous(), kc1, vc1,
+                              t, w, s)[:, 0]
+        pos = torch.full((B,), t, dtype=torch.int64, device="cuda")
+        b = swa.append_decode_step(qg[:, t].contiguous(), kc2, vc2, kg[:, t].contiguous(), vg[:, t].contiguous(),
+                                   pos, w, s, workspace=ws)
+        worst = max(worst, float((a - b).abs().max()))
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
