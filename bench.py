@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--prefill-only", default="", help="only time this prefill workload (profiling)")
     ap.add_argument("--cold", action="store_true", help="with --prefill-only: evict the caches before each launch")
     ap.add_argument("--decode-only", type=int, default=0, help="only time the decode graph at this batch (profiling)")
+    ap.add_argument("--chunked", default="", help="only time this prefill workload fed in chunks (swa_prefill_chunk)")
+    ap.add_argument("--chunk", type=int, default=4096, help="with --chunked: tokens per chunk")
     ap.add_argument("--cache-sets", type=int, default=1, help="with --decode-only: caches the steps rotate over")
     return ap.parse_args()
 
@@ -255,6 +257,64 @@ def prefill_only(args, dev):
           flush=True)
 
 
+def chunked_only(args, dev):
+    """--chunked WORKLOAD --chunk C: the workload's sequences fed to swa_prefill_chunk in chunks
+    of C tokens from an empty cache (every chunk call captured in one HIP graph; the cache is
+    cleared before each replay), against the whole-sequence prefill.  One JSON line."""
+    import torch
+
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import accounting as acc
+    from sliding_window_attention_02_amd import inputs
+
+    wl = inputs.prefill_workloads()[args.chunked]
+    w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+    C = args.chunk
+    q, k, v = inputs.prefill_inputs(wl)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    kc, vc = swa.alloc_cache(wl.B, wl.Hkv, wl.d, wl.w, wl.s, wl.conv, device=dev)
+    starts = list(range(0, wl.L, C))
+    pieces = [(p, min(C, wl.L - p)) for p in starts]
+    qs = [qg[:, p:p + n].contiguous() for p, n in pieces]
+    ks = [kg[:, p:p + n].contiguous() for p, n in pieces]
+    vs = [vg[:, p:p + n].contiguous() for p, n in pieces]
+    outs = [torch.empty((wl.B, n, wl.Hq, wl.d), dtype=torch.float32, device=dev) for _, n in pieces]
+    ws = swa.alloc_chunk_workspace(wl.B, wl.Hkv, C, wl.d, wl.w, wl.s, wl.conv, device=dev)
+
+    def run():
+        for i, (p, n) in enumerate(pieces):
+            swa.prefill_chunk(qs[i], ks[i], vs[i], kc, vc, p, wl.w, wl.s, wl.scale, wl.conv, out=outs[i], workspace=ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        run()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(args.warmup + args.steps):
+        kc.zero_()
+        vc.zero_()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    chunked = sum(ms[args.warmup:]) / args.steps
+    whole = sum(prefill_timing(swa, wl, qg, kg, vg, out, args.steps, args.warmup)) / args.steps
+    useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    print(json.dumps({"workload": wl.name, "chunk": C, "chunks": len(pieces), "chunked_ms": round(chunked, 4),
+                      "chunked_useful_tflops": round(useful / (chunked * 1e-3) / 1e12, 3),
+                      "whole_sequence_ms": round(whole, 4),
+                      "whole_sequence_useful_tflops": round(useful / (whole * 1e-3) / 1e12, 3),
+                      "chunked_over_whole": round(chunked / whole, 3)}), flush=True)
+
+
 def decode_only(args, dev):
     """--decode-only B: time the decode graph at batch B and print one JSON line."""
     import sliding_window_attention_02_amd as swa
@@ -293,6 +353,9 @@ def main():
         return
     if args.decode_only:
         decode_only(args, dev)
+        return
+    if args.chunked:
+        chunked_only(args, dev)
         return
 
     # ---------------------------------------------------------------- prefill inputs
