@@ -280,11 +280,10 @@ def chunked_only(args, dev):
     ks = [kg[:, p:p + n].contiguous() for p, n in pieces]
     vs = [vg[:, p:p + n].contiguous() for p, n in pieces]
     outs = [torch.empty((wl.B, n, wl.Hq, wl.d), dtype=torch.float32, device=dev) for _, n in pieces]
-    ws = swa.alloc_chunk_workspace(wl.B, wl.Hkv, C, wl.d, wl.w, wl.s, wl.conv, device=dev)
 
     def run():
         for i, (p, n) in enumerate(pieces):
-            swa.prefill_chunk(qs[i], ks[i], vs[i], kc, vc, p, wl.w, wl.s, wl.scale, wl.conv, out=outs[i], workspace=ws)
+            swa.prefill_chunk(qs[i], ks[i], vs[i], kc, vc, p, wl.w, wl.s, wl.scale, wl.conv, out=outs[i])
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())

@@ -170,18 +170,14 @@ int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const vo
  *   v_cache
  *   out         fp32 [B][C][Hq][d]   (out)
  *   pos0        position of the chunk's first token, >= 0 (host value)
- *   workspace   device scratch of at least swa_prefill_chunk_workspace_bytes(...) bytes
- *               (the chunk's keys with the cached ones they see, gathered in position order);
- *               contents on entry are ignored.
- * Three launches on `stream` (gather, attend, append); no synchronisation.
- * Errors: as swa_prefill, plus SWA_EINVAL for C < 1, pos0 < 0, or a missing, misaligned or
- * too-small workspace; SWA_EUNSUPPORTED when s + w_loc - 1 + C rows of one sequence exceed
- * 2^31-1 elements.
+ * Two launches on `stream` (attend, reading the cached keys in place; then append); no
+ * workspace, no synchronisation.
+ * Errors: as swa_prefill, plus SWA_EINVAL for C < 1 or pos0 < 0; SWA_EUNSUPPORTED when
+ * s + w_loc - 1 + C keys, or the C query rows, of one sequence exceed 2^31-1 elements.
  */
-size_t swa_prefill_chunk_workspace_bytes(int B, int Hkv, int C, int d, int w, int s, int conv);
 int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache,
                       float *out, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s,
-                      float scale, int conv, void *workspace, size_t workspace_bytes, void *stream);
+                      float scale, int conv, void *stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char *swa_last_error(void);

@@ -9,7 +9,6 @@ from .binding import (  # noqa: F401
     TOTAL,
     SwaError,
     alloc_cache,
-    alloc_chunk_workspace,
     alloc_workspace,
     append_decode_step,
     debug_decode_slots,
@@ -21,5 +20,4 @@ from .binding import (  # noqa: F401
     local_window,
     prefill,
     prefill_chunk,
-    prefill_chunk_workspace_bytes,
 )

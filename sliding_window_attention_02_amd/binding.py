@@ -30,7 +30,6 @@ EXPORTS = (
     "swa_decode_workspace_bytes",
     "swa_decode_step",
     "swa_append_decode_step",
-    "swa_prefill_chunk_workspace_bytes",
     "swa_prefill_chunk",
     "swa_last_error",
     "swa_debug_prefill_mask",
@@ -69,10 +68,7 @@ def lib() -> ctypes.CDLL:
                                          vp]
     L.swa_append_decode_step.restype = i32
     i64 = ctypes.c_int64
-    L.swa_prefill_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
-    L.swa_prefill_chunk_workspace_bytes.restype = sz
-    L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
-                                    sz, vp]
+    L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.swa_prefill_chunk.restype = i32
     L.swa_last_error.argtypes = []
     L.swa_last_error.restype = ctypes.c_char_p
@@ -226,17 +222,8 @@ def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, s
     return out
 
 
-def prefill_chunk_workspace_bytes(B: int, Hkv: int, C: int, d: int, w: int, s: int, conv: int = ADDITIVE) -> int:
-    return int(lib().swa_prefill_chunk_workspace_bytes(B, Hkv, C, d, w, s, conv))
-
-
-def alloc_chunk_workspace(B: int, Hkv: int, C: int, d: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
-    n = prefill_chunk_workspace_bytes(B, Hkv, C, d, w, s, conv)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
-
-
 def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: float | None = None,
-                  conv: int = ADDITIVE, out=None, workspace=None):
+                  conv: int = ADDITIVE, out=None):
     """Prefill of a chunk at positions pos0 .. pos0+C-1 against the cache (state after pos0-1),
     then the chunk appended.  q bf16 [B][C][Hq][d], k/v bf16 [B][C][Hkv][d] -> fp32 [B][C][Hq][d]."""
     if q.dim() != 4 or k.dim() != 4:
@@ -252,13 +239,9 @@ def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: f
     if out is None:
         out = torch.empty((B, C, Hq, d), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (B, C, Hq, d))
-    if workspace is None:
-        workspace = alloc_chunk_workspace(B, Hkv, C, d, w, s, conv, device=q.device)
-    _need(workspace, "workspace", torch.uint8)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib().swa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                   out.data_ptr(), int(pos0), B, Hq, Hkv, C, d, w, s, scale, conv,
-                                   workspace.data_ptr(), workspace.numel(), _stream(q)))
+                                   out.data_ptr(), int(pos0), B, Hq, Hkv, C, d, w, s, scale, conv, _stream(q)))
     return out
 
 

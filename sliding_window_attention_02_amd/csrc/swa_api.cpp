@@ -153,18 +153,8 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
                                              static_cast<hipStream_t>(stream)));
 }
 
-// Chunked prefill scratch: the gathered keys and values, each [B][s + w_loc - 1 + C][Hkv][d]
-// bf16 at most, the values' half starting 256-byte aligned.  0 if it does not fit size_t.
-size_t chunk_half_bytes(int B, int Hkv, int C, int d, int w_loc, int s)
-{
-    const unsigned long long rows = (unsigned long long)s + w_loc - 1 + C;
-    const unsigned long long bytes = (unsigned long long)B * rows * Hkv * d * 2;
-    return (size_t)((bytes + 255) / 256 * 256);
-}
-
 int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void *k_cache, void *v_cache, float *out,
-               int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv,
-               void *workspace, size_t workspace_bytes, void *stream)
+               int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv, void *stream)
 {
     CHECK_PTR(q);
     CHECK_PTR(k);
@@ -184,23 +174,15 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
         return rc;
     if ((rc = check_scale(fn, scale)))
         return rc;
-    const long long rows_max = (long long)s + w_loc - 1 + C;
-    if (rows_max > 0x7fffffffLL || rows_max * Hq * d > 0x7fffffffLL)
+    if ((long long)s + w_loc - 1 + C > 0x7fffffffLL || (long long)C * Hq * d > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: one sequence's keys or queries exceed 2^31-1 elements", fn);
-    const size_t half = chunk_half_bytes(B, Hkv, C, d, w_loc, s);
-    if (workspace == nullptr || workspace_bytes < 2 * half)
-        return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, 2 * half,
-                    workspace == nullptr ? (size_t)0 : workspace_bytes);
-    if (!aligned16(workspace))
-        return fail(SWA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const swa::ChunkPlan plan = swa::chunk_plan(pos0, C, w_loc, s);
-    void *ks = workspace;
-    void *vs = static_cast<unsigned char *>(workspace) + half;
-    hipError_t e = swa::launch_chunk_gather(ks, vs, k_cache, v_cache, k, v, pos0, plan, B, Hkv, d, w_loc, s, C, st);
-    if (e == hipSuccess)
-        e = swa::launch_prefill(q, ks, vs, out, B, Hq, Hkv, plan.rows, d, w_loc, s, scale, st, nullptr, nullptr, C,
-                                plan.ns + plan.nw);
+    const swa::PrefillKeySource cached = {k_cache, v_cache, plan.ns + plan.nw, plan.ns, plan.ring0};
+    // Attend (reading the cache as it stands), then append: the chunk's slots may hold keys
+    // that its first queries still need.
+    hipError_t e = swa::launch_prefill(q, k, v, out, B, Hq, Hkv, plan.rows, d, w_loc, s, scale, st, nullptr,
+                                       nullptr, &cached);
     if (e == hipSuccess)
         e = swa::launch_kv_append(k_cache, v_cache, k, v, nullptr, B, Hkv, d, w_loc, s, C, st, pos0);
     return hip_status(fn, e);
@@ -212,25 +194,12 @@ extern "C" {
 
 const char *swa_last_error(void) { return g_last_error.c_str(); }
 
-size_t swa_prefill_chunk_workspace_bytes(int B, int Hkv, int C, int d, int w, int s, int conv)
-{
-    const char *fn = "swa_prefill_chunk_workspace_bytes";
-    if (check_heads(fn, B, Hkv, Hkv, d) || C < 1)
-        return 0;
-    int w_loc = 0;
-    if (resolve_window(fn, w, s, conv, &w_loc))
-        return 0;
-    if ((long long)s + w_loc - 1 + C > 0x7fffffffLL)
-        return 0;
-    return 2 * chunk_half_bytes(B, Hkv, C, d, w_loc, s);
-}
-
 int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache, float *out,
                       int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv,
-                      void *workspace, size_t workspace_bytes, void *stream)
+                      void *stream)
 {
     return chunk_impl("swa_prefill_chunk", q, k, v, k_cache, v_cache, out, pos0, B, Hq, Hkv, C, d, w, s, scale,
-                      conv, workspace, workspace_bytes, stream);
+                      conv, stream);
 }
 
 

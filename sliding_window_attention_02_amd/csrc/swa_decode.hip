@@ -383,44 +383,6 @@ __global__ void kv_append_kernel(uint16_t *kc, uint16_t *vc, const uint16_t *kn,
     *reinterpret_cast<u32x4 *>(vc + dst) = *reinterpret_cast<const u32x4 *>(vn + src);
 }
 
-// Chunked prefill, step 1: the keys a chunk at positions [p0, p0 + C) attends to, in position
-// order, as one contiguous sequence [B][ns + nw + C][Hkv][d]: the ns = min(s, p0) sinks below
-// p0 and the nw window positions p0 - nw .. p0 - 1 from the cache (slot p or s + p mod w_loc),
-// then the chunk's own rows.  One thread per (b, row, kv-head, 16-byte piece).
-template <int D>
-__global__ void chunk_gather_kernel(uint16_t *ks, uint16_t *vs, const uint16_t *kc, const uint16_t *vc,
-                                    const uint16_t *kn, const uint16_t *vn, int64_t p0, int B, int Hkv, int s,
-                                    int w_loc, int ns, int nw, int C)
-{
-    constexpr int kPieces = D / 8;
-    const int rows = ns + nw + C;
-    const size_t total = (size_t)B * rows * Hkv * kPieces;
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total)
-        return;
-    const int piece = (int)(idx % kPieces);
-    size_t rest = idx / kPieces;
-    const int hkv = (int)(rest % Hkv);
-    rest /= Hkv;
-    const int row = (int)(rest % rows);
-    const int b = (int)(rest / rows);
-    const uint16_t *ksrc, *vsrc;
-    if (row < ns + nw) {
-        const int64_t p = row < ns ? row : p0 - nw + (row - ns);
-        const int64_t slot = append_slot(p, s, w_loc);
-        const size_t src = (((size_t)b * Hkv + hkv) * ((size_t)s + w_loc) + slot) * D + piece * 8;
-        ksrc = kc + src;
-        vsrc = vc + src;
-    } else {
-        const size_t src = (((size_t)b * C + (row - ns - nw)) * Hkv + hkv) * D + piece * 8;
-        ksrc = kn + src;
-        vsrc = vn + src;
-    }
-    const size_t dst = (((size_t)b * rows + row) * Hkv + hkv) * D + piece * 8;
-    *reinterpret_cast<u32x4 *>(ks + dst) = *reinterpret_cast<const u32x4 *>(ksrc);
-    *reinterpret_cast<u32x4 *>(vs + dst) = *reinterpret_cast<const u32x4 *>(vsrc);
-}
-
 __global__ void debug_decode_slots_kernel(int64_t *slot_pos, const int64_t *pos, int B, int s, int w_loc)
 {
     const int n_slots = s + w_loc;
@@ -535,30 +497,8 @@ ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s)
     p.ns = pos0 < s ? (int)pos0 : s;
     p.nw = pos0 > s ? (int)(pos0 - s < w_loc - 1 ? pos0 - s : w_loc - 1) : 0;
     p.rows = p.ns + p.nw + C;
+    p.ring0 = (int)((pos0 - p.nw) % w_loc);
     return p;
-}
-
-hipError_t launch_chunk_gather(void *k_scratch, void *v_scratch, const void *k_cache, const void *v_cache,
-                               const void *k_new, const void *v_new, int64_t pos0, const ChunkPlan &plan, int B,
-                               int Hkv, int d, int w_loc, int s, int C, hipStream_t stream)
-{
-    const size_t total = (size_t)B * plan.rows * Hkv * (d / 8);
-    const size_t blocks = (total + 255) / 256;
-    if (blocks > 0x7fffffffULL)
-        return hipErrorInvalidConfiguration;
-    uint16_t *ks = static_cast<uint16_t *>(k_scratch);
-    uint16_t *vs = static_cast<uint16_t *>(v_scratch);
-    const uint16_t *kc = static_cast<const uint16_t *>(k_cache);
-    const uint16_t *vc = static_cast<const uint16_t *>(v_cache);
-    const uint16_t *kn = static_cast<const uint16_t *>(k_new);
-    const uint16_t *vn = static_cast<const uint16_t *>(v_new);
-    if (d == 128)
-        hipLaunchKernelGGL(chunk_gather_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, ks, vs, kc, vc, kn,
-                           vn, pos0, B, Hkv, s, w_loc, plan.ns, plan.nw, C);
-    else
-        hipLaunchKernelGGL(chunk_gather_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, ks, vs, kc, vc, kn,
-                           vn, pos0, B, Hkv, s, w_loc, plan.ns, plan.nw, C);
-    return hipGetLastError();
 }
 
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,

@@ -20,12 +20,21 @@ struct PrefillGeometry {
 };
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
 
+// Chunked prefill: the first n_cached of the L keys are read from a sink+ring cache
+// [B][Hkv][s + w_loc][d] (key j < ns: sink slot j; key j >= ns: ring slot
+// s + (ring0 + j - ns) mod w_loc), the rest from k and v, which hold L - n_cached rows; only
+// the last L - n_cached keys are queries (q and out hold L - n_cached rows).
+struct PrefillKeySource {
+    const void *k_cache, *v_cache;
+    int n_cached, ns, ring0;
+};
+
 // start/stop: optional events stamped by the kernel dispatch itself (null: plain launch).
-// Lq, q_lo: when Lq >= 0, only the queries at key positions q_lo .. q_lo + Lq - 1 are computed;
-// q and out then hold Lq rows per sequence (k and v hold L).  Lq < 0: every position.
+// cached: null for a whole-sequence prefill.
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
-                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int Lq = -1, int q_lo = 0);
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
+                          const PrefillKeySource *cached = nullptr);
 
 hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w_loc, int s,
                                      hipStream_t stream);
@@ -60,15 +69,12 @@ hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void
 // queries are the last C, on which the SWA(w,s) predicate holds unchanged (the window rows
 // hold no sink positions and run contiguously into the chunk).
 struct ChunkPlan {
-    int ns;    // min(s, pos0)
-    int nw;    // min(w_loc - 1, pos0 - s) when pos0 > s, else 0
-    int rows;  // ns + nw + C
+    int ns;     // min(s, pos0)
+    int nw;     // min(w_loc - 1, pos0 - s) when pos0 > s, else 0
+    int rows;   // ns + nw + C
+    int ring0;  // (pos0 - nw) mod w_loc: ring slot s + ring0 holds the first window key
 };
 ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s);
-
-hipError_t launch_chunk_gather(void *k_scratch, void *v_scratch, const void *k_cache, const void *v_cache,
-                               const void *k_new, const void *v_new, int64_t pos0, const ChunkPlan &plan, int B,
-                               int Hkv, int d, int w_loc, int s, int C, hipStream_t stream);
 
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,
                                      hipStream_t stream);

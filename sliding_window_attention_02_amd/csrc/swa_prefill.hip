@@ -59,6 +59,12 @@ struct PrefillArgs {
     float *out;
     int L, Hq, Hkv, G, Gw, Tm, n_qtiles, n_hslices;
     int Lq, q_lo;  // queries are key positions q_lo .. q_lo + Lq - 1 (rows 0 .. Lq-1 of q, out)
+    // Keys 0 .. n_cached-1 come from a sink+ring cache [B][Hkv][s + w_loc][d] instead of k, v
+    // (chunked prefill): key j < ns is sink slot j; key j >= ns is ring slot
+    // s + (ring0 + j - ns) mod w_loc, with ring0 < w_loc and j - ns < w_loc.  k and v then hold
+    // keys n_cached .. L-1.  n_cached = 0 for a whole-sequence prefill.
+    const uint16_t *kc, *vc;
+    int n_cached, ns, ring0;
     int w_loc, s;
     float scale_log2;
     int nblocks;
@@ -184,8 +190,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 
     const int kv_row = a.Hkv * D;  // elements between consecutive positions
-    const uint16_t *kbase = a.k + ((size_t)bc.b * a.L * a.Hkv + bc.hkv) * D;
-    const uint16_t *vbase = a.v + ((size_t)bc.b * a.L * a.Hkv + bc.hkv) * D;
+    const int L_in = a.L - a.n_cached;  // key rows held by k and v
+    const uint16_t *kbase = a.k + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
+    const uint16_t *vbase = a.v + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
+    const size_t cache_base = ((size_t)bc.b * a.Hkv + bc.hkv) * ((size_t)a.s + a.w_loc) * D;
 
     // Direct global -> LDS loads: load j of a tile fills LDS bytes [1024 j, 1024 j + 1024),
     // lane l the 16 bytes at 16 l: row kRowsPerLoad*j + l / kPieces, physical piece
@@ -207,11 +215,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int j = wave * kLoadsPerWave + i;
             const int key = min(j0 + ld_row[i], last);
+            const uint16_t *ksrc, *vsrc;
+            if (key >= a.n_cached) {
+                ksrc = kbase + (key - a.n_cached) * kv_row + ld_kpiece[i] * 8;
+                vsrc = vbase + (key - a.n_cached) * kv_row + ld_vpiece[i] * 8;
+            } else {  // a cached key: its sink or ring slot
+                int slot = key;
+                if (key >= a.ns) {
+                    const int r = a.ring0 + key - a.ns;
+                    slot = a.s + (r >= a.w_loc ? r - a.w_loc : r);
+                }
+                ksrc = a.kc + cache_base + (size_t)slot * D + ld_kpiece[i] * 8;
+                vsrc = a.vc + cache_base + (size_t)slot * D + ld_vpiece[i] * 8;
+            }
             // (the builtin takes a non-const global pointer; the source is only read)
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(kbase + key * kv_row + ld_kpiece[i] * 8),
-                                             SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vbase + key * kv_row + ld_vpiece[i] * 8),
-                                             SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(ksrc), SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0,
+                                             0);
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vsrc), SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0,
+                                             0);
         }
     };
 
@@ -475,11 +496,12 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
-                          hipEvent_t start, hipEvent_t stop, int Lq, int q_lo)
+                          hipEvent_t start, hipEvent_t stop, const PrefillKeySource *cached)
 {
-    if (Lq < 0) {
-        Lq = L;
-        q_lo = 0;
+    int Lq = L, q_lo = 0;
+    if (cached != nullptr) {
+        Lq = L - cached->n_cached;
+        q_lo = cached->n_cached;
     }
     const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
     PrefillArgs a;
@@ -490,6 +512,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     a.L = L;
     a.Lq = Lq;
     a.q_lo = q_lo;
+    a.kc = cached ? static_cast<const uint16_t *>(cached->k_cache) : nullptr;
+    a.vc = cached ? static_cast<const uint16_t *>(cached->v_cache) : nullptr;
+    a.n_cached = cached ? cached->n_cached : 0;
+    a.ns = cached ? cached->ns : 0;
+    a.ring0 = cached ? cached->ring0 : 0;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = g.G;

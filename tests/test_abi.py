@@ -143,32 +143,23 @@ def test_append_decode_step_rejects_on_host(lib):
     assert f(A, A, A, A, A, A, A, 64, 32, 8, 96, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EUNSUPPORTED
 
 
-def test_prefill_chunk_workspace_and_rejection(lib):
-    wsz = lib.swa_prefill_chunk_workspace_bytes
-    # gathered keys and values: 2 x B x (s + w_loc - 1 + C) x Hkv x d bf16, each half 256-byte aligned
-    assert wsz(2, 8, 64, 128, 64, 4, 0) == 2 * 2 * (4 + 64 - 1 + 64) * 8 * 128 * 2
-    assert wsz(1, 1, 1, 64, 1, 0, 0) == 2 * 256
-    assert wsz(1, 8, 0, 128, 64, 4, 0) == 0  # C < 1
-    assert wsz(1, 8, 16, 96, 64, 4, 0) == 0  # d unsupported
-    assert wsz(1, 8, 16, 128, 4, 4, 1) == 0  # TOTAL window leaves nothing
-    ws = wsz(1, 8, 16, 128, 64, 4, 0)
+def test_prefill_chunk_rejects_on_host(lib):
     f = lib.swa_prefill_chunk
     good = dict(q=A, k=A, v=A, kc=A, vc=A, out=A, pos0=0, B=1, Hq=32, Hkv=8, C=16, d=128, w=64, s=4, scale=0.1,
-                conv=0, ws=A, wsb=ws)
+                conv=0)
 
     def call(**kw):
         a = dict(good, **kw)
         return f(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["out"], a["pos0"], a["B"], a["Hq"], a["Hkv"], a["C"],
-                 a["d"], a["w"], a["s"], a["scale"], a["conv"], a["ws"], a["wsb"], None)
+                 a["d"], a["w"], a["s"], a["scale"], a["conv"], None)
 
     assert call(kc=None) == binding.SWA_EINVAL and "k_cache" in err(lib)
     assert call(v=MIS) == binding.SWA_EINVAL and "aligned" in err(lib)
     assert call(C=0) == binding.SWA_EINVAL and "C must be" in err(lib)
     assert call(pos0=-1) == binding.SWA_EINVAL and "pos0" in err(lib)
-    assert call(ws=None) == binding.SWA_EINVAL and "workspace" in err(lib)
-    assert call(wsb=ws - 16) == binding.SWA_EINVAL and "workspace" in err(lib)
-    assert call(ws=MIS) == binding.SWA_EINVAL and "aligned" in err(lib)
     assert call(d=96) == binding.SWA_EUNSUPPORTED
     assert call(Hq=12) == binding.SWA_EINVAL  # 12 % 8 != 0
     assert call(scale=0.0) == binding.SWA_EINVAL
     assert call(conv=7) == binding.SWA_EINVAL
+    assert call(w=4, conv=1) == binding.SWA_EINVAL  # TOTAL window leaves nothing after the sinks
+    assert call(C=2 ** 30) == binding.SWA_EUNSUPPORTED

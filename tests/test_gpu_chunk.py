@@ -63,10 +63,9 @@ def test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv
     kc, vc = nan_cache(B, Hkv, d, w, s, conv)
     outs, p0 = [], 0
     for C in chunks:
-        ws = swa.alloc_chunk_workspace(B, Hkv, C, d, w, s, conv)
         sl = slice(p0, p0 + C)
         outs.append(swa.prefill_chunk(qg[:, sl].contiguous(), kg[:, sl].contiguous(), vg[:, sl].contiguous(),
-                                      kc, vc, p0, w, s, scale, conv, workspace=ws))
+                                      kc, vc, p0, w, s, scale, conv))
         p0 += C
     got = torch.cat(outs, dim=1).cpu().numpy()
     err = np.abs(got - ref)
