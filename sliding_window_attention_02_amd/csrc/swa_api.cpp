@@ -88,10 +88,6 @@ int hip_status(const char *fn, hipError_t e)
     return ok();
 }
 
-}  // namespace
-
-namespace {
-
 int prefill_impl(const char *fn, const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv,
                  int L, int d, int w, int s, float scale, int conv, void *stream, void *start, void *stop)
 {
@@ -115,10 +111,6 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
                                               static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start),
                                               static_cast<hipEvent_t>(stop)));
 }
-
-}  // namespace
-
-namespace {
 
 int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache, const void *k_new,
                 const void *v_new, float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,

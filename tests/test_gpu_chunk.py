@@ -138,3 +138,27 @@ def test_chunk_of_one_token_equals_decode_step():
     assert worst <= TOL
     assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
     assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+
+
+def _random_chunkings(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        w = int(rng.integers(1, 120))
+        s = int(rng.integers(0, 8))
+        L = int(rng.integers(1, 300))
+        chunks, left = [], L
+        while left > 0:
+            c = int(min(left, rng.integers(1, 2 * w + 8)))
+            chunks.append(c)
+            left -= c
+        out.append((int(rng.integers(1, 3)), G * Hkv, Hkv, d, w, s, 0, chunks))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv,chunks", _random_chunkings(6, 777))
+def test_chunked_prefill_on_drawn_chunkings(B, Hq, Hkv, d, w, s, conv, chunks):
+    test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks)

@@ -188,3 +188,32 @@ def test_timed_prefill_matches_and_stamps_kernel_time():
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert e0.elapsed_time(e1) > 0
+
+
+def _random_cases(n, seed):
+    """Shapes drawn from a fixed generator: every run checks the same cases."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        d = int(rng.choice([64, 128]))
+        L = int(rng.integers(1, 700))
+        w = int(rng.integers(1, 400))
+        s = int(rng.integers(0, 12))
+        conv = int(rng.integers(0, 2))
+        if conv == 1 and w - s < 1:
+            w = s + 1 + int(rng.integers(0, 50))
+        B = int(rng.integers(1, 3))
+        cases.append((B, L, G * Hkv, Hkv, d, w, s, conv))
+    return cases
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,w,s,conv", _random_cases(12, 20261203))
+def test_prefill_matches_oracle_on_drawn_shapes(B, L, Hq, Hkv, d, w, s, conv):
+    say("drawn", B, L, Hq, Hkv, d, w, s, conv)
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=L * 7 + w, std=1.0, sink_boost_n=4, sink_boost=4.0)
+    scale = 1.0 / np.sqrt(d)
+    ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    got = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, scale, conv).cpu().numpy()
+    check_close(got, ref, "drawn")
