@@ -85,6 +85,7 @@ def parse():
     ap.add_argument("--decode-only", type=int, default=0, help="only time the decode graph at this batch (profiling)")
     ap.add_argument("--chunked", default="", help="only time this prefill workload fed in chunks (swa_prefill_chunk)")
     ap.add_argument("--chunk", type=int, default=4096, help="with --chunked: tokens per chunk")
+    ap.add_argument("--compare-full", action="store_true", help="only time SWA against full causal attention")
     ap.add_argument("--cache-sets", type=int, default=1, help="with --decode-only: caches the steps rotate over")
     return ap.parse_args()
 
@@ -127,7 +128,7 @@ def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev, n_sets: int = 1):
     swa_append_decode_step (append the token's K/V to its slot and attend), and a function that
     restores the caches to their state after position P-1 (run it before every replay, so each
     replay decodes the same tokens).  Every input is seeded: a cache holds the sinks and
-    positions P-w_loc .. P-1.  With n_sets > 1 the steps rotate over that many independent
+    positions max(s, P-w_loc) .. P-1.  With n_sets > 1 the steps rotate over that many independent
     caches (step i uses cache i % n_sets at position P + i // n_sets), so that consecutive steps
     never find their cache in the Infinity Cache once n_sets caches exceed it."""
     import torch
@@ -136,12 +137,16 @@ def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev, n_sets: int = 1):
     gen = dict(B=B, Hkv=dw.Hkv, d=dw.d, std=dw.std, sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost)
     kc, vc = swa.alloc_cache(B, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
     ws = swa.alloc_workspace(B, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
-    seed_pos = list(range(dw.s)) + list(range(P - w_loc, P))
+    lo = max(dw.s, P - w_loc)  # first window position in the cache after P-1
+    seed_pos = list(range(min(dw.s, P))) + list(range(lo, P))
     sk, sv = inputs.kv_span(dw.seed, seed_pos, **gen)
-    swa.kv_append(kc, vc, sk[:, :dw.s].contiguous().to(dev), sv[:, :dw.s].contiguous().to(dev),
-                  torch.zeros(B, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
-    swa.kv_append(kc, vc, sk[:, dw.s:].contiguous().to(dev), sv[:, dw.s:].contiguous().to(dev),
-                  torch.full((B,), P - w_loc, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    n_sink = min(dw.s, P)
+    if n_sink > 0:
+        swa.kv_append(kc, vc, sk[:, :n_sink].contiguous().to(dev), sv[:, :n_sink].contiguous().to(dev),
+                      torch.zeros(B, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    if P > lo:
+        swa.kv_append(kc, vc, sk[:, n_sink:].contiguous().to(dev), sv[:, n_sink:].contiguous().to(dev),
+                      torch.full((B,), lo, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
     snap_k, snap_v = kc.clone(), vc.clone()
     caches = [(kc, vc)] + [(snap_k.clone(), snap_v.clone()) for _ in range(n_sets - 1)]
     n_pos = (T + n_sets - 1) // n_sets
@@ -314,6 +319,50 @@ def chunked_only(args, dev):
                       "chunked_over_whole": round(chunked / whole, 3)}), flush=True)
 
 
+def compare_full(args, dev):
+    """--compare-full: SWA against full causal attention with the same kernels (full attention
+    is SWA with a window covering the whole sequence or context).  Prefill: the Mistral-shaped
+    workload with w=4096 and with w >= L.  Decode at batch 1: SWA(64,4) on its 68-slot ring
+    against a growing cache holding every position up to the context, at contexts 2^7 .. 2^17,
+    64 append+attend steps each (one HIP graph).  One JSON line; every input is seeded."""
+    import math
+
+    import torch
+
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import accounting as acc
+    from sliding_window_attention_02_amd import inputs
+
+    rec = {"prefill": {}, "decode": []}
+    wl = inputs.prefill_workloads()["mistral7b_w4096_s4"]
+    q, k, v = inputs.prefill_inputs(wl)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    for name, w, s in (("swa_w4096_s4", wl.w, wl.s), ("full_causal", wl.L, 0)):
+        cfg = type("W", (), dict(w=w, s=s, scale=wl.scale, conv=0))
+        ms = prefill_timing(swa, cfg, qg, kg, vg, out, args.steps, args.warmup)
+        mean = sum(ms) / len(ms)
+        useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w, s)
+        rec["prefill"][name] = {"ms": round(mean, 4), "useful_tflops": round(useful / (mean * 1e-3) / 1e12, 2)}
+    rec["prefill"]["full_over_swa"] = round(rec["prefill"]["full_causal"]["ms"] / rec["prefill"]["swa_w4096_s4"]["ms"], 3)
+
+    dw = inputs.decode_workloads()["decode_swa64_4_b1"]
+    T = 64
+    for e in range(7, 18):
+        P = 2 ** e
+        swa_pt = decode_point(swa, inputs, acc, dw, 1, T, P, dev, reps=3)
+        # Full attention: s = 0 and a local window of P + T slots, so the cache grows with the
+        # context and no position is evicted (slot p holds position p).
+        full = type("D", (), dict(w=P + T, s=0, conv=0, Hq=dw.Hq, Hkv=dw.Hkv, d=dw.d, std=dw.std,
+                                  sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost, seed=dw.seed,
+                                  scale=dw.scale))
+        full_pt = decode_point(swa, inputs, acc, full, 1, T, P, dev, reps=3)
+        rec["decode"].append({"context": P, "swa_us_per_step": swa_pt["us_per_token_step"],
+                              "full_us_per_step": full_pt["us_per_token_step"],
+                              "full_kv_gb_per_s": full_pt["kv_gb_per_s"]})
+    print(json.dumps(rec), flush=True)
+
+
 def decode_only(args, dev):
     """--decode-only B: time the decode graph at batch B and print one JSON line."""
     import sliding_window_attention_02_amd as swa
@@ -355,6 +404,9 @@ def main():
         return
     if args.chunked:
         chunked_only(args, dev)
+        return
+    if args.compare_full:
+        compare_full(args, dev)
         return
 
     # ---------------------------------------------------------------- prefill inputs

@@ -332,23 +332,55 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
     }
 }
 
-// Fixed-order merge of the split partials.  grid: (Hq, B), block: D threads.
+// Fixed-order merge of the split partials.  grid: (Hq, B), block: kMergeThreads.  Thread t
+// takes element dd = t % D of the splits i = g, g + G, g + 2G, ... (g = t / D, G groups); the
+// groups' sums are then added in group order, so the result does not depend on scheduling.
+constexpr int kMergeThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float *ws, float *out, int Hq, int n_split)
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws, float *out, int Hq, int n_split)
 {
-    const int h = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
+    constexpr int G = kMergeThreads / D;
+    __shared__ float red[kMergeThreads];
+    __shared__ float red_l[G];
+    const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int dd = t % D, g = t / D;
     const float *part = ws + ((size_t)b * Hq + h) * n_split * (D + 2);
+    // Maximum of the split maxima.
     float mm = -INFINITY;
-    for (int i = 0; i < n_split; ++i)
-        mm = fmaxf(mm, part[i * (D + 2)]);
+    for (int i = t; i < n_split; i += kMergeThreads)
+        mm = fmaxf(mm, part[(size_t)i * (D + 2)]);
+    red[t] = mm;
+    __syncthreads();
+    for (int stride = kMergeThreads / 2; stride > 0; stride >>= 1) {
+        if (t < stride)
+            red[t] = fmaxf(red[t], red[t + stride]);
+        __syncthreads();
+    }
+    mm = red[0];
+    __syncthreads();
     const float m_use = mm == -INFINITY ? 0.f : mm;
     float ll = 0.f, oo = 0.f;
-    for (int i = 0; i < n_split; ++i) {
-        const float sc = __builtin_amdgcn_exp2f(part[i * (D + 2)] - m_use);
-        ll += part[i * (D + 2) + 1] * sc;
-        oo += part[i * (D + 2) + 2 + dd] * sc;
+#pragma unroll 4
+    for (int i = g; i < n_split; i += G) {
+        const float *pi = part + (size_t)i * (D + 2);
+        const float sc = __builtin_amdgcn_exp2f(pi[0] - m_use);
+        ll += pi[1] * sc;
+        oo += pi[2 + dd] * sc;
     }
-    out[((size_t)b * Hq + h) * D + dd] = ll > 0.f ? oo / ll : 0.f;
+    red[t] = oo;
+    if (dd == 0)
+        red_l[g] = ll;
+    __syncthreads();
+    if (g == 0) {
+        float o_sum = 0.f, l_sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            o_sum += red[j * D + dd];
+            l_sum += red_l[j];
+        }
+        out[((size_t)b * Hq + h) * D + dd] = l_sum > 0.f ? o_sum / l_sum : 0.f;
+    }
 }
 
 // One thread per (b, token, kv-head, 16-byte chunk).  Positions that a later token of the
@@ -485,9 +517,11 @@ hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void
     if (e != hipSuccess || plan.n_split == 1)
         return e;
     if (d == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, dim3(Hq, B), dim3(128), 0, stream, a.ws, out, Hq, plan.n_split);
+        hipLaunchKernelGGL(merge_kernel<128>, dim3(Hq, B), dim3(kMergeThreads), 0, stream, a.ws, out, Hq,
+                           plan.n_split);
     else
-        hipLaunchKernelGGL(merge_kernel<64>, dim3(Hq, B), dim3(64), 0, stream, a.ws, out, Hq, plan.n_split);
+        hipLaunchKernelGGL(merge_kernel<64>, dim3(Hq, B), dim3(kMergeThreads), 0, stream, a.ws, out, Hq,
+                           plan.n_split);
     return hipGetLastError();
 }
 

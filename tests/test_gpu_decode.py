@@ -218,3 +218,31 @@ def test_fused_append_decode_equals_two_calls(B, Hq, Hkv, d, w, s, conv):
         b = swa.append_decode_step(qs[t], kc2, vc2, ks[t], vs[t], pos, w, s, None, conv, workspace=ws)
         assert torch.equal(a, b), t
     assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+
+
+@pytest.mark.parametrize("P,B,Hq,Hkv,d", [(5000, 1, 8, 2, 128), (3000, 2, 4, 4, 64)])
+def test_full_attention_decode_at_long_context(P, B, Hq, Hkv, d):
+    """Full causal attention as SWA with s = 0 and a window holding the whole context (the
+    comparator of the SWA-versus-full measurement): the cache holds positions 0 .. P-1, the
+    step appends P and attends to every position; thousands of slots, so split + merge."""
+    say("full-decode", P, B, Hq, Hkv, d)
+    w, s = P + 1, 0
+    g = torch.Generator().manual_seed(P)
+    k = torch.randn(B, P + 1, Hkv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, P + 1, Hkv, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s)
+    swa.kv_append(kc, vc, k[:, :P].contiguous().cuda(), v[:, :P].contiguous().cuda(), gpos([0] * B), w, s)
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s)
+    assert ws.numel() > 16  # split over workgroups
+    out = swa.append_decode_step(q.cuda(), kc, vc, k[:, P].contiguous().cuda(), v[:, P].contiguous().cuda(),
+                                 gpos([P] * B), w, s, workspace=ws).cpu().numpy()
+    scale = 1.0 / np.sqrt(d)
+    pos = np.arange(P + 1, dtype=np.int64)
+    worst = 0.0
+    for b in range(B):
+        ref, kept = orc.decode_row(f64(q[b]), pos, f64(k[b]), f64(v[b]), P, w, s, scale)
+        assert kept == P + 1
+        worst = max(worst, float(np.abs(out[b] - ref).max()))
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
