@@ -200,7 +200,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     // l % kPieces, which holds logical piece (physical ^ swizzle).  This wave issues loads
     // j = wave*kLoadsPerWave .. +kLoadsPerWave-1.  Rows past the end of the sequence read the
     // last row (finite values; such keys are always masked).
+    // The wave index as a uniform (scalar) value: the LDS destinations (M0) are then scalar.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     int ld_row[kLoadsPerWave], ld_kpiece[kLoadsPerWave], ld_vpiece[kLoadsPerWave];
+    uint32_t ld_koff[kLoadsPerWave], ld_voff[kLoadsPerWave];  // byte offsets from the tile's first row
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int j = wave * kLoadsPerWave + i;
@@ -208,12 +211,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         const int phys = lane % kPieces;
         ld_kpiece[i] = phys ^ swz_k<D>(ld_row[i]);
         ld_vpiece[i] = phys ^ swz_v(ld_row[i]);
+        ld_koff[i] = (uint32_t)(ld_row[i] * kv_row + ld_kpiece[i] * 8) * 2u;
+        ld_voff[i] = (uint32_t)(ld_row[i] * kv_row + ld_vpiece[i] * 8) * 2u;
     }
     auto issue_tile = [&](int j0, int buf) {
         const int last = a.L - 1;
+        if (j0 >= a.n_cached && j0 + kTileN - 1 <= last) {
+            // Every row of the tile is a key of k/v inside the sequence: a scalar tile base plus
+            // the per-lane offsets.
+            const char *kt0 = reinterpret_cast<const char *>(kbase + (size_t)(j0 - a.n_cached) * kv_row);
+            const char *vt0 = reinterpret_cast<const char *>(vbase + (size_t)(j0 - a.n_cached) * kv_row);
+#pragma unroll
+            for (int i = 0; i < kLoadsPerWave; ++i) {
+                const int j = wave_u * kLoadsPerWave + i;
+                __builtin_amdgcn_global_load_lds(const_cast<char *>(kt0 + ld_koff[i]),
+                                                 SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(const_cast<char *>(vt0 + ld_voff[i]),
+                                                 SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int j = wave * kLoadsPerWave + i;
+            const int j = wave_u * kLoadsPerWave + i;
             const int key = min(j0 + ld_row[i], last);
             const uint16_t *ksrc, *vsrc;
             if (key >= a.n_cached) {
