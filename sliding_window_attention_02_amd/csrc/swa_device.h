@@ -46,6 +46,36 @@ __device__ __forceinline__ TileWalk plan_tiles(int t0, int t1, int w_loc, int s,
     return tw;
 }
 
+// The window tiles all of whose keys every token of [t0, t1] may see (each key is at most t0 and
+// inside the window of t1) need neither a chunk selection nor an element mask: they are the
+// middle tiles [mid_lo, mid_hi] (none when mid_lo > mid_hi).  The other tiles of the walk are
+// its edge tiles, visited in walk order by edge_tile(i), i < n_edge.
+struct WalkSplit {
+    int mid_lo, mid_hi, n_edge;
+    __device__ __forceinline__ int n_mid() const { return mid_hi >= mid_lo ? mid_hi - mid_lo + 1 : 0; }
+    __device__ __forceinline__ int edge_tile(const TileWalk &tw, int i) const
+    {
+        if (i < tw.n_sink)
+            return i;
+        int t = tw.win_lo + (i - tw.n_sink);
+        if (t >= mid_lo)
+            t += n_mid();
+        return t;
+    }
+};
+
+__device__ __forceinline__ WalkSplit split_walk(const TileWalk &tw, int t0, int t1, int w_loc, int tile_n)
+{
+    WalkSplit sp;
+    const int lo = t1 - w_loc + 1;  // first key inside the window of t1
+    const int first = lo > 0 ? (lo + tile_n - 1) / tile_n : 0;
+    sp.mid_lo = first > tw.win_lo ? first : tw.win_lo;
+    const int last = (t0 + 1) / tile_n - 1;  // last tile whose keys are all <= t0
+    sp.mid_hi = last < tw.win_hi ? last : tw.win_hi;
+    sp.n_edge = tw.count() - sp.n_mid();
+    return sp;
+}
+
 // A tile is processed in chunks of kChunkN keys.  Sets [c_lo, c_hi], the smallest chunk
 // range that covers every chunk holding a key of A(t) for some t in [t0, t1] (the needed
 // keys of a q-tile are the sinks [0, min(s, t1+1)) and the window [max(0, t0-w_loc+1), t1]);

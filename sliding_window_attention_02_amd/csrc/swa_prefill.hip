@@ -136,6 +136,13 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
     return c;
 }
 
+// Key tile of the walk: first key, needed chunk range, and whether no element mask is needed.
+struct TileInfo {
+    int j0, c_lo, c_hi;
+    int mask_free;  // (an int: a bool member would leave padding that the copies carry)
+    __device__ __forceinline__ bool full() const { return c_lo == 0 && c_hi == 1 && mask_free; }
+};
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
@@ -202,78 +209,77 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     // last row (finite values; such keys are always masked).
     // The wave index as a uniform (scalar) value: the LDS destinations (M0) are then scalar.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int ld_row[kLoadsPerWave], ld_kpiece[kLoadsPerWave], ld_vpiece[kLoadsPerWave];
     uint32_t ld_koff[kLoadsPerWave], ld_voff[kLoadsPerWave];  // byte offsets from the tile's first row
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int j = wave * kLoadsPerWave + i;
-        ld_row[i] = kRowsPerLoad * j + lane / kPieces;
+        const int row = kRowsPerLoad * (wave * kLoadsPerWave + i) + lane / kPieces;
         const int phys = lane % kPieces;
-        ld_kpiece[i] = phys ^ swz_k<D>(ld_row[i]);
-        ld_vpiece[i] = phys ^ swz_v(ld_row[i]);
-        ld_koff[i] = (uint32_t)(ld_row[i] * kv_row + ld_kpiece[i] * 8) * 2u;
-        ld_voff[i] = (uint32_t)(ld_row[i] * kv_row + ld_vpiece[i] * 8) * 2u;
+        ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
+        ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
     }
-    auto issue_tile = [&](int j0, int buf) {
+    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf.
+    auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
+        constexpr int kv = decltype(kv_c)::value;
+        const uint16_t *base = kv ? vbase : kbase;
         const int last = a.L - 1;
         if (j0 >= a.n_cached && j0 + kTileN - 1 <= last) {
             // Every row of the tile is a key of k/v inside the sequence: a scalar tile base plus
             // the per-lane offsets.
-            const char *kt0 = reinterpret_cast<const char *>(kbase + (size_t)(j0 - a.n_cached) * kv_row);
-            const char *vt0 = reinterpret_cast<const char *>(vbase + (size_t)(j0 - a.n_cached) * kv_row);
+            const char *tile0 = reinterpret_cast<const char *>(base + (size_t)(j0 - a.n_cached) * kv_row);
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int j = wave_u * kLoadsPerWave + i;
-                __builtin_amdgcn_global_load_lds(const_cast<char *>(kt0 + ld_koff[i]),
-                                                 SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(const_cast<char *>(vt0 + ld_voff[i]),
-                                                 SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0, 0);
+                // (the builtin takes a non-const global pointer; the source is only read)
+                __builtin_amdgcn_global_load_lds(const_cast<char *>(tile0 + (kv ? ld_voff[i] : ld_koff[i])),
+                                                 SWA_LDS_PTR(&lds[buf][kv][1024 * j]), 16, 0, 0);
             }
             return;
         }
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int j = wave_u * kLoadsPerWave + i;
-            const int key = min(j0 + ld_row[i], last);
-            const uint16_t *ksrc, *vsrc;
+            const int row = kRowsPerLoad * j + lane / kPieces;
+            const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
+            const int key = min(j0 + row, last);
+            const uint16_t *src;
             if (key >= a.n_cached) {
-                ksrc = kbase + (key - a.n_cached) * kv_row + ld_kpiece[i] * 8;
-                vsrc = vbase + (key - a.n_cached) * kv_row + ld_vpiece[i] * 8;
+                src = base + (key - a.n_cached) * kv_row + piece * 8;
             } else {  // a cached key: its sink or ring slot
                 int slot = key;
                 if (key >= a.ns) {
                     const int r = a.ring0 + key - a.ns;
                     slot = a.s + (r >= a.w_loc ? r - a.w_loc : r);
                 }
-                ksrc = a.kc + cache_base + (size_t)slot * D + ld_kpiece[i] * 8;
-                vsrc = a.vc + cache_base + (size_t)slot * D + ld_vpiece[i] * 8;
+                src = (kv ? a.vc : a.kc) + cache_base + (size_t)slot * D + piece * 8;
             }
-            // (the builtin takes a non-const global pointer; the source is only read)
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(ksrc), SWA_LDS_PTR(&lds[buf][0][1024 * j]), 16, 0,
-                                             0);
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vsrc), SWA_LDS_PTR(&lds[buf][1][1024 * j]), 16, 0,
-                                             0);
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(src), SWA_LDS_PTR(&lds[buf][kv][1024 * j]), 16,
+                                             0, 0);
         }
     };
-
+    // (tags as types, passed as temporaries: named tag objects captured by the lambdas below
+    // end up in private memory)
+    using KRows = std::integral_constant<int, 0>;
+    using VRows = std::integral_constant<int, 1>;
     // LDS read offsets (bytes, within a tile) that do not depend on the tile.
-    // K fragment (kc, h, kk): row 32kc + 8(c16/4) + 4h + c16%4, logical piece 4kk + g16.
-    int k_off[2][2][kKSteps];
+    // K fragment (kc, h, kk): row 32kc + 4h + r with r = 8(c16/4) + c16%4, logical piece
+    // 4kk + g16.  Adding 32kc + 4h to r changes neither r % 4 nor (r / 8) % 4, so the row's
+    // swizzle is that of r: the offset is k_lane[kk] plus the constant (32kc + 4h) * kRowBytes.
+    int k_lane[kKSteps];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = kc * kChunkN + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
-#pragma unroll
-            for (int kk = 0; kk < kKSteps; ++kk)
-                k_off[kc][h][kk] = row * kRowBytes + 16 * ((4 * kk + g16) ^ swz_k<D>(row));
-        }
+    for (int kk = 0; kk < kKSteps; ++kk) {
+        const int r = 8 * (c16 >> 2) + (c16 & 3);
+        k_lane[kk] = r * kRowBytes + 16 * ((4 * kk + g16) ^ swz_k<D>(r));
+    }
     // V^T fragment (db, kc) from two transposed 8-byte reads (h = 0, 1): lane 16g + s reads
-    // row 32kc + 8g + 4h + s/4 at d = 16db + 4(s%4) .. +3; the read hands lane s the values
-    // at d = 16db + s of the four rows 32kc + 8g + 4h .. +3.
-    const int vt_row0 = 8 * g16 + (c16 >> 2);  // + 32kc + 4h
-    const int vt_half = 8 * (c16 & 1);          // byte offset inside the 16-byte piece
-    const int vt_pbit = (c16 >> 1) & 1;         // which piece of the 2-piece column block
+    // row 32kc + 4h + 8g + s/4 at d = 16db + 4(s%4) .. +3 (byte 8(s%2) of logical piece
+    // 2db + (s/2)%2); the read hands lane s the values at d = 16db + s of the four rows
+    // 32kc + 4h + 8g .. +3.  The row's swizzle is 2(s/4) whatever kc, h, and XOR with an even
+    // swizzle keeps the low piece bit, so the physical piece is 2(db ^ s/4) + (s/2)%2 and the
+    // offset is v_lane[db % 4] plus the constant (32kc + 4h) * kRowBytes + 32 (db - db % 4).
+    int v_lane[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        v_lane[m] = (8 * g16 + (c16 >> 2)) * kRowBytes + 32 * (m ^ (c16 >> 2)) + 16 * ((c16 >> 1) & 1) + 8 * (c16 & 1);
 
     f32x4 o[kDBlocks][2];
 #pragma unroll
@@ -292,40 +298,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
     const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
-    const int ntiles = tw.count();
+    const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
+    auto tile_info = [&](int tile) __attribute__((always_inline)) {
+        TileInfo ti;
+        ti.j0 = tile * kTileN;
+        tile_chunks(ti.j0, 2, t0, t1, a.w_loc, a.s, ti.c_lo, ti.c_hi);
+        ti.mask_free = range_mask_free(ti.j0 + ti.c_lo * kChunkN, ti.j0 + ti.c_hi * kChunkN + kChunkN - 1, t0, t1,
+                                       a.w_loc, a.s);
+        return ti;
+    };
 
-    int j0 = tw.tile(0) * kTileN, c_lo, c_hi;
-    tile_chunks(j0, 2, t0, t1, a.w_loc, a.s, c_lo, c_hi);
-    issue_tile(j0, 0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
+    // The steps below take `fast` as a compile-time flag: a fast tile has both chunks needed and
+    // no element mask, so its code is straight-line; otherwise chunks outside [c_lo, c_hi] are
+    // skipped (loads aside: a tile is always loaded whole) and the mask is applied.
 
-    // One tile step; the LDS buffer index is a compile-time constant (the loop below is
-    // unrolled by two), so every LDS address is a per-lane base plus an immediate offset.
-    auto tile_step = [&](const int n, auto buf_c) {
-        constexpr int buf = decltype(buf_c)::value;
-        const unsigned char *kt = lds[buf][0];
-        const unsigned char *vt = lds[buf][1];
-        int nj0 = 0, nc_lo = 2, nc_hi = -1;
-        if (n + 1 < ntiles) {
-            nj0 = tw.tile(n + 1) * kTileN;
-            tile_chunks(nj0, 2, t0, t1, a.w_loc, a.s, nc_lo, nc_hi);
-            issue_tile(nj0, buf ^ 1);
-        }
-
-        // S^T = K Q^T over the needed chunks.  Row m of 16-key block (kc, h) holds key
-        // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
-        f32x4 sacc[2][2][2];  // [kc][h][qb]
+    // S^T = K Q^T of one tile, K from LDS.  Row m of 16-key block (kc, h) holds key
+    // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
+    // (Skipped chunks are set to zero all the same: every element of sacc is then written by
+    // each call, so the compiler does not keep the previous tile's scores alive.)
+    auto scores = [&](f32x4(&sacc)[2][2][2], const unsigned char *kt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
+        constexpr bool fast = decltype(fast_c)::value;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            if (kc < c_lo || kc > c_hi)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
                 continue;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < kKSteps; ++kk) {
-                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(kt + k_off[kc][h][kk]);
+                    const bf16x8 af =
+                        *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + (kc * kChunkN + 4 * h) * kRowBytes);
 #pragma unroll
                     for (int qb = 0; qb < 2; ++qb)
                         sacc[kc][h][qb] =
@@ -333,14 +338,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 }
             }
         }
+    };
 
-        // Element mask, only when some visited (query, key) pair is outside A(t).
-        const bool mask_free =
-            range_mask_free(j0 + c_lo * kChunkN, j0 + c_hi * kChunkN + kChunkN - 1, t0, t1, a.w_loc, a.s);
-        if (!mask_free) {
+    // Element mask of one tile (when some visited pair is outside A(t)), its column maxima, and
+    // the lazy move of the reference maximum: m_ref only moves (and O and the sums are rescaled
+    // by alpha) when the column maximum exceeds it by more than 8 in log2 units, so the
+    // probabilities stay below 256 and most tiles need no rescale.  Returns whether any column
+    // of this lane moved.
+    auto tile_max = [&](f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, float(&alpha)[2]) __attribute__((always_inline)) {
+        constexpr bool fast = decltype(fast_c)::value;
+        if (!fast && !ti.mask_free) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                if (kc < c_lo || kc > c_hi)
+                if (kc < ti.c_lo || kc > ti.c_hi)
                     continue;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
@@ -348,45 +358,48 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const int key = j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
+                            const int key = ti.j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
                             const int t = tok[qb];
                             const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
                             sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
                         }
             }
         }
-
-        // Online softmax with lazy rescaling: the reference maximum only moves (and O and the
-        // sums are rescaled) when the column maximum exceeds it by more than 8 in log2 units,
-        // so the probabilities stay below 256 and most tiles skip the rescale.
-        bf16x8 pf[2][2];  // [kc][qb]: P^T B-operand fragments
-        float alpha[2];
         bool grow_any = false;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            // (pairs folded into the running maximum: three-input maxima)
             float mx = -INFINITY;
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                if (kc < c_lo || kc > c_hi)
+                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
                     continue;
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    mx = fmaxf(mx, fmaxf(fmaxf(sacc[kc][h][qb][0], sacc[kc][h][qb][1]),
-                                         fmaxf(sacc[kc][h][qb][2], sacc[kc][h][qb][3])));
+                for (int h = 0; h < 2; ++h) {
+                    mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][0]), sacc[kc][h][qb][1]);
+                    mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][2]), sacc[kc][h][qb][3]);
+                }
             }
             mx = max_over_groups(mx);
             const float m_tile = mx * c;
             const bool grow = m_tile > m_ref[qb] + 8.f;
-            alpha[qb] = 1.f;
-            if (grow) {
-                alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - m_tile);
-                m_ref[qb] = m_tile;
-            }
+            // (a column with no allowed key so far keeps m_ref = -inf and alpha = 1)
+            alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile) : 1.f;
+            m_ref[qb] = grow ? m_tile : m_ref[qb];
             grow_any |= grow;
+        }
+        return grow_any;
+    };
+
+    // Probabilities of one tile against the reference maximum, as P^T B-operand fragments.
+    auto probs = [&](const f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, bf16x8(&pf)[2][2]) __attribute__((always_inline)) {
+        constexpr bool fast = decltype(fast_c)::value;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
             const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                if (kc < c_lo || kc > c_hi)
+                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
                     continue;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
@@ -396,20 +409,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                             static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc][h][qb][j], c, -m_use)));
             }
         }
-        if (__any(grow_any)) {
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db) {
-                o[db][0] *= alpha[0];
-                o[db][1] *= alpha[1];
-            }
-            lsum[0] *= alpha[0];
-            lsum[1] *= alpha[1];
-        }
+    };
 
-        // O^T += V^T P^T over the needed chunks, and the probability sums.
+    // O^T += V^T P^T over the tile's needed chunks, V from LDS, and the probability sums.
+    auto accumulate = [&](const bf16x8(&pf)[2][2], const unsigned char *vt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
+        constexpr bool fast = decltype(fast_c)::value;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            if (kc < c_lo || kc > c_hi)
+            if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
                 continue;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -419,8 +426,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 bf16x8 af;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int row = kc * kChunkN + 4 * h + vt_row0;
-                    const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ swz_v(row)) + vt_half;
+                    const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
                     const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4 *)(vt + off));
                     const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -434,17 +440,116 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[kc][qb], o[db][qb], 0, 0, 0);
             }
         }
-
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
-        __syncthreads();
-        j0 = nj0;
-        c_lo = nc_lo;
-        c_hi = nc_hi;
     };
-    for (int n = 0; n < ntiles; n += 2) {
-        tile_step(n, std::integral_constant<int, 0>());
-        if (n + 1 < ntiles)
-            tile_step(n + 1, std::integral_constant<int, 1>());
+
+    auto rescale = [&](const float(&alpha)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+            o[db][0] *= alpha[0];
+            o[db][1] *= alpha[1];
+        }
+        lsum[0] *= alpha[0];
+        lsum[1] *= alpha[1];
+    };
+
+    // The online softmax takes the tiles in any order: the edge tiles first, one per step,
+    // then the middle tiles through a software pipeline.
+    f32x4 sacc[2][2][2][2];  // [tile parity][kc][h][qb]
+    float alpha[2];
+    using Generic = std::integral_constant<bool, false>;
+    using Fast = std::integral_constant<bool, true>;
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+
+    // Edge tiles: step i computes tile i while K and V of tile i+1 load into the other buffer.
+    if (sp.n_edge > 0) {
+        TileInfo cur = tile_info(sp.edge_tile(tw, 0));
+        issue(cur.j0, 0, KRows());
+        issue(cur.j0, 0, VRows());
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        auto edge_step = [&](const int i, auto buf_c) __attribute__((always_inline)) {
+            constexpr int buf = decltype(buf_c)::value;  // i & 1
+            TileInfo nxt = cur;
+            if (i + 1 < sp.n_edge) {
+                nxt = tile_info(sp.edge_tile(tw, i + 1));
+                issue(nxt.j0, buf ^ 1, KRows());
+                issue(nxt.j0, buf ^ 1, VRows());
+            }
+            scores(sacc[0], lds[buf][0], cur, Generic());
+            if (__any(tile_max(sacc[0], cur, Generic(), alpha)))
+                rescale(alpha);
+            bf16x8 pf[2][2];
+            probs(sacc[0], cur, Generic(), pf);
+            accumulate(pf, lds[buf][1], cur, Generic());
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
+            __syncthreads();
+            cur = nxt;
+        };
+        for (int i = 0; i < sp.n_edge; i += 2) {
+            edge_step(i, Even());
+            if (i + 1 < sp.n_edge)
+                edge_step(i + 1, Odd());
+        }
+    }
+
+    // Middle tiles m = 0 .. nm-1 (keys jm + 64m ..): full and mask-free.  Step m computes, with
+    // no dependence between the two halves,
+    //     matrix cores: S of tile m+1, then O += V^T P^T of tile m
+    //     vector ALUs:  probabilities of tile m, then the maxima of tile m+1
+    // so the exponentials of one tile run while the matrix cores work on the next.  K runs one
+    // tile ahead of V: step m reads K of tile m+1 and V of tile m (LDS buffers (m+1)&1 and m&1)
+    // while K of tile m+2 and V of tile m+1 load into the other two; one barrier per step.  The
+    // rescale for tile m+1 (rare) closes step m, after O has taken tile m.
+    const int nm = sp.n_mid();
+    if (nm > 0) {
+        const int jm = sp.mid_lo * kTileN;
+        const TileInfo full = {0, 0, 1, 1};  // (the fast steps read none of it)
+        issue(jm, 0, KRows());
+        issue(jm, 0, VRows());
+        if (nm > 1)
+            issue(jm + kTileN, 1, KRows());
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        scores(sacc[0], lds[0][0], full, Fast());
+        if (__any(tile_max(sacc[0], full, Fast(), alpha)))
+            rescale(alpha);
+
+        auto mid_step = [&](const int m, auto buf_c) __attribute__((always_inline)) {  // m + 1 < nm
+            constexpr int buf = decltype(buf_c)::value;  // m & 1
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's loads of the last step landed
+            __syncthreads();                            // ... and every wave's; K buffer buf, V buffer buf^1 free
+            if (m + 2 < nm)
+                issue(jm + (m + 2) * kTileN, buf, KRows());
+            issue(jm + (m + 1) * kTileN, buf ^ 1, VRows());
+            scores(sacc[buf ^ 1], lds[buf ^ 1][0], full, Fast());
+            bf16x8 pf[2][2];
+            probs(sacc[buf], full, Fast(), pf);
+            accumulate(pf, lds[buf][1], full, Fast());
+            const bool grow = tile_max(sacc[buf ^ 1], full, Fast(), alpha);
+            if (__any(grow))
+                rescale(alpha);
+        };
+        // The last middle tile: its probabilities and O += V^T P^T.
+        auto mid_last = [&](auto buf_c) __attribute__((always_inline)) {
+            constexpr int buf = decltype(buf_c)::value;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __syncthreads();
+            bf16x8 pf[2][2];
+            probs(sacc[buf], full, Fast(), pf);
+            accumulate(pf, lds[buf][1], full, Fast());
+        };
+        int m = 0;
+        for (; m + 2 < nm; m += 2) {
+            mid_step(m, Even());
+            mid_step(m + 1, Odd());
+        }
+        if (m + 1 < nm) {
+            mid_step(m, Even());
+            mid_last(Odd());
+        } else {
+            mid_last(Even());
+        }
     }
 
     // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
@@ -465,19 +570,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 }
 
-// Debug: the set of (query, key) pairs the prefill kernel admits, from the same tile walk,
-// chunk selection, mask-free classification and element predicate.  One workgroup per q-tile.
+// Debug: the set of (query, key) pairs the prefill kernel admits, from the same tile walk and
+// split: edge tiles through the chunk selection, mask-free classification and element
+// predicate; middle tiles whole and unmasked, as the kernel takes them.  One workgroup per
+// q-tile.
 __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int w_loc, int s)
 {
     const int t0 = blockIdx.x * Tm;
     const int t1 = min(t0 + Tm - 1, L - 1);
     const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
+    const WalkSplit sp = split_walk(tw, t0, t1, w_loc, kTileN);
     for (int n = 0; n < tw.count(); ++n) {
-        const int j0 = tw.tile(n) * kTileN;
-        int c_lo, c_hi;
-        tile_chunks(j0, kTileN / kChunkN, t0, t1, w_loc, s, c_lo, c_hi);
+        const bool middle = n >= sp.n_edge;
+        const int j0 = (middle ? sp.mid_lo + (n - sp.n_edge) : sp.edge_tile(tw, n)) * kTileN;
+        int c_lo = 0, c_hi = kTileN / kChunkN - 1;
+        if (!middle)
+            tile_chunks(j0, kTileN / kChunkN, t0, t1, w_loc, s, c_lo, c_hi);
         const int k_lo = j0 + c_lo * kChunkN, k_hi = j0 + c_hi * kChunkN + kChunkN - 1;
-        const bool mask_free = range_mask_free(k_lo, k_hi, t0, t1, w_loc, s);
+        const bool mask_free = middle || range_mask_free(k_lo, k_hi, t0, t1, w_loc, s);
         const int width = k_hi - k_lo + 1;
         for (int idx = threadIdx.x; idx < Tm * width; idx += blockDim.x) {
             const int t = t0 + idx / width;
