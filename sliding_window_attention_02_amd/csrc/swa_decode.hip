@@ -274,8 +274,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
     }
     if (fused && slot_t >= seg_lo && slot_t < seg_hi && lane < kPieces) {
         const int ch = (slot_t - seg_lo) / kChunk, r = (slot_t - seg_lo) % kChunk;
-        *reinterpret_cast<u32x4 *>(&vlds[0][0] + ch * kChunk * kRowBytes + r * kRowBytes + 16 * (lane ^ swz_v(r))) =
-            vn_piece;
+        // Rows past the segment loaded the segment's last slot.  When that slot is the one this
+        // step writes (with s = 0, the step that first fills the ring's last slot is the step
+        // the ring wraps), they hold its bytes from before the write, which may not be finite;
+        // their weight is 0, but 0 * NaN is NaN, so they take the new row as well.
+        const int r_end = slot_t == seg_hi - 1 ? kChunk : r + 1;
+        for (int rr = r; rr < r_end; ++rr)
+            *reinterpret_cast<u32x4 *>(&vlds[0][0] + ch * kChunk * kRowBytes + rr * kRowBytes +
+                                       16 * (lane ^ swz_v(rr))) = vn_piece;
     }
     const int vt_row0 = 8 * g16 + (c16 >> 2);
     const int vt_half = 8 * (c16 & 1);

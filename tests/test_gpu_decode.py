@@ -140,6 +140,32 @@ def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv):
     assert np.isfinite(got).all() and err.max() <= TOL
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,s", [(2, 4, 4, 64, 5, 0), (1, 8, 2, 128, 40, 0), (2, 8, 2, 128, 33, 0),
+                                           (1, 8, 2, 128, 150, 0), (2, 4, 2, 64, 7, 3)])
+def test_fused_append_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s):
+    """The fused step (append and attend in one launch) from a NaN-filled cache.  With s = 0
+    and s + w_loc not a multiple of 32, the step that wraps the ring is the one that first
+    writes the segment's last slot, which the rows past the segment also load."""
+    say("fused-empty", B, Hq, Hkv, d, w, s)
+    T = 2 * (s + w) + 3
+    qs, ks, vs = history(98, T, B, Hq, Hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    ref = orc.prefill(f64(qs), f64(ks), f64(vs), w, s, scale, 0)
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s, 0)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s, 0)
+    qg, kg, vg = qs.cuda(), ks.cuda(), vs.cuda()
+    outs = []
+    for t in range(T):
+        outs.append(swa.append_decode_step(qg[:, t].contiguous(), kc, vc, kg[:, t].contiguous(), vg[:, t].contiguous(),
+                                           gpos([t] * B), w, s, scale, workspace=ws))
+    got = torch.stack(outs, dim=1).cpu().numpy()
+    err = np.abs(got - ref)
+    say(f"max {err.max():.3e}")
+    assert np.isfinite(got).all() and err.max() <= TOL
+
+
 @pytest.mark.parametrize("B", [1, 64])
 def test_decode_workload_positions(B):
     """SWA(64,4), Hq=32, Hkv=8, d=128 at positions 2^7 .. 2^18: the cache is seeded with the
