@@ -179,6 +179,66 @@ int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache
                       float *out, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s,
                       float scale, int conv, void *stream);
 
+/*
+ * Decoder-layer decode step around SWA(w,s) attention, for the multi-layer decode
+ * measurement of page "滑动窗口注意力（SWA）配 sinks 比 post-training 线性注意力更划算"
+ * (section "小窗口也有工程优势": decode throughput and state memory of a 4-layer Transformer
+ * at batch 1 from 128 to 256K tokens of context).  The pages fix no layer recipe; this is the
+ * standard pre-norm layer, with activations stored in bf16 where noted:
+ *
+ *   h = bf16(rmsnorm(x) * attn_norm);  q | k_new | v_new = bf16(w_qkv h)
+ *   o = SWA(w,s) decode of q at pos[b] after appending (k_new, v_new) there (as
+ *       swa_append_decode_step, on this layer's cache)
+ *   x += w_o bf16(o);  h = bf16(rmsnorm(x) * mlp_norm)
+ *   x += w_down bf16(silu(gate) * up),  gate | up = w_gate_up h
+ *
+ * with rmsnorm(x) = x / sqrt(mean(x^2) + eps), silu(z) = z / (1 + e^-z); no positional
+ * encoding, no output head.  All pointers are device memory owned by the caller; every call
+ * is asynchronous on `stream`; nothing is allocated.
+ */
+enum { SWA_LINEAR_STORE = 0, SWA_LINEAR_ADD = 1, SWA_LINEAR_SILU_MUL = 2 };
+
+typedef struct swa_layer_weights {
+    const void *attn_norm;  /* bf16 [dm] */
+    const void *w_qkv;      /* bf16 [(Hq + 2 Hkv) d][dm]: q rows (head-major), then k, then v */
+    const void *w_o;        /* bf16 [dm][Hq d] */
+    const void *mlp_norm;   /* bf16 [dm] */
+    const void *w_gate_up;  /* bf16 [2 f][dm]: gate rows, then up rows */
+    const void *w_down;     /* bf16 [dm][f] */
+} swa_layer_weights;
+
+/* out bf16 [B][n] = bf16(x / sqrt(mean(x^2) + eps) * weight); x fp32 [B][n], weight bf16 [n].
+ * Errors: SWA_EINVAL for null or unaligned pointers, B < 1, n not a positive multiple of 4,
+ * eps negative or not finite. */
+int swa_rmsnorm(const float *x, const void *weight, void *out, int B, int n, float eps, void *stream);
+
+/* y[b][n] = sum_k W[n][k] x[b][k], fp32 accumulation, for x [B][K] bf16 (x_f32 = 0) or fp32
+ * rounded to bf16 as it is read (x_f32 != 0); K % 8 == 0.
+ *   SWA_LINEAR_STORE     W bf16 [N][K]; out bf16 [B][N] = bf16(y)
+ *   SWA_LINEAR_ADD       W bf16 [N][K]; out fp32 [B][N] += y
+ *   SWA_LINEAR_SILU_MUL  W bf16 [2N][K] (gate rows, then up rows); out bf16 [B][N] = bf16(silu(g) u)
+ * Errors: SWA_EINVAL for null or unaligned pointers, an unknown mode, B or N < 1, K not a
+ * positive multiple of 8; SWA_EUNSUPPORTED for N or K above 2^28. */
+int swa_linear(const void *W, const void *x, int x_f32, void *out, int mode, int B, int N, int K,
+               void *stream);
+
+/* Workspace bytes swa_layer_decode_step needs (0 for invalid arguments). */
+size_t swa_layer_workspace_bytes(int B, int dm, int Hq, int Hkv, int d, int f, int w, int s, int conv);
+
+/* One decode step of one layer for B sequences:
+ *   x        fp32 [B][dm] residual stream (in/out, updated in place)
+ *   wts      the layer's weights (host struct of device pointers, each 16-byte aligned)
+ *   k_cache, bf16 [B][Hkv][s + w_loc][d] (in/out): this layer's sink + ring cache, the layout
+ *   v_cache  swa_kv_append writes; the step appends its token at pos[b]
+ *   pos      int64 [B] device: position of this step's token
+ * dm, f % 8 == 0; d in {64, 128}.  Seven launches on `stream`.
+ * Errors: as swa_append_decode_step and swa_linear, plus SWA_EINVAL for a workspace smaller
+ * than swa_layer_workspace_bytes. */
+int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache, void *v_cache,
+                          const int64_t *pos, int B, int dm, int Hq, int Hkv, int d, int f, int w, int s,
+                          float scale, int conv, float eps, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char *swa_last_error(void);
 

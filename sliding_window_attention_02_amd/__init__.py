@@ -17,7 +17,11 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     kv_append,
     last_error,
+    layer_decode_step,
+    layer_workspace_bytes,
+    linear,
     local_window,
     prefill,
     prefill_chunk,
+    rmsnorm,
 )

@@ -34,7 +34,17 @@ EXPORTS = (
     "swa_last_error",
     "swa_debug_prefill_mask",
     "swa_debug_decode_slots",
+    "swa_rmsnorm",
+    "swa_linear",
+    "swa_layer_workspace_bytes",
+    "swa_layer_decode_step",
 )
+
+LINEAR_MODES = {"store": 0, "add": 1, "silu_mul": 2}
+
+
+class _LayerWeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")]
 
 _lib = None
 
@@ -76,6 +86,15 @@ def lib() -> ctypes.CDLL:
     L.swa_debug_prefill_mask.restype = i32
     L.swa_debug_decode_slots.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     L.swa_debug_decode_slots.restype = i32
+    L.swa_rmsnorm.argtypes = [vp, vp, vp, i32, i32, f32, vp]
+    L.swa_rmsnorm.restype = i32
+    L.swa_linear.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp]
+    L.swa_linear.restype = i32
+    L.swa_layer_workspace_bytes.argtypes = [i32] * 9
+    L.swa_layer_workspace_bytes.restype = sz
+    L.swa_layer_decode_step.argtypes = [vp, ctypes.POINTER(_LayerWeightsC), vp, vp, vp] + [i32] * 8 + [f32, i32, f32,
+                                                                                             vp, sz, vp]
+    L.swa_layer_decode_step.restype = i32
     _lib = L
     return L
 
@@ -259,3 +278,80 @@ def debug_decode_slots(pos, w: int, s: int, conv: int = ADDITIVE):
     out = torch.empty((B, s + local_window(w, s, conv)), dtype=torch.int64, device=pos.device)
     _check(lib().swa_debug_decode_slots(out.data_ptr(), pos.data_ptr(), B, w, s, conv, _stream(pos)))
     return out
+
+
+# ------------------------------------------------------------------ decoder-layer pieces
+
+def rmsnorm(x, weight, eps: float, out=None):
+    """bf16 [B][n] = bf16(x / sqrt(mean(x^2) + eps) * weight); x fp32 [B][n], weight bf16 [n]."""
+    B, n = x.shape
+    _need(x, "x", torch.float32)
+    _need(weight, "weight", torch.bfloat16, (n,))
+    if out is None:
+        out = torch.empty((B, n), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (B, n))
+    _check(lib().swa_rmsnorm(x.data_ptr(), weight.data_ptr(), out.data_ptr(), B, n, float(eps), _stream(x)))
+    return out
+
+
+def linear(W, x, mode: str = "store", out=None):
+    """y = W x over x [B][K] (bf16, or fp32 rounded to bf16 on read), fp32 accumulation.
+
+    mode "store": W bf16 [N][K] -> bf16 [B][N]; "add": W [N][K], out fp32 [B][N] += y (out
+    required); "silu_mul": W [2N][K] (gate rows, then up rows) -> bf16 silu(gate) * up [B][N].
+    """
+    B, K = x.shape
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bf16 or fp32")
+    _need(x, "x", x.dtype)
+    _need(W, "W", torch.bfloat16)
+    if W.dim() != 2 or W.shape[1] != K:
+        raise ValueError(f"W must be [N][{K}]")
+    m = LINEAR_MODES[mode]
+    N = W.shape[0] // 2 if mode == "silu_mul" else W.shape[0]
+    if mode == "add":
+        if out is None:
+            raise ValueError("mode 'add' accumulates into out, which must be given")
+        _need(out, "out", torch.float32, (B, N))
+    else:
+        if out is None:
+            out = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+        _need(out, "out", torch.bfloat16, (B, N))
+    _check(lib().swa_linear(W.data_ptr(), x.data_ptr(), int(x.dtype == torch.float32), out.data_ptr(), m, B, N, K,
+                            _stream(x)))
+    return out
+
+
+def layer_workspace_bytes(B: int, dm: int, Hq: int, Hkv: int, d: int, f: int, w: int, s: int,
+                          conv: int = ADDITIVE) -> int:
+    return int(lib().swa_layer_workspace_bytes(B, dm, Hq, Hkv, d, f, w, s, conv))
+
+
+def layer_decode_step(x, weights: dict, k_cache, v_cache, pos, Hq: int, w: int, s: int, scale: float | None = None,
+                      conv: int = ADDITIVE, eps: float = 1e-5, workspace=None):
+    """One decode step of one decoder layer; x fp32 [B][dm] is updated in place.
+
+    weights: dict of bf16 tensors attn_norm [dm], w_qkv [(Hq + 2 Hkv) d][dm], w_o [dm][Hq d],
+    mlp_norm [dm], w_gate_up [2 f][dm], w_down [dm][f].  k_cache/v_cache: this layer's bf16
+    [B][Hkv][s + w_loc][d]; pos int64 [B]: position of this step's token.
+    """
+    B, dm = x.shape
+    _, Hkv, n_slots, d = k_cache.shape
+    f = weights["w_down"].shape[1]
+    _need(x, "x", torch.float32)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _need(pos, "pos", torch.int64, (B,))
+    shapes = {"attn_norm": (dm,), "w_qkv": ((Hq + 2 * Hkv) * d, dm), "w_o": (dm, Hq * d), "mlp_norm": (dm,),
+              "w_gate_up": (2 * f, dm), "w_down": (dm, f)}
+    for name, shape in shapes.items():
+        _need(weights[name], name, torch.bfloat16, shape)
+    cw = _LayerWeightsC(*[weights[n].data_ptr() for n in shapes])
+    need = layer_workspace_bytes(B, dm, Hq, Hkv, d, f, w, s, conv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_layer_decode_step(x.data_ptr(), ctypes.byref(cw), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       pos.data_ptr(), B, dm, Hq, Hkv, d, f, w, s, scale, conv, float(eps),
+                                       workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return x

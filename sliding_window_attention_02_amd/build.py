@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libswa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["swa_api.cpp", "swa_prefill.hip", "swa_decode.hip"]
+SOURCES = ["swa_api.cpp", "swa_prefill.hip", "swa_decode.hip", "swa_model.hip"]
 
 # Per-source flags.  The decode kernel runs one wave per workgroup, so the compiler may give
 # it AGPRs; keeping MFMA results in arch VGPRs spares the AGPR -> VGPR copies before the

@@ -180,6 +180,59 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
     return hip_status(fn, e);
 }
 
+// ----------------------------------------------------------------- decoder-layer step
+//
+// Workspace of one layer step: bf16 h [B][dm], q [B][Hq d], k_new and v_new [B][Hkv d], fp32
+// attention output [B][Hq d], bf16 MLP activation [B][f], then the attention's split
+// workspace; each piece starts on a 256-byte boundary.
+struct LayerWorkspace {
+    size_t h, q, kn, vn, o, act, dec, total;
+};
+
+LayerWorkspace layer_workspace(int B, int dm, int Hq, int Hkv, int d, int f, size_t dec_bytes)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    LayerWorkspace L;
+    size_t off = 0;
+    L.h = off;
+    off += up((size_t)B * dm * 2);
+    L.q = off;
+    off += up((size_t)B * Hq * d * 2);
+    L.kn = off;
+    off += up((size_t)B * Hkv * d * 2);
+    L.vn = off;
+    off += up((size_t)B * Hkv * d * 2);
+    L.o = off;
+    off += up((size_t)B * Hq * d * 4);
+    L.act = off;
+    off += up((size_t)B * f * 2);
+    L.dec = off;
+    off += up(dec_bytes);
+    L.total = off;
+    return L;
+}
+
+int check_layer_dims(const char *fn, int B, int dm, int Hq, int Hkv, int d, int f)
+{
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    if (dm < 8 || dm % 8 != 0 || dm > (1 << 24))
+        return fail(SWA_EINVAL, "%s: dm must be a multiple of 8 in [8, 2^24] (got %d)", fn, dm);
+    if (f < 8 || f % 8 != 0 || f > (1 << 24))
+        return fail(SWA_EINVAL, "%s: f must be a multiple of 8 in [8, 2^24] (got %d)", fn, f);
+    if ((long long)B * (dm > f ? dm : f) > 0x7fffffffLL || (long long)(Hq + 2 * Hkv) * d > (1 << 24))
+        return fail(SWA_EUNSUPPORTED, "%s: sizes exceed the supported range", fn);
+    return SWA_OK;
+}
+
+int check_eps(const char *fn, float eps)
+{
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(SWA_EINVAL, "%s: eps must be finite and >= 0", fn);
+    return SWA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,6 +352,113 @@ int swa_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w, 
         return rc;
     return hip_status(fn, swa::launch_debug_decode_slots(slot_pos, pos, B, w_loc, s,
                                                          static_cast<hipStream_t>(stream)));
+}
+
+int swa_rmsnorm(const float *x, const void *weight, void *out, int B, int n, float eps, void *stream)
+{
+    const char *fn = "swa_rmsnorm";
+    CHECK_PTR(x);
+    CHECK_PTR(weight);
+    CHECK_PTR(out);
+    if (B < 1 || n < 4 || n % 4 != 0)
+        return fail(SWA_EINVAL, "%s: need B >= 1 and n a positive multiple of 4 (got %d, %d)", fn, B, n);
+    int rc = check_eps(fn, eps);
+    if (rc)
+        return rc;
+    return hip_status(fn, swa::launch_rmsnorm(x, weight, out, B, n, eps, static_cast<hipStream_t>(stream)));
+}
+
+int swa_linear(const void *W, const void *x, int x_f32, void *out, int mode, int B, int N, int K, void *stream)
+{
+    const char *fn = "swa_linear";
+    CHECK_PTR(W);
+    CHECK_PTR(x);
+    CHECK_PTR(out);
+    if (mode != SWA_LINEAR_STORE && mode != SWA_LINEAR_ADD && mode != SWA_LINEAR_SILU_MUL)
+        return fail(SWA_EINVAL, "%s: unknown mode %d", fn, mode);
+    if (B < 1 || N < 1 || K < 8 || K % 8 != 0)
+        return fail(SWA_EINVAL, "%s: need B, N >= 1 and K a positive multiple of 8 (got %d, %d, %d)", fn, B, N, K);
+    if (N > (1 << 28) || K > (1 << 28) || (long long)B * (N > K ? N : K) > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: sizes exceed the supported range", fn);
+    void *outs[3] = {out, out, out};
+    const int seg[4] = {0, N, N, N};
+    const int m = mode == SWA_LINEAR_STORE ? swa::LIN_STORE : mode == SWA_LINEAR_ADD ? swa::LIN_ADD : swa::LIN_SILU_MUL;
+    return hip_status(fn, swa::launch_linear(m, x_f32 != 0, W, x, B, N, K, outs, seg, static_cast<float *>(out),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t swa_layer_workspace_bytes(int B, int dm, int Hq, int Hkv, int d, int f, int w, int s, int conv)
+{
+    const char *fn = "swa_layer_workspace_bytes";
+    if (check_layer_dims(fn, B, dm, Hq, Hkv, d, f))
+        return 0;
+    int w_loc = 0;
+    if (resolve_window(fn, w, s, conv, &w_loc) || (long long)s + w_loc > 0x7fffffffLL)
+        return 0;
+    return layer_workspace(B, dm, Hq, Hkv, d, f, swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes).total;
+}
+
+int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache, void *v_cache, const int64_t *pos,
+                          int B, int dm, int Hq, int Hkv, int d, int f, int w, int s, float scale, int conv, float eps,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "swa_layer_decode_step";
+    CHECK_PTR(x);
+    if (wts == nullptr)
+        return fail(SWA_EINVAL, "%s: wts is null", fn);
+    CHECK_PTR(wts->attn_norm);
+    CHECK_PTR(wts->w_qkv);
+    CHECK_PTR(wts->w_o);
+    CHECK_PTR(wts->mlp_norm);
+    CHECK_PTR(wts->w_gate_up);
+    CHECK_PTR(wts->w_down);
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    CHECK_PTR(workspace);
+    if (pos == nullptr)
+        return fail(SWA_EINVAL, "%s: pos is null", fn);
+    int rc = check_layer_dims(fn, B, dm, Hq, Hkv, d, f);
+    if (rc)
+        return rc;
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((rc = check_scale(fn, scale)) || (rc = check_eps(fn, eps)))
+        return rc;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    const LayerWorkspace L = layer_workspace(B, dm, Hq, Hkv, d, f, plan.workspace_bytes);
+    if (workspace_bytes < L.total)
+        return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, L.total, workspace_bytes);
+    char *ws = static_cast<char *>(workspace);
+    void *h = ws + L.h, *q = ws + L.q, *kn = ws + L.kn, *vn = ws + L.vn, *act = ws + L.act;
+    float *o = reinterpret_cast<float *>(ws + L.o);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int nq = Hq * d, nkv = Hkv * d, nqkv = nq + 2 * nkv;
+    void *none[3] = {nullptr, nullptr, nullptr};
+    const int seg_none[4] = {0, 0, 0, 0};
+    void *qkv_out[3] = {q, kn, vn};
+    const int qkv_seg[4] = {0, nq, nq + nkv, nqkv};
+    void *act_out[3] = {act, act, act};
+    const int act_seg[4] = {0, f, f, f};
+    // h = norm(x); q, k_new, v_new = W_qkv h; attend (appending k_new, v_new); x += W_o o;
+    // h = norm(x); act = silu(W_gate h) * (W_up h); x += W_down act.
+    hipError_t e = swa::launch_rmsnorm(x, wts->attn_norm, h, B, dm, eps, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_STORE, false, wts->w_qkv, h, B, nqkv, dm, qkv_out, qkv_seg, nullptr, st);
+    if (e == hipSuccess)
+        e = swa::launch_decode(q, k_cache, v_cache, kn, vn, o, pos, B, Hq, Hkv, d, w_loc, s, scale,
+                               plan.workspace_bytes > 0 ? ws + L.dec : nullptr, plan, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_ADD, true, wts->w_o, o, B, dm, nq, none, seg_none, x, st);
+    if (e == hipSuccess)
+        e = swa::launch_rmsnorm(x, wts->mlp_norm, h, B, dm, eps, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_SILU_MUL, false, wts->w_gate_up, h, B, f, dm, act_out, act_seg, nullptr, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_ADD, false, wts->w_down, act, B, dm, f, none, seg_none, x, st);
+    return hip_status(fn, e);
 }
 
 }  // extern "C"

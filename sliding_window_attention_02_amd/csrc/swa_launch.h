@@ -76,6 +76,19 @@ struct ChunkPlan {
 };
 ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s);
 
+// ---------------------------------------------------------------- decoder-layer pieces
+//
+// out bf16 [B][n] = bf16(x / sqrt(mean(x^2) + eps) * g), x fp32 [B][n], g bf16 [n]; n % 4 == 0.
+hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int B, int n, float eps, hipStream_t stream);
+
+// y = W x for x [B][K] (bf16, or fp32 rounded to bf16 on read when x_f32), K % 8 == 0:
+//   LIN_STORE    W [N][K]; outputs [seg[i], seg[i+1]) -> out_bf16[i] as bf16 [B][seg[i+1] - seg[i]]
+//   LIN_ADD      W [N][K]; out_f32 [B][N] += y
+//   LIN_SILU_MUL W [2N][K] (gate rows, then up rows); out_bf16[0] [B][N] = bf16(silu(gate) * up)
+enum { LIN_STORE = 0, LIN_ADD = 1, LIN_SILU_MUL = 2 };
+hipError_t launch_linear(int mode, bool x_f32, const void *W, const void *x, int B, int N, int K,
+                         void *const out_bf16[3], const int seg[4], float *out_f32, hipStream_t stream);
+
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,
                                      hipStream_t stream);
 

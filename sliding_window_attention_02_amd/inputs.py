@@ -15,6 +15,11 @@ Recipe (every draw on the CPU, torch.Generator, fp32 N(0,1)):
     v of a position ([B][Hkv][d] each, k first), stream 1 gives the query [B][Hq][d].
     The same std / sink boost / bf16 rounding apply.
 
+  * decoder layers (multi-layer decode): one generator seeded with (seed, layer) draws, in
+    order, the two norm weights (1 + 0.1 N(0,1)) and the weight matrices w_qkv, w_o,
+    w_gate_up, w_down, each N(0,1) / sqrt(fan-in); all rounded to bf16.  The residual
+    stream of a step is N(0,1) fp32 from the generator seeded with (seed, 2, step).
+
 The workloads mirror the shapes the pages discuss: Llama-3.1-8B heads (32 q-heads, 8
 kv-heads, d=128) at 4K context with windows 64..512 as in the S-NIAH study, the decode
 sweep from 128 to 256K context, and Mistral-7B at 16K with window 4096.
@@ -166,3 +171,23 @@ def q_at(seed: int, position: int, B: int, Hq: int, d: int, std: float = 1.0):
     """Query bf16 [B][Hq][d] of the token at one absolute position."""
     g = torch.Generator().manual_seed(position_seed(seed, 1, position))
     return _round_bf16(torch.randn(B, Hq, d, generator=g, dtype=torch.float32) * std)
+
+
+def layer_weights(seed: int, layer: int, dm: int, Hq: int, Hkv: int, d: int, f: int) -> dict:
+    """bf16 CPU tensors of one decoder layer (names as the layer step takes them)."""
+    g = torch.Generator().manual_seed(position_seed(seed, 3, layer))
+    def mat(n, k):
+        return _round_bf16(torch.randn(n, k, generator=g) / (k ** 0.5))
+    out = {"attn_norm": _round_bf16(1 + 0.1 * torch.randn(dm, generator=g)),
+           "mlp_norm": _round_bf16(1 + 0.1 * torch.randn(dm, generator=g))}
+    out["w_qkv"] = mat((Hq + 2 * Hkv) * d, dm)
+    out["w_o"] = mat(dm, Hq * d)
+    out["w_gate_up"] = mat(2 * f, dm)
+    out["w_down"] = mat(dm, f)
+    return out
+
+
+def residual(seed: int, step: int, B: int, dm: int) -> torch.Tensor:
+    """fp32 [B][dm] N(0,1) residual-stream input of a step."""
+    g = torch.Generator().manual_seed(position_seed(seed, 2, step))
+    return torch.randn(B, dm, generator=g)

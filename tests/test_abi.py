@@ -163,3 +163,34 @@ def test_prefill_chunk_rejects_on_host(lib):
     assert call(conv=7) == binding.SWA_EINVAL
     assert call(w=4, conv=1) == binding.SWA_EINVAL  # TOTAL window leaves nothing after the sinks
     assert call(C=2 ** 30) == binding.SWA_EUNSUPPORTED
+
+
+def test_layer_pieces_reject_on_host(lib):
+    assert lib.swa_rmsnorm(None, A, A, 1, 64, 1e-5, None) == binding.SWA_EINVAL
+    assert lib.swa_rmsnorm(A, A, A, 1, 6, 1e-5, None) == binding.SWA_EINVAL and "multiple of 4" in err(lib)
+    assert lib.swa_rmsnorm(A, A, A, 0, 64, 1e-5, None) == binding.SWA_EINVAL
+    assert lib.swa_rmsnorm(A, A, A, 1, 64, -1.0, None) == binding.SWA_EINVAL and "eps" in err(lib)
+    assert lib.swa_linear(A, A, 0, A, 7, 1, 16, 64, None) == binding.SWA_EINVAL and "mode" in err(lib)
+    assert lib.swa_linear(A, A, 0, A, 0, 1, 16, 12, None) == binding.SWA_EINVAL and "multiple of 8" in err(lib)
+    assert lib.swa_linear(A, A, 0, A, 0, 1, 0, 64, None) == binding.SWA_EINVAL
+    assert lib.swa_linear(A, MIS, 0, A, 1, 1, 16, 64, None) == binding.SWA_EINVAL and "aligned" in err(lib)
+    assert lib.swa_linear(A, A, 0, A, 0, 1, 1 << 29, 64, None) == binding.SWA_EUNSUPPORTED
+
+
+def test_layer_step_workspace_query_and_rejection(lib):
+    dims = (1, 4096, 32, 8, 128, 14336)
+    ws = lib.swa_layer_workspace_bytes(*dims, 64, 4, 0)
+    # h, q, k_new, v_new, o, act (each 256-byte aligned); SWA(64,4) needs no split workspace
+    assert ws == 4096 * 2 + 4096 * 2 + 1024 * 2 * 2 + 4096 * 4 + 14336 * 2
+    assert lib.swa_layer_workspace_bytes(*dims, 4096, 0, 0) > ws  # a split decode adds partials
+    assert lib.swa_layer_workspace_bytes(1, 4100, 32, 8, 128, 14336, 64, 4, 0) == 0  # dm % 8
+    wts = binding._LayerWeightsC(A, A, A, A, A, A)
+    f = lib.swa_layer_decode_step
+    args = lambda **kw: [kw.get("x", A), ctypes.byref(kw.get("wts", wts)), A, A, kw.get("pos", A), 1, 4096, 32, 8, 128,
+                         kw.get("f", 14336), 64, 4, 0.1, 0, kw.get("eps", 1e-5), A, kw.get("ws", ws), None]
+    assert f(*args(ws=ws - 1)) == binding.SWA_EINVAL and "workspace" in err(lib)
+    assert f(*args(pos=None)) == binding.SWA_EINVAL and "pos" in err(lib)
+    assert f(*args(f=100)) == binding.SWA_EINVAL and "f must be" in err(lib)
+    assert f(*args(eps=float("inf"))) == binding.SWA_EINVAL and "eps" in err(lib)
+    assert f(*args(wts=binding._LayerWeightsC(A, A, None, A, A, A))) == binding.SWA_EINVAL and "w_o" in err(lib)
+    assert f(*args(x=MIS)) == binding.SWA_EINVAL and "aligned" in err(lib)

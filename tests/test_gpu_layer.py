@@ -1,0 +1,189 @@
+"""GPU parity of the decoder-layer pieces (swa_rmsnorm, swa_linear, swa_layer_decode_step)
+against the fp64 layer oracle, through the C ABI.
+
+Tolerances come from the arithmetic: outputs stored in bf16 may differ from the fp64 value
+by one bf16 rounding (2^-8 relative) plus the fp32 accumulation error of the products
+(bounded here by 1e-5 of the sum of |w x|).  Layer steps take fresh seeded residual inputs
+each step, so only the KV history is carried between steps, and every layer is compared with
+the oracle layer on the same input (the GPU's); the bar there is max abs error <= 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_attention_02_amd as swa
+from oracle import layer as lo
+from sliding_window_attention_02_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ------------------------------------------------------------------------------ rmsnorm
+
+@pytest.mark.parametrize("B,n", [(1, 4096), (3, 260), (2, 14336)])
+def test_rmsnorm_matches_oracle(B, n):
+    say("rmsnorm", B, n)
+    x = inputs.residual(11, 0, B, n) * 3.0
+    g = inputs.layer_weights(11, 0, n, 1, 1, 64, 8)["attn_norm"]
+    got = f64(swa.rmsnorm(x.cuda(), g.cuda(), 1e-5))
+    ref = lo.rmsnorm(f64(x), f64(g), 1e-5)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+    assert np.mean(got == lo.bf16_round(ref)) > 0.99
+
+
+# ------------------------------------------------------------------------------- linear
+
+LINEAR_CASES = [
+    # mode, B, N, K, x in fp32
+    ("store", 1, 6144, 4096, False), ("store", 3, 37, 264, False), ("store", 2, 64, 4096, True),
+    ("add", 1, 4096, 4096, True), ("add", 5, 100, 4096, False), ("add", 1, 4096, 14336, False),
+    ("silu_mul", 1, 14336, 4096, False), ("silu_mul", 2, 33, 520, False),
+]
+
+
+@pytest.mark.parametrize("mode,B,N,K,x_f32", LINEAR_CASES)
+def test_linear_matches_oracle(mode, B, N, K, x_f32):
+    say("linear", mode, B, N, K, x_f32)
+    g = torch.Generator().manual_seed(N * 7 + K)
+    rows = 2 * N if mode == "silu_mul" else N
+    W = (torch.randn(rows, K, generator=g) / K ** 0.5).to(torch.bfloat16)
+    x = torch.randn(B, K, generator=g) * 2.0
+    if not x_f32:
+        x = x.to(torch.bfloat16)
+    xb = lo.bf16_round(f64(x))  # what the kernel multiplies (fp32 input is rounded on read)
+    Wd = f64(W)
+    prod = xb @ Wd.T
+    absum = np.abs(xb) @ np.abs(Wd).T
+    if mode == "add":
+        out0 = torch.randn(B, N, generator=g)
+        got = f64(swa.linear(W.cuda(), x.cuda(), "add", out=out0.clone().cuda()))
+        ref = f64(out0) + prod
+        assert np.all(np.abs(got - ref) <= 1e-5 * absum + 1e-6 * np.abs(f64(out0)) + 1e-6)
+        return
+    got = f64(swa.linear(W.cuda(), x.cuda(), mode))
+    if mode == "store":
+        ref, bound = prod, 1e-5 * absum
+    else:
+        gate, up = prod[:, :N], prod[:, N:]
+        ref = lo.silu(gate) * up
+        bound = 2e-5 * (absum[:, :N] * np.abs(up) + absum[:, N:] * (np.abs(gate) + 1.0))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + bound + 1e-30)
+
+
+# ---------------------------------------------------------------------------- layer step
+
+def oracle_weights(w):
+    return lo.LayerWeights(g_attn=f64(w["attn_norm"]), w_qkv=f64(w["w_qkv"]), w_o=f64(w["w_o"]),
+                           g_mlp=f64(w["mlp_norm"]), w_gate_up=f64(w["w_gate_up"]), w_down=f64(w["w_down"]))
+
+
+def run_stack(layers, B, dm, Hq, Hkv, d, f, steps, seed, positions=None, prefill=None):
+    """Run `steps` decode steps of a stack of layers [(weights, w, s)] on the GPU and, layer by
+    layer on the GPU's inputs, in the oracle; returns the worst max-abs difference.
+
+    positions: [steps] positions (default 0..steps-1).  prefill: per layer, a list of
+    (position, k [B][Hkv][d], v) already in the cache before the first step.
+    """
+    eps, conv = 1e-5, 0
+    scale = 1.0 / np.sqrt(d)
+    positions = list(range(steps)) if positions is None else positions
+    gw, ow, caches, hists, workspaces = [], [], [], [], []
+    for li, (w, wn, s) in enumerate(layers):
+        gw.append({k: v.cuda() for k, v in w.items()})
+        ow.append(oracle_weights(w))
+        kc, vc = swa.alloc_cache(B, Hkv, d, wn, s, conv)
+        kc.fill_(float("nan"))
+        vc.fill_(float("nan"))
+        hist = [lo.History() for _ in range(B)]
+        for (p, kk, vv) in (prefill[li] if prefill else []):
+            pos = torch.full((B,), p, dtype=torch.int64, device="cuda")
+            swa.kv_append(kc, vc, kk[:, None].contiguous().cuda(), vv[:, None].contiguous().cuda(), pos, wn, s, conv)
+            for b in range(B):
+                hist[b].add(p, f64(kk[b]), f64(vv[b]))
+        caches.append((kc, vc))
+        hists.append(hist)
+        workspaces.append(torch.empty(swa.layer_workspace_bytes(B, dm, Hq, Hkv, d, f, wn, s, conv), dtype=torch.uint8,
+                                      device="cuda"))
+    worst = 0.0
+    for step, p in enumerate(positions):
+        xg = inputs.residual(seed, step, B, dm).cuda()
+        pos = torch.full((B,), p, dtype=torch.int64, device="cuda")
+        for li, (w, wn, s) in enumerate(layers):
+            # Each layer is compared on the same input: the oracle layer takes the GPU's input
+            # to that layer, so differences do not compound through the stack (each oracle
+            # layer keeps its own history of the keys and values it computed).
+            x_in = f64(xg)
+            swa.layer_decode_step(xg, gw[li], caches[li][0], caches[li][1], pos, Hq, wn, s, scale, conv, eps,
+                                  workspace=workspaces[li])
+            ref = lo.layer_step(x_in, ow[li], hists[li], [p] * B, Hq, Hkv, d, wn, s, scale, conv, eps)
+            got = f64(xg)
+            assert np.isfinite(got).all()
+            worst = max(worst, float(np.abs(got - ref).max()))
+    return worst
+
+
+@pytest.mark.parametrize("w,s", [(8, 2), (5, 0), (300, 0)])
+def test_layer_step_small_dims_through_wrap(w, s):
+    """B=2, dm=256, Hq=4, Hkv=2, d=64, f=384; 20 steps from an empty (NaN-filled) cache: sink
+    fill, ring fill and wrap-around (w=300: the window covers every step)."""
+    B, dm, Hq, Hkv, d, f = 2, 256, 4, 2, 64, 384
+    say("layer small", w, s)
+    layer = (inputs.layer_weights(21, 0, dm, Hq, Hkv, d, f), w, s)
+    worst = run_stack([layer], B, dm, Hq, Hkv, d, f, steps=20, seed=21)
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_layer_step_split_decode():
+    """A 200-slot full-attention cache (s=0, w=200): the attention inside the step splits the
+    slots over three workgroups and merges the partials from the layer's workspace."""
+    B, dm, Hq, Hkv, d, f = 1, 256, 8, 2, 128, 256
+    say("layer split")
+    w = 200
+    gen = dict(B=B, Hkv=Hkv, d=d, std=1.0)
+    pre = []
+    for p in range(150):
+        kk, vv = inputs.kv_at(31, p, **gen)
+        pre.append((p, kk, vv))
+    layer = (inputs.layer_weights(31, 0, dm, Hq, Hkv, d, f), w, 0)
+    worst = run_stack([layer], B, dm, Hq, Hkv, d, f, steps=6, seed=31, positions=list(range(150, 156)),
+                      prefill=[pre])
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_layer_step_llama_dims_far_position():
+    """Llama-3.1-8B layer shape (dm=4096, Hq=32, Hkv=8, d=128, f=14336), SWA(64,4), B=1, three
+    steps at position 2^18 after the sinks and the window before it."""
+    B, dm, Hq, Hkv, d, f = 1, 4096, 32, 8, 128, 14336
+    w, s, P = 64, 4, 2 ** 18
+    say("layer llama", P)
+    gen = dict(B=B, Hkv=Hkv, d=d, std=1.0)
+    pre = [(p, *inputs.kv_at(41, p, **gen)) for p in list(range(s)) + list(range(P - w, P))]
+    layer = (inputs.layer_weights(41, 0, dm, Hq, Hkv, d, f), w, s)
+    worst = run_stack([layer], B, dm, Hq, Hkv, d, f, steps=3, seed=41, positions=[P, P + 1, P + 2], prefill=[pre])
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
+
+
+def test_hybrid_stack_of_window_and_full_layers():
+    """Per-layer dispatch: an SWA(8,2) layer, a full-attention layer (a window wider than the
+    run, no sinks) and an SWA(16,4) layer, each with its own cache; 24 chained steps."""
+    B, dm, Hq, Hkv, d, f = 2, 512, 8, 4, 128, 512
+    say("hybrid stack")
+    layers = [(inputs.layer_weights(51, 0, dm, Hq, Hkv, d, f), 8, 2),
+              (inputs.layer_weights(51, 1, dm, Hq, Hkv, d, f), 64, 0),
+              (inputs.layer_weights(51, 2, dm, Hq, Hkv, d, f), 16, 4)]
+    worst = run_stack(layers, B, dm, Hq, Hkv, d, f, steps=24, seed=51)
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
