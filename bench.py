@@ -87,6 +87,11 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4096, help="with --chunked: tokens per chunk")
     ap.add_argument("--compare-full", action="store_true", help="only time SWA against full causal attention")
     ap.add_argument("--cache-sets", type=int, default=1, help="with --decode-only: caches the steps rotate over")
+    ap.add_argument("--model-sweep", action="store_true",
+                    help="only time decode of a 4-layer decoder (Llama-3.1-8B layer shape, batch 1) against context")
+    ap.add_argument("--model-layers", type=int, default=4)
+    ap.add_argument("--model-tokens", type=int, default=8, help="with --model-sweep: tokens per HIP graph")
+    ap.add_argument("--model-contexts", default="128,1024,4096,16384,65536,262144")
     return ap.parse_args()
 
 
@@ -363,6 +368,112 @@ def compare_full(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def model_sweep(args, dev):
+    """--model-sweep: decode throughput and KV state memory of a stack of decoder layers at
+    batch 1 against context length, the measurement the pages report for a 4-layer Transformer
+    (128 to 256K tokens of context).  Layers have the Llama-3.1-8B shape (dm 4096, 32 q-heads,
+    8 kv-heads, d 128, SwiGLU 14336) with seeded random bf16 weights; attention is SWA(w,4) on a
+    sink + ring cache for w in 64..512, full attention (a cache holding every position), or a
+    hybrid stack (every layer SWA(64,4) but the last, which is full).  Each point is a HIP graph
+    of T tokens, every token one swa_layer_decode_step per layer; caches hold seeded random
+    keys and values for the positions before the context.  One JSON line."""
+    import math
+
+    import torch
+
+    import sliding_window_attention_02_amd as swa
+    from sliding_window_attention_02_amd import inputs
+
+    nl = args.model_layers
+    dm, Hq, Hkv, d, f = 4096, 32, 8, 128, 14336
+    B, T, eps, seed = 1, args.model_tokens, 1e-5, 2026
+    scale = 1.0 / math.sqrt(d)
+    weights = [{k: v.to(dev) for k, v in inputs.layer_weights(seed, li, dm, Hq, Hkv, d, f).items()}
+               for li in range(nl)]
+    weight_bytes = sum(v.numel() * 2 for w in weights for v in w.values())
+    rec = {"model": {"layers": nl, "dm": dm, "Hq": Hq, "Hkv": Hkv, "d": d, "f": f, "batch": B,
+                     "weight_gb": round(weight_bytes / 1e9, 4), "tokens_per_graph": T}, "points": []}
+
+    # Streaming bandwidth of the linear kernel on the largest matrix (gate and up, 235 MB),
+    # rotating over the layers so that no launch finds its weights in the Infinity Cache.
+    h = torch.randn(B, dm, device=dev).to(torch.bfloat16)
+    act = torch.empty(B, f, dtype=torch.bfloat16, device=dev)
+    for li in range(nl):
+        swa.linear(weights[li]["w_gate_up"], h, "silu_mul", out=act)
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for li in range(nl):
+            swa.linear(weights[li]["w_gate_up"], h, "silu_mul", out=act)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nl)
+    gu_bytes = 2 * f * dm * 2
+    rec["linear_gate_up"] = {"us_per_launch": round(us, 2), "gb_per_s": round(gu_bytes / (us * 1e-6) / 1e9, 1),
+                             "frac_of_hbm_peak": round(gu_bytes / (us * 1e-6) / 8e12, 4)}
+
+    variants = [("swa64_4", [(64, 4)] * nl), ("swa128_4", [(128, 4)] * nl), ("swa256_4", [(256, 4)] * nl),
+                ("swa512_4", [(512, 4)] * nl), ("full", None), ("hybrid_swa64_4_last_full", "hybrid")]
+    contexts = [int(c) for c in args.model_contexts.split(",")]
+    gen = torch.Generator(device=dev)
+    for P in contexts:
+        for name, cfg in variants:
+            if cfg is None:
+                layer_cfg = [(P + T, 0)] * nl  # a window covering every position: full attention
+            elif cfg == "hybrid":
+                layer_cfg = [(64, 4)] * (nl - 1) + [(P + T, 0)]
+            else:
+                layer_cfg = cfg
+            gen.manual_seed(seed + P)
+            caches = []
+            for (w, s) in layer_cfg:
+                kc, vc = swa.alloc_cache(B, Hkv, d, w, s, device=dev)
+                kc.copy_(torch.randn(kc.shape, generator=gen, device=dev))
+                vc.copy_(torch.randn(vc.shape, generator=gen, device=dev))
+                caches.append((kc, vc))
+            state_bytes = sum(kc.numel() * 2 * 2 for kc, _ in caches)
+            ws = torch.empty(max(swa.layer_workspace_bytes(B, dm, Hq, Hkv, d, f, w, s) for w, s in layer_cfg),
+                             dtype=torch.uint8, device=dev)
+            xin = torch.stack([inputs.residual(seed, i, B, dm) for i in range(T)]).to(dev)
+            x = torch.empty(B, dm, dtype=torch.float32, device=dev)
+            dpos = [torch.full((B,), P + i, dtype=torch.int64, device=dev) for i in range(T)]
+
+            def tokens():
+                for i in range(T):
+                    x.copy_(xin[i])
+                    for li, (w, s) in enumerate(layer_cfg):
+                        swa.layer_decode_step(x, weights[li], caches[li][0], caches[li][1], dpos[i], Hq, w, s, scale,
+                                              0, eps, workspace=ws)
+
+            stream = torch.cuda.Stream(device=dev)
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                tokens()
+            stream.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                tokens()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_tok = e0.elapsed_time(e1) / (reps * T)
+            assert torch.isfinite(x).all(), "non-finite residual stream"
+            rec["points"].append({"attention": name, "context": P, "ms_per_token": round(ms_tok, 4),
+                                  "tokens_per_s": round(1e3 / ms_tok, 1), "kv_state_mb": round(state_bytes / 2 ** 20, 3),
+                                  "weight_gb_per_s": round(weight_bytes / (ms_tok * 1e-3) / 1e9, 1)})
+            print(json.dumps(rec["points"][-1]), file=sys.stderr, flush=True)
+            del graph, caches, ws
+            torch.cuda.empty_cache()
+    print(json.dumps(rec), flush=True)
+
+
 def decode_only(args, dev):
     """--decode-only B: time the decode graph at batch B and print one JSON line."""
     import sliding_window_attention_02_amd as swa
@@ -404,6 +515,9 @@ def main():
         return
     if args.chunked:
         chunked_only(args, dev)
+        return
+    if args.model_sweep:
+        model_sweep(args, dev)
         return
     if args.compare_full:
         compare_full(args, dev)
