@@ -414,6 +414,33 @@ def model_sweep(args, dev):
     rec["linear_gate_up"] = {"us_per_launch": round(us, 2), "gb_per_s": round(gu_bytes / (us * 1e-6) / 1e9, 1),
                              "frac_of_hbm_peak": round(gu_bytes / (us * 1e-6) / 8e12, 4)}
 
+    # The fp64 layer oracle on the host, as it stands, for the same SWA(64,4) step: one layer
+    # (its weights converted once, outside the timing) over a history of 68 positions, timed
+    # for a few tokens and scaled to the stack.
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        from oracle import layer as olayer
+        wcpu = inputs.layer_weights(seed, 0, dm, Hq, Hkv, d, f)
+        ow = olayer.LayerWeights(*[wcpu[k].double().numpy() for k in
+                                   ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")])
+        hist = [olayer.History()]
+        kvg = torch.Generator().manual_seed(seed)
+        for pcpu in list(range(4)) + list(range(1000 - 64, 1000)):
+            hist[0].add(pcpu, torch.randn(Hkv, d, generator=kvg).double().numpy(),
+                        torch.randn(Hkv, d, generator=kvg).double().numpy())
+        xo = inputs.residual(seed, 0, B, dm).double().numpy()
+        n_tok, t0 = 0, time.perf_counter()
+        while n_tok < 3 or time.perf_counter() - t0 < 5.0:
+            xo = olayer.layer_step(xo, ow, hist, [1000 + n_tok], Hq, Hkv, d, 64, 4, scale, 0, eps)
+            n_tok += 1
+        sec_layer = (time.perf_counter() - t0) / n_tok
+        rec["cpu_baseline"] = {"value": round(1.0 / (sec_layer * nl), 3), "unit": "tokens/s", "kind": "oracle",
+                               "cores": len(os.sched_getaffinity(0)),
+                               "sample": f"{n_tok} single-layer fp64 oracle steps (numpy matmuls, SWA(64,4) over 68 "
+                                         f"cached positions), scaled to {nl} layers"}
+        del ow, wcpu
+
     variants = [("swa64_4", [(64, 4)] * nl), ("swa128_4", [(128, 4)] * nl), ("swa256_4", [(256, 4)] * nl),
                 ("swa512_4", [(512, 4)] * nl), ("full", None), ("hybrid_swa64_4_last_full", "hybrid")]
     contexts = [int(c) for c in args.model_contexts.split(",")]
@@ -653,6 +680,22 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved_gbs / acc.PEAK_HBM_GBS, 5),
             "traffic": traffic,
+        },
+        # The decode kernel takes most of the step's GPU time (256 one-token launches against one
+        # prefill), so its roofline is reported beside the prefill's: KV bytes per step over the
+        # per-step time of the graph (launch gap included).
+        "roofline_decode": {
+            "kernel": "decode_kernel<128, 3> (fused append + attend)",
+            "bound": "hbm",
+            "batch": DB,
+            "achieved": round(dec_gbs, 2),
+            "peak": acc.PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
+            "note": "the batch-64 working set stays in the Infinity Cache and the step is latency-bound; "
+                    "at batch 1024 (other_batches) the same kernel streams its KV bytes from HBM",
+            "batch_1024": next(({"achieved": pt["kv_gb_per_s"], "frac": pt["frac_of_hbm_peak"]}
+                                for pt in points if pt.get("B") == 1024 and "cache_sets" not in pt), None),
         },
         "cpu_baseline": base,
     }
