@@ -87,14 +87,14 @@ def oracle_weights(w):
                            g_mlp=f64(w["mlp_norm"]), w_gate_up=f64(w["w_gate_up"]), w_down=f64(w["w_down"]))
 
 
-def run_stack(layers, B, dm, Hq, Hkv, d, f, steps, seed, positions=None, prefill=None):
+def run_stack(layers, B, dm, Hq, Hkv, d, f, steps, seed, positions=None, prefill=None, conv=0):
     """Run `steps` decode steps of a stack of layers [(weights, w, s)] on the GPU and, layer by
     layer on the GPU's inputs, in the oracle; returns the worst max-abs difference.
 
     positions: [steps] positions (default 0..steps-1).  prefill: per layer, a list of
     (position, k [B][Hkv][d], v) already in the cache before the first step.
     """
-    eps, conv = 1e-5, 0
+    eps = 1e-5
     scale = 1.0 / np.sqrt(d)
     positions = list(range(steps)) if positions is None else positions
     gw, ow, caches, hists, workspaces = [], [], [], [], []
@@ -132,14 +132,15 @@ def run_stack(layers, B, dm, Hq, Hkv, d, f, steps, seed, positions=None, prefill
     return worst
 
 
-@pytest.mark.parametrize("w,s", [(8, 2), (5, 0), (300, 0)])
-def test_layer_step_small_dims_through_wrap(w, s):
+@pytest.mark.parametrize("w,s,conv", [(8, 2, 0), (5, 0, 0), (300, 0, 0), (12, 4, 1)])
+def test_layer_step_small_dims_through_wrap(w, s, conv):
     """B=2, dm=256, Hq=4, Hkv=2, d=64, f=384; 20 steps from an empty (NaN-filled) cache: sink
-    fill, ring fill and wrap-around (w=300: the window covers every step)."""
+    fill, ring fill and wrap-around (w=300: the window covers every step; conv=1: the
+    total-window convention, 8 ring slots)."""
     B, dm, Hq, Hkv, d, f = 2, 256, 4, 2, 64, 384
-    say("layer small", w, s)
+    say("layer small", w, s, conv)
     layer = (inputs.layer_weights(21, 0, dm, Hq, Hkv, d, f), w, s)
-    worst = run_stack([layer], B, dm, Hq, Hkv, d, f, steps=20, seed=21)
+    worst = run_stack([layer], B, dm, Hq, Hkv, d, f, steps=20, seed=21, conv=conv)
     say(f"max {worst:.3e}")
     assert worst <= TOL
 
