@@ -55,7 +55,20 @@ __device__ __forceinline__ float wave_sum(float x)
 // ----------------------------------------------------------------------------- RMSNorm
 //
 // out[b][i] = bf16( x[b][i] / sqrt(mean_i x[b][i]^2 + eps) * g[i] ); one workgroup per row.
+// Rows of at most kNormThreads * 4 * kNormHeld elements stay in registers between the sum of
+// squares and the scaling (one memory round trip); longer rows are read twice.
 constexpr int kNormThreads = 256;
+constexpr int kNormHeld = 4;  // float4 pieces per thread held in registers
+
+__device__ __forceinline__ void norm_store(uint16_t *orow, int i, f32x4 v, uint2 gg, float inv)
+{
+    const float g0 = __uint_as_float(gg.x << 16), g1 = __uint_as_float(gg.x & 0xffff0000u);
+    const float g2 = __uint_as_float(gg.y << 16), g3 = __uint_as_float(gg.y & 0xffff0000u);
+    uint2 o;
+    o.x = pack_bf16(v.x * inv * g0, v.y * inv * g1);
+    o.y = pack_bf16(v.z * inv * g2, v.w * inv * g3);
+    *reinterpret_cast<uint2 *>(orow + i) = o;
+}
 
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *x, const uint16_t *g, uint16_t *out,
                                                                int n, float eps)
@@ -63,10 +76,26 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *x, c
     const int b = blockIdx.x;
     const float *xr = x + (size_t)b * n;
     uint16_t *orow = out + (size_t)b * n;
+    const bool held = n <= kNormThreads * 4 * kNormHeld;
+    f32x4 v[kNormHeld];
+    uint2 gg[kNormHeld];
     float ss = 0.f;
-    for (int i = threadIdx.x * 4; i < n; i += kNormThreads * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    if (held) {
+#pragma unroll
+        for (int k = 0; k < kNormHeld; ++k) {
+            const int i = (threadIdx.x + k * kNormThreads) * 4;
+            v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (i < n) {
+                v[k] = *reinterpret_cast<const f32x4 *>(xr + i);
+                gg[k] = *reinterpret_cast<const uint2 *>(g + i);
+            }
+            ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+        }
+    } else {
+        for (int i = threadIdx.x * 4; i < n; i += kNormThreads * 4) {
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(xr + i);
+            ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+        }
     }
     __shared__ float part[kNormThreads / 64];
     ss = wave_sum(ss);
@@ -78,15 +107,17 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *x, c
     for (int w = 0; w < kNormThreads / 64; ++w)
         ss += part[w];
     const float inv = 1.f / sqrtf(ss / (float)n + eps);
-    for (int i = threadIdx.x * 4; i < n; i += kNormThreads * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
-        const uint2 gg = *reinterpret_cast<const uint2 *>(g + i);
-        const float g0 = __uint_as_float(gg.x << 16), g1 = __uint_as_float(gg.x & 0xffff0000u);
-        const float g2 = __uint_as_float(gg.y << 16), g3 = __uint_as_float(gg.y & 0xffff0000u);
-        uint2 o;
-        o.x = pack_bf16(v.x * inv * g0, v.y * inv * g1);
-        o.y = pack_bf16(v.z * inv * g2, v.w * inv * g3);
-        *reinterpret_cast<uint2 *>(orow + i) = o;
+    if (held) {
+#pragma unroll
+        for (int k = 0; k < kNormHeld; ++k) {
+            const int i = (threadIdx.x + k * kNormThreads) * 4;
+            if (i < n)
+                norm_store(orow, i, v[k], gg[k], inv);
+        }
+    } else {
+        for (int i = threadIdx.x * 4; i < n; i += kNormThreads * 4)
+            norm_store(orow, i, *reinterpret_cast<const f32x4 *>(xr + i), *reinterpret_cast<const uint2 *>(g + i),
+                       inv);
     }
 }
 
