@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *x, c
 // LDS exchange.  Weights are read once (non-temporal loads: they do not fit in the caches);
 // x is tiny and stays in L2.
 constexpr int kLinThreads = 256;
-constexpr int kLinRows = 4;
+constexpr int kLinRows = 2;
 constexpr int kLinBatch = 4;
 
 struct LinearArgs {
