@@ -9,10 +9,12 @@
 // A step reads (s + w_loc) * d * 2 * 2 bytes per (b, kv-head) and does 4*d flops per key
 // and q-head: with 4 q-heads per kv-head that is 8 flops per byte, more than the fp32 vector
 // units sustain at HBM speed, so the products run on bf16 MFMA (the q-heads of a kv-head
-// are the MFMA columns) and the kernel stays bound by the bytes it reads.  The slot range
-// of a (b, kv-head) is split over workgroups (split-K) only when it exceeds what one
-// workgroup holds (96 slots); partial (max, sum, weighted values) then merge in a separate
-// kernel that visits splits in a fixed order, so results do not depend on scheduling.
+// are the MFMA columns) and the kernel stays bound by the bytes it reads.  Split-K over the
+// slot range of a (b, kv-head): when the grid is small and the range is at most four
+// 32-slot chunks, the waves of one workgroup take one chunk each and merge their partial
+// (max, sum, weighted values) through LDS; when the range exceeds what one wave holds (96
+// slots), the splits are workgroups whose partials merge in a separate kernel.  Both merges
+// visit the splits in a fixed order, so results do not depend on scheduling.
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -36,7 +38,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
 constexpr int kChunk = 32;      // slots per MFMA step
-constexpr int kMaxChunks = 3;   // slots per workgroup <= 96
+constexpr int kMaxChunks = 3;   // slots per wave <= 96
+constexpr int kMaxWaveSplits = 4;  // waves (one chunk each) when a workgroup splits its slots
+// Largest grid (in waves) that splits a workgroup's slots over its waves: beyond it the
+// single-wave workgroups already occupy every SIMD several times over.
+constexpr long long kWaveSplitMaxWaves = 8192;
 
 // Sum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one MFMA column, with
 // the gfx950 cross-row swaps: permlane32_swap(x, x) hands each lane its own value and the
@@ -70,8 +76,9 @@ struct DecodeArgs {
     float scale_log2;
 };
 
-// grid: (n_split, Hkv * n_hslices, B); one wave per workgroup, which owns the slot segment
-// [seg_lo, seg_hi) (at most NCH chunks of 32 slots) of one (b, kv-head, head slice).  The
+// grid: (n_split / WAVES, Hkv * n_hslices, B); WAVES waves per workgroup, wave w owning the
+// slot segment [seg_lo, seg_hi) of split blockIdx.x * WAVES + w (at most NCH chunks of 32
+// slots) of one (b, kv-head, head slice).  The
 // GB <= 16 q-heads of the kv-head are the 16 columns of a bf16 MFMA (unused columns are zero),
 // so the per-key work runs on the matrix cores:
 //     S^T (32 keys x heads) = K (32 keys x d) . Q^T (d x heads)
@@ -86,8 +93,8 @@ struct DecodeArgs {
 // A(t).  Before that, the V rows of empty slots are zeroed in LDS after they land and their
 // scores are masked, so whatever bytes such a slot holds never reach the result.  The fused
 // path takes the new token's K (registers) and V (written over its LDS row) from the input.
-template <int D, int NCH>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
+template <int D, int NCH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 {
     constexpr int kKSteps = D / 32;   // MFMA k-steps for S
     constexpr int kDBlocks = D / 16;  // 16-row blocks of O^T
@@ -95,12 +102,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
     constexpr int kRowBytes = D * 2;
     constexpr int kRowsPerLoad = 1024 / kRowBytes;
     constexpr int kLoads = kChunk / kRowsPerLoad;  // 1 KiB direct loads per chunk of V
-    __shared__ __attribute__((aligned(1024))) unsigned char vlds[NCH][kChunk * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char vlds_all[WAVES][NCH][kChunk * kRowBytes];
+    __shared__ float red_m[WAVES][16], red_l[WAVES][16];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int g16 = lane >> 4;
     const int c16 = lane & 15;
-    const int split = blockIdx.x;
+    // The wave as a uniform value (the direct-to-LDS destinations are scalar).
+    const int wave = WAVES > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    unsigned char(&vlds)[NCH][kChunk * kRowBytes] = vlds_all[wave];
+    const int split = blockIdx.x * WAVES + wave;
     const int hkv = blockIdx.y / a.n_hslices;
     const int hs = blockIdx.y % a.n_hslices;
     const int b = blockIdx.z;
@@ -313,12 +324,49 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a)
         }
     }
 
-    // ---- output (one split) or the partial (m, l, o) of this split.
-    const float ll = sum_over_groups(lsum[0]);  // non-zero in lane group 0 only
+    // ---- output (one split), the partial (m, l, o) of this split, or the fixed-order merge of
+    // the WAVES splits of this workgroup through LDS.
+    float ll = sum_over_groups(lsum[0]);  // non-zero in lane group 0 only
+    if constexpr (WAVES > 1) {
+        if (g16 == 0) {
+            red_m[wave][c16] = m_ref;
+            red_l[wave][c16] = ll;
+        }
+        __syncthreads();  // (also: every wave is done with its V rows, whose LDS now takes O)
+        float mm = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+            mm = fmaxf(mm, red_m[w][c16]);
+        const float mm_use = mm == -INFINITY ? 0.f : mm;
+        float sc[WAVES];
+        ll = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            sc[w] = __builtin_amdgcn_exp2f(red_m[w][c16] - mm_use);  // 0 for a split with no key
+            ll += red_l[w][c16] * sc[w];
+        }
+        // Waves 1.. leave their scaled O^T in their own LDS rows; wave 0 adds them in order.
+        f32x4 *ored = reinterpret_cast<f32x4 *>(&vlds[0][0]);
+        if (wave > 0) {
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db)
+                ored[db * 64 + lane] = o[db] * sc[wave];
+        }
+        __syncthreads();
+        if (wave > 0)
+            return;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+            o[db] *= sc[0];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                o[db] += reinterpret_cast<const f32x4 *>(&vlds_all[w][0][0])[db * 64 + lane];
+        }
+    }
     if (c16 >= GB)
         return;
     const int h = h0 + c16;
-    if (a.n_split == 1) {
+    if (a.n_split == WAVES) {
         const float inv = ll > 0.f ? 1.f / ll : 0.f;
         float *orow = a.out + ((size_t)b * a.Hq + h) * D;
 #pragma unroll
@@ -432,16 +480,22 @@ __global__ void debug_decode_slots_kernel(int64_t *slot_pos, const int64_t *pos,
 }
 
 template <int D>
-void launch_decode_d(const DecodeArgs &a, int B, hipStream_t stream)
+void launch_decode_d(const DecodeArgs &a, int wg_waves, int B, hipStream_t stream)
 {
-    const dim3 grid(a.n_split, a.Hkv * a.n_hslices, B);
+    const dim3 grid(a.n_split / wg_waves, a.Hkv * a.n_hslices, B);
     const int nch = (a.slots_per_split + kChunk - 1) / kChunk;
-    if (nch <= 1)
-        hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(64), 0, stream, a);
+    if (wg_waves == 2)
+        hipLaunchKernelGGL((decode_kernel<D, 1, 2>), grid, dim3(128), 0, stream, a);
+    else if (wg_waves == 3)
+        hipLaunchKernelGGL((decode_kernel<D, 1, 3>), grid, dim3(192), 0, stream, a);
+    else if (wg_waves == 4)
+        hipLaunchKernelGGL((decode_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a);
+    else if (nch <= 1)
+        hipLaunchKernelGGL((decode_kernel<D, 1, 1>), grid, dim3(64), 0, stream, a);
     else if (nch == 2)
-        hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, 2, 1>), grid, dim3(64), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, 3>), grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, 3, 1>), grid, dim3(64), 0, stream, a);
 }
 
 }  // namespace
@@ -458,11 +512,21 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s)
             break;
         }
     p.n_hslices = G / p.Gb;
-    // As few splits as the kernel's register and LDS budget (kMaxChunks * 32 slots per
-    // workgroup) allows: a step costs one memory round trip either way, and a second kernel
+    // Few enough slots for at most four 32-slot chunks, and few enough workgroups that one wave
+    // each would leave SIMDs idle: one workgroup of up to four waves per (b, kv-head, head
+    // slice), one chunk per wave, merged in LDS.  Otherwise one wave per workgroup over as few
+    // splits as its register and LDS budget (kMaxChunks * 32 slots) allows: a second kernel
     // (the merge) costs more than the parallelism it buys, even at batch 1.
-    (void)B;
-    (void)d;
+    const long long groups = (long long)B * Hkv * p.n_hslices;
+    const int chunks = (p.n_slots + kChunk - 1) / kChunk;
+    if (chunks > 1 && chunks <= kMaxWaveSplits && groups * chunks <= kWaveSplitMaxWaves) {
+        p.slots_per_split = kChunk;
+        p.n_split = chunks;
+        p.wg_waves = chunks;
+        p.workspace_bytes = 0;
+        return p;
+    }
+    p.wg_waves = 1;
     const long long want = (p.n_slots + kMaxChunks * kChunk - 1) / (kMaxChunks * kChunk);
     p.slots_per_split = (int)((p.n_slots + want - 1) / want);
     p.n_split = (p.n_slots + p.slots_per_split - 1) / p.slots_per_split;
@@ -516,11 +580,11 @@ hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void
     a.slots_per_split = plan.slots_per_split;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (d == 128)
-        launch_decode_d<128>(a, B, stream);
+        launch_decode_d<128>(a, plan.wg_waves, B, stream);
     else
-        launch_decode_d<64>(a, B, stream);
+        launch_decode_d<64>(a, plan.wg_waves, B, stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.n_split == 1)
+    if (e != hipSuccess || plan.n_split == plan.wg_waves)
         return e;
     if (d == 128)
         hipLaunchKernelGGL(merge_kernel<128>, dim3(Hq, B), dim3(kMergeThreads), 0, stream, a.ws, out, Hq,

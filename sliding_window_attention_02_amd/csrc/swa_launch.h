@@ -44,7 +44,8 @@ struct DecodePlan {
     int n_slots;          // s + w_loc
     int Gb;               // q-heads per workgroup (largest divisor of G that is <= 16)
     int n_hslices;        // G / Gb
-    int n_split;          // workgroups over the slot range of one (b, kv-head, head slice)
+    int n_split;          // splits of the slot range of one (b, kv-head, head slice)
+    int wg_waves;         // splits per workgroup (one wave each): 1, or n_split (merged in LDS)
     int slots_per_split;  // slots per split
     size_t workspace_bytes;
 };
