@@ -10,8 +10,7 @@
 // and q-head: with 4 q-heads per kv-head that is 8 flops per byte, more than the fp32 vector
 // units sustain at HBM speed, so the products run on bf16 MFMA (the q-heads of a kv-head
 // are the MFMA columns) and the kernel stays bound by the bytes it reads.  Split-K over the
-// slot range of a (b, kv-head): when the grid is small and the range is at most four
-// 32-slot chunks, the waves of one workgroup take one chunk each and merge their partial
+// slot range of a (b, kv-head): when the range is at most four 32-slot chunks, the waves of one workgroup take one chunk each and merge their partial
 // (max, sum, weighted values) through LDS; when the range exceeds what one wave holds (96
 // slots), the splits are workgroups whose partials merge in a separate kernel.  Both merges
 // visit the splits in a fixed order, so results do not depend on scheduling.
@@ -40,9 +39,6 @@ __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 constexpr int kChunk = 32;      // slots per MFMA step
 constexpr int kMaxChunks = 3;   // slots per wave <= 96
 constexpr int kMaxWaveSplits = 4;  // waves (one chunk each) when a workgroup splits its slots
-// Largest grid (in waves) that splits a workgroup's slots over its waves: beyond it the
-// single-wave workgroups already occupy every SIMD several times over.
-constexpr long long kWaveSplitMaxWaves = 8192;
 
 // Sum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one MFMA column, with
 // the gfx950 cross-row swaps: permlane32_swap(x, x) hands each lane its own value and the
@@ -512,14 +508,13 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s)
             break;
         }
     p.n_hslices = G / p.Gb;
-    // Few enough slots for at most four 32-slot chunks, and few enough workgroups that one wave
-    // each would leave SIMDs idle: one workgroup of up to four waves per (b, kv-head, head
-    // slice), one chunk per wave, merged in LDS.  Otherwise one wave per workgroup over as few
-    // splits as its register and LDS budget (kMaxChunks * 32 slots) allows: a second kernel
-    // (the merge) costs more than the parallelism it buys, even at batch 1.
-    const long long groups = (long long)B * Hkv * p.n_hslices;
+    // At most four 32-slot chunks: one workgroup of one wave per chunk for each (b, kv-head,
+    // head slice), merged in LDS (faster than one wave over every chunk at each batch size
+    // measured, 1 to 2048).  Otherwise one wave per workgroup over as few splits as its
+    // register and LDS budget (kMaxChunks * 32 slots) allows: a second kernel (the merge)
+    // costs more than the parallelism it buys, even at batch 1.
     const int chunks = (p.n_slots + kChunk - 1) / kChunk;
-    if (chunks > 1 && chunks <= kMaxWaveSplits && groups * chunks <= kWaveSplitMaxWaves) {
+    if (chunks > 1 && chunks <= kMaxWaveSplits) {
         p.slots_per_split = kChunk;
         p.n_split = chunks;
         p.wg_waves = chunks;
