@@ -685,7 +685,7 @@ def main():
         # prefill), so its roofline is reported beside the prefill's: KV bytes per step over the
         # per-step time of the graph (launch gap included).
         "roofline_decode": {
-            "kernel": "decode_kernel<128, 3> (fused append + attend)",
+            "kernel": "decode_kernel<128, 1, 3> (fused append + attend; three waves, one 32-slot chunk each)",
             "bound": "hbm",
             "batch": DB,
             "achieved": round(dec_gbs, 2),
