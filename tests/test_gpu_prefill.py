@@ -79,6 +79,10 @@ PARITY = [
     (1, 1000, 16, 4, 128, 256, 0, 0, 1.0, 4),
     (1, 1100, 8, 2, 128, 512, 4, 0, 1.0, 4),
     (1, 1500, 8, 2, 128, 1000, 4, 0, 1.0, 0),
+    # windows of 1000+ keys at d = 128: long runs of middle tiles, ragged tails, G = 4, 2, 1
+    (1, 2600, 8, 2, 128, 1024, 4, 0, 1.0, 4),
+    (2, 1300, 6, 3, 128, 1100, 0, 1, 1.0, 0),
+    (1, 1200, 2, 2, 128, 2000, 3, 0, 1.0, 4),
     (1, 200, 12, 4, 128, 33, 70, 0, 1.0, 4),
     (1, 333, 16, 2, 64, 50, 5, 1, 1.0, 4),
     (1, 129, 4, 4, 64, 1, 0, 0, 1.0, 0),
