@@ -76,6 +76,28 @@ __device__ __forceinline__ WalkSplit split_walk(const TileWalk &tw, int t0, int 
     return sp;
 }
 
+// The kChunkN-key chunks (kChunkN below) holding a key of A(t) for some t in [t0, t1]: the sink
+// chunks below the window's first chunk, then the window's chunks, in that order.  The chunk
+// walk of the resident prefill, which keeps every chunk of a q-tile in LDS at once.
+struct ChunkWalk {
+    int n_sink;          // chunks 0 .. n_sink-1 (sinks below the window)
+    int win_lo, win_hi;  // window chunks
+    __device__ __forceinline__ int count() const { return n_sink + (win_hi - win_lo + 1); }
+    __device__ __forceinline__ int chunk(int k) const { return k < n_sink ? k : win_lo + (k - n_sink); }
+};
+
+__device__ __forceinline__ ChunkWalk plan_chunks(int t0, int t1, int w_loc, int s, int chunk_n)
+{
+    ChunkWalk cw;
+    const int lo = (t0 - w_loc + 1 > 0) ? t0 - w_loc + 1 : 0;
+    cw.win_lo = lo / chunk_n;
+    cw.win_hi = t1 / chunk_n;
+    const int sink_keys = s < t1 + 1 ? s : t1 + 1;
+    const int sink_chunks = (sink_keys + chunk_n - 1) / chunk_n;
+    cw.n_sink = sink_chunks < cw.win_lo ? sink_chunks : cw.win_lo;
+    return cw;
+}
+
 // A tile is processed in chunks of kChunkN keys.  Sets [c_lo, c_hi], the smallest chunk
 // range that covers every chunk holding a key of A(t) for some t in [t0, t1] (the needed
 // keys of a q-tile are the sinks [0, min(s, t1+1)) and the window [max(0, t0-w_loc+1), t1]);

@@ -19,6 +19,9 @@ struct PrefillGeometry {
     int n_qtiles;   // ceil(L / Tm)
 };
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
+// Whether q-tiles of Tm tokens starting at q_lo need at most four 32-key chunks for any q-tile:
+// then the prefill keeps all of a q-tile's keys in LDS at once (the resident form).
+bool prefill_resident(int Tm, int q_lo, int w_loc, int s);
 
 // Chunked prefill: the first n_cached of the L keys are read from a sink+ring cache
 // [B][Hkv][s + w_loc][d] (key j < ns: sink slot j; key j >= ns: ring slot

@@ -143,7 +143,7 @@ struct TileInfo {
     __device__ __forceinline__ bool full() const { return c_lo == 0 && c_hi == 1 && mask_free; }
 };
 
-template <int D>
+template <int D, bool RES>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     constexpr int kPieces = Lds<D>::kPieces;
@@ -297,275 +297,381 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
-    const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
-    const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
-    auto tile_info = [&](int tile) __attribute__((always_inline)) {
-        TileInfo ti;
-        ti.j0 = tile * kTileN;
-        tile_chunks(ti.j0, 2, t0, t1, a.w_loc, a.s, ti.c_lo, ti.c_hi);
-        ti.mask_free = range_mask_free(ti.j0 + ti.c_lo * kChunkN, ti.j0 + ti.c_hi * kChunkN + kChunkN - 1, t0, t1,
-                                       a.w_loc, a.s);
-        return ti;
-    };
-
-    // The steps below take `fast` as a compile-time flag: a fast tile has both chunks needed and
-    // no element mask, so its code is straight-line; otherwise chunks outside [c_lo, c_hi] are
-    // skipped (loads aside: a tile is always loaded whole) and the mask is applied.
-
-    // S^T = K Q^T of one tile, K from LDS.  Row m of 16-key block (kc, h) holds key
-    // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
-    // (Skipped chunks are set to zero all the same: every element of sacc is then written by
-    // each call, so the compiler does not keep the previous tile's scores alive.)
-    auto scores = [&](f32x4(&sacc)[2][2][2], const unsigned char *kt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
-        constexpr bool fast = decltype(fast_c)::value;
+    if constexpr (RES) {
+        // Resident form (windows whose q-tile needs at most four 32-key chunks): every chunk of
+        // the q-tile is loaded at once, chunk k into rows 32 (k & 1) .. of buffer k >> 1 (waves
+        // 2 (k & 1) and 2 (k & 1) + 1 load it), then one barrier, after which the workgroup
+        // issues no more loads.  The wave's two 16-column blocks are then done one after the
+        // other, each over all chunks and stored at once: the first block's stores drain while
+        // the second computes (a later wait for a load would also wait for those stores, since
+        // loads and stores share one in-order counter).
+        const ChunkWalk cw = plan_chunks(t0, t1, a.w_loc, a.s, kChunkN);
+        // Four chunk slots are always loaded and computed (straight-line code): a slot past the
+        // q-tile's chunks holds keys after t1 (rows past the sequence read its last row), which
+        // the element mask removes by causality.
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                continue;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int kk = 0; kk < kKSteps; ++kk) {
-                    const bf16x8 af =
-                        *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + (kc * kChunkN + 4 * h) * kRowBytes);
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        sacc[kc][h][qb] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sacc[kc][h][qb], 0, 0, 0);
-                }
+        for (int k = 0; k < 4; ++k) {
+            if ((wave_u >> 1) == (k & 1)) {
+                const int j0 = cw.chunk(k) * kChunkN - (k & 1) * kChunkN;  // tile row 0 holds key j0
+                issue(j0, k >> 1, KRows());
+                issue(j0, k >> 1, VRows());
             }
         }
-    };
-
-    // Element mask of one tile (when some visited pair is outside A(t)), its column maxima, and
-    // the lazy move of the reference maximum: m_ref only moves (and O and the sums are rescaled
-    // by alpha) when the column maximum exceeds it by more than 8 in log2 units, so the
-    // probabilities stay below 256 and most tiles need no rescale.  Returns whether any column
-    // of this lane moved.
-    auto tile_max = [&](f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, float(&alpha)[2]) __attribute__((always_inline)) {
-        constexpr bool fast = decltype(fast_c)::value;
-        if (!fast && !ti.mask_free) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        // With every key of the q-tile at hand the softmax needs no running maximum: all scores,
+        // the exact column maximum, the probabilities, then O^T = V^T P^T.
+        auto pass = [&](auto qb_c) __attribute__((always_inline)) {
+            constexpr int qb = decltype(qb_c)::value;
+            const int t = tok[qb];
+            f32x4 sr[4][2];
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                if (kc < ti.c_lo || kc > ti.c_hi)
-                    continue;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int key = ti.j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
-                            const int t = tok[qb];
-                            const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
-                            sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
-                        }
-            }
-        }
-        bool grow_any = false;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            // (pairs folded into the running maximum: three-input maxima)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                    continue;
+            for (int k = 0; k < 4; ++k) {
+                const unsigned char *kt = &lds[k >> 1][0][0] + (k & 1) * kChunkN * kRowBytes;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][0]), sacc[kc][h][qb][1]);
-                    mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][2]), sacc[kc][h][qb][3]);
+                    sr[k][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < kKSteps; ++kk) {
+                        const bf16x8 af = *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + 4 * h * kRowBytes);
+                        sr[k][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sr[k][h], 0, 0, 0);
+                    }
                 }
             }
-            mx = max_over_groups(mx);
-            const float m_tile = mx * c;
-            const bool grow = m_tile > m_ref[qb] + 8.f;
-            // (a column with no allowed key so far keeps m_ref = -inf and alpha = 1)
-            alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile) : 1.f;
-            m_ref[qb] = grow ? m_tile : m_ref[qb];
-            grow_any |= grow;
-        }
-        return grow_any;
-    };
-
-    // Probabilities of one tile against the reference maximum, as P^T B-operand fragments.
-    auto probs = [&](const f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, bf16x8(&pf)[2][2]) __attribute__((always_inline)) {
-        constexpr bool fast = decltype(fast_c)::value;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+            for (int k = 0; k < 4; ++k) {
+                const int key0 = cw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                    continue;
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = key0 + 4 * h + j;
+                        const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
+                        sr[k][h][j] = ok ? sr[k][h][j] : -INFINITY;
+                    }
+                    mx = fmaxf(fmaxf(mx, sr[k][h][0]), sr[k][h][1]);
+                    mx = fmaxf(fmaxf(mx, sr[k][h][2]), sr[k][h][3]);
+                }
+            }
+            const float mm = max_over_groups(mx) * c;
+            const float m_use = mm == -INFINITY ? 0.f : mm;
+            // Probabilities, their column sums (the ones-row MFMA), then O^T one 16-row block at a
+            // time, each stored as soon as it is complete, so the stores spread over the compute.
+            bf16x8 pf[4];
+            f32x4 lq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        pf[kc][qb][4 * h + j] =
-                            static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc][h][qb][j], c, -m_use)));
+                        pf[k][4 * h + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sr[k][h][j], c, -m_use)));
+                lq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[k], lq, 0, 0, 0);
             }
-        }
-    };
-
-    // O^T += V^T P^T over the tile's needed chunks, V from LDS, and the probability sums.
-    auto accumulate = [&](const bf16x8(&pf)[2][2], const unsigned char *vt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
-        constexpr bool fast = decltype(fast_c)::value;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                continue;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-                lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[kc][qb], lsum[qb], 0, 0, 0);
+            float l = lq[0];  // non-zero in lane group 0 only
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const float inv = 1.f / l;
+            float *orow = a.out + (((size_t)bc.b * a.Lq + (valid[qb] ? tok[qb] - a.q_lo : 0)) * a.Hq +
+                                   (valid[qb] ? head[qb] : 0)) * D;
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
-                bf16x8 af;
+                f32x4 od = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
-                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vt + off));
-                    const bf16x4 y = __builtin_bit_cast(bf16x4, x);
-                    af[4 * h + 0] = y[0];
-                    af[4 * h + 1] = y[1];
-                    af[4 * h + 2] = y[2];
-                    af[4 * h + 3] = y[3];
+                for (int k = 0; k < 4; ++k) {
+                    const unsigned char *vt = &lds[k >> 1][1][0] + (k & 1) * kChunkN * kRowBytes;
+                    bf16x8 af;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int off = v_lane[db & 3] + 4 * h * kRowBytes + 32 * (db & ~3);
+                        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(vt + off));
+                        const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+                        af[4 * h + 0] = y[0];
+                        af[4 * h + 1] = y[1];
+                        af[4 * h + 2] = y[2];
+                        af[4 * h + 3] = y[3];
+                    }
+                    od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[k], od, 0, 0, 0);
                 }
-#pragma unroll
+                if (valid[qb])
+                    *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = od * inv;
+            }
+        };
+        pass(std::integral_constant<int, 0>());
+        pass(std::integral_constant<int, 1>());
+    } else {
+        const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
+        const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
+        auto tile_info = [&](int tile) __attribute__((always_inline)) {
+            TileInfo ti;
+            ti.j0 = tile * kTileN;
+            tile_chunks(ti.j0, 2, t0, t1, a.w_loc, a.s, ti.c_lo, ti.c_hi);
+            ti.mask_free = range_mask_free(ti.j0 + ti.c_lo * kChunkN, ti.j0 + ti.c_hi * kChunkN + kChunkN - 1, t0, t1,
+                                           a.w_loc, a.s);
+            return ti;
+        };
+
+        // The steps below take `fast` as a compile-time flag: a fast tile has both chunks needed and
+        // no element mask, so its code is straight-line; otherwise chunks outside [c_lo, c_hi] are
+        // skipped (loads aside: a tile is always loaded whole) and the mask is applied.
+
+        // S^T = K Q^T of one tile, K from LDS.  Row m of 16-key block (kc, h) holds key
+        // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
+        // (Skipped chunks are set to zero all the same: every element of sacc is then written by
+        // each call, so the compiler does not keep the previous tile's scores alive.)
+        auto scores = [&](f32x4(&sacc)[2][2][2], const unsigned char *kt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
+            constexpr bool fast = decltype(fast_c)::value;
+    #pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+    #pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
+                    continue;
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+    #pragma unroll
+                    for (int kk = 0; kk < kKSteps; ++kk) {
+                        const bf16x8 af =
+                            *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + (kc * kChunkN + 4 * h) * kRowBytes);
+    #pragma unroll
+                        for (int qb = 0; qb < 2; ++qb)
+                            sacc[kc][h][qb] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sacc[kc][h][qb], 0, 0, 0);
+                    }
+                }
+            }
+        };
+
+        // Element mask of one tile (when some visited pair is outside A(t)), its column maxima, and
+        // the lazy move of the reference maximum: m_ref only moves (and O and the sums are rescaled
+        // by alpha) when the column maximum exceeds it by more than 8 in log2 units, so the
+        // probabilities stay below 256 and most tiles need no rescale.  Returns whether any column
+        // of this lane moved.
+        auto tile_max = [&](f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, float(&alpha)[2]) __attribute__((always_inline)) {
+            constexpr bool fast = decltype(fast_c)::value;
+            if (!fast && !ti.mask_free) {
+    #pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    if (kc < ti.c_lo || kc > ti.c_hi)
+                        continue;
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                        for (int qb = 0; qb < 2; ++qb)
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int key = ti.j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
+                                const int t = tok[qb];
+                                const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
+                                sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
+                            }
+                }
+            }
+            bool grow_any = false;
+    #pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                // (pairs folded into the running maximum: three-input maxima)
+                float mx = -INFINITY;
+    #pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
+                        continue;
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][0]), sacc[kc][h][qb][1]);
+                        mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][2]), sacc[kc][h][qb][3]);
+                    }
+                }
+                mx = max_over_groups(mx);
+                const float m_tile = mx * c;
+                const bool grow = m_tile > m_ref[qb] + 8.f;
+                // (a column with no allowed key so far keeps m_ref = -inf and alpha = 1)
+                alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile) : 1.f;
+                m_ref[qb] = grow ? m_tile : m_ref[qb];
+                grow_any |= grow;
+            }
+            return grow_any;
+        };
+
+        // Probabilities of one tile against the reference maximum, as P^T B-operand fragments.
+        auto probs = [&](const f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, bf16x8(&pf)[2][2]) __attribute__((always_inline)) {
+            constexpr bool fast = decltype(fast_c)::value;
+    #pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+    #pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
+                        continue;
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            pf[kc][qb][4 * h + j] =
+                                static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc][h][qb][j], c, -m_use)));
+                }
+            }
+        };
+
+        // O^T += V^T P^T over the tile's needed chunks, V from LDS, and the probability sums.
+        auto accumulate = [&](const bf16x8(&pf)[2][2], const unsigned char *vt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
+            constexpr bool fast = decltype(fast_c)::value;
+    #pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
+                    continue;
+    #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
-                    o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[kc][qb], o[db][qb], 0, 0, 0);
+                    lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[kc][qb], lsum[qb], 0, 0, 0);
+    #pragma unroll
+                for (int db = 0; db < kDBlocks; ++db) {
+                    bf16x8 af;
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
+                        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(vt + off));
+                        const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+                        af[4 * h + 0] = y[0];
+                        af[4 * h + 1] = y[1];
+                        af[4 * h + 2] = y[2];
+                        af[4 * h + 3] = y[3];
+                    }
+    #pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[kc][qb], o[db][qb], 0, 0, 0);
+                }
             }
-        }
-    };
+        };
 
-    auto rescale = [&](const float(&alpha)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int db = 0; db < kDBlocks; ++db) {
-            o[db][0] *= alpha[0];
-            o[db][1] *= alpha[1];
-        }
-        lsum[0] *= alpha[0];
-        lsum[1] *= alpha[1];
-    };
-
-    // The online softmax takes the tiles in any order: the edge tiles first, one per step,
-    // then the middle tiles through a software pipeline.
-    f32x4 sacc[2][2][2][2];  // [tile parity][kc][h][qb]
-    float alpha[2];
-    using Generic = std::integral_constant<bool, false>;
-    using Fast = std::integral_constant<bool, true>;
-    using Even = std::integral_constant<int, 0>;
-    using Odd = std::integral_constant<int, 1>;
-
-    // Edge tiles: step i computes tile i while K and V of tile i+1 load into the other buffer.
-    if (sp.n_edge > 0) {
-        TileInfo cur = tile_info(sp.edge_tile(tw, 0));
-        issue(cur.j0, 0, KRows());
-        issue(cur.j0, 0, VRows());
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __syncthreads();
-        auto edge_step = [&](const int i, auto buf_c) __attribute__((always_inline)) {
-            constexpr int buf = decltype(buf_c)::value;  // i & 1
-            TileInfo nxt = cur;
-            if (i + 1 < sp.n_edge) {
-                nxt = tile_info(sp.edge_tile(tw, i + 1));
-                issue(nxt.j0, buf ^ 1, KRows());
-                issue(nxt.j0, buf ^ 1, VRows());
+        auto rescale = [&](const float(&alpha)[2]) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                o[db][0] *= alpha[0];
+                o[db][1] *= alpha[1];
             }
-            scores(sacc[0], lds[buf][0], cur, Generic());
-            if (__any(tile_max(sacc[0], cur, Generic(), alpha)))
-                rescale(alpha);
-            bf16x8 pf[2][2];
-            probs(sacc[0], cur, Generic(), pf);
-            accumulate(pf, lds[buf][1], cur, Generic());
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
-            __syncthreads();
-            cur = nxt;
+            lsum[0] *= alpha[0];
+            lsum[1] *= alpha[1];
         };
-        for (int i = 0; i < sp.n_edge; i += 2) {
-            edge_step(i, Even());
-            if (i + 1 < sp.n_edge)
-                edge_step(i + 1, Odd());
-        }
-    }
 
-    // Middle tiles m = 0 .. nm-1 (keys jm + 64m ..): full and mask-free.  Step m computes, with
-    // no dependence between the two halves,
-    //     matrix cores: S of tile m+1, then O += V^T P^T of tile m
-    //     vector ALUs:  probabilities of tile m, then the maxima of tile m+1
-    // so the exponentials of one tile run while the matrix cores work on the next.  K runs one
-    // tile ahead of V: step m reads K of tile m+1 and V of tile m (LDS buffers (m+1)&1 and m&1)
-    // while K of tile m+2 and V of tile m+1 load into the other two; one barrier per step.  The
-    // rescale for tile m+1 (rare) closes step m, after O has taken tile m.
-    const int nm = sp.n_mid();
-    if (nm > 0) {
-        const int jm = sp.mid_lo * kTileN;
-        const TileInfo full = {0, 0, 1, 1};  // (the fast steps read none of it)
-        issue(jm, 0, KRows());
-        issue(jm, 0, VRows());
-        if (nm > 1)
-            issue(jm + kTileN, 1, KRows());
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __syncthreads();
-        scores(sacc[0], lds[0][0], full, Fast());
-        if (__any(tile_max(sacc[0], full, Fast(), alpha)))
-            rescale(alpha);
+        // The online softmax takes the tiles in any order: the edge tiles first, one per step,
+        // then the middle tiles through a software pipeline.
+        f32x4 sacc[2][2][2][2];  // [tile parity][kc][h][qb]
+        float alpha[2];
+        using Generic = std::integral_constant<bool, false>;
+        using Fast = std::integral_constant<bool, true>;
+        using Even = std::integral_constant<int, 0>;
+        using Odd = std::integral_constant<int, 1>;
 
-        auto mid_step = [&](const int m, auto buf_c) __attribute__((always_inline)) {  // m + 1 < nm
-            constexpr int buf = decltype(buf_c)::value;  // m & 1
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's loads of the last step landed
-            __syncthreads();                            // ... and every wave's; K buffer buf, V buffer buf^1 free
-            if (m + 2 < nm)
-                issue(jm + (m + 2) * kTileN, buf, KRows());
-            issue(jm + (m + 1) * kTileN, buf ^ 1, VRows());
-            scores(sacc[buf ^ 1], lds[buf ^ 1][0], full, Fast());
-            bf16x8 pf[2][2];
-            probs(sacc[buf], full, Fast(), pf);
-            accumulate(pf, lds[buf][1], full, Fast());
-            const bool grow = tile_max(sacc[buf ^ 1], full, Fast(), alpha);
-            if (__any(grow))
-                rescale(alpha);
-        };
-        // The last middle tile: its probabilities and O += V^T P^T.
-        auto mid_last = [&](auto buf_c) __attribute__((always_inline)) {
-            constexpr int buf = decltype(buf_c)::value;
+        // Edge tiles: step i computes tile i while K and V of tile i+1 load into the other buffer.
+        if (sp.n_edge > 0) {
+            TileInfo cur = tile_info(sp.edge_tile(tw, 0));
+            issue(cur.j0, 0, KRows());
+            issue(cur.j0, 0, VRows());
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();
-            bf16x8 pf[2][2];
-            probs(sacc[buf], full, Fast(), pf);
-            accumulate(pf, lds[buf][1], full, Fast());
-        };
-        int m = 0;
-        for (; m + 2 < nm; m += 2) {
-            mid_step(m, Even());
-            mid_step(m + 1, Odd());
+            auto edge_step = [&](const int i, auto buf_c) __attribute__((always_inline)) {
+                constexpr int buf = decltype(buf_c)::value;  // i & 1
+                TileInfo nxt = cur;
+                if (i + 1 < sp.n_edge) {
+                    nxt = tile_info(sp.edge_tile(tw, i + 1));
+                    issue(nxt.j0, buf ^ 1, KRows());
+                    issue(nxt.j0, buf ^ 1, VRows());
+                }
+                scores(sacc[0], lds[buf][0], cur, Generic());
+                if (__any(tile_max(sacc[0], cur, Generic(), alpha)))
+                    rescale(alpha);
+                bf16x8 pf[2][2];
+                probs(sacc[0], cur, Generic(), pf);
+                accumulate(pf, lds[buf][1], cur, Generic());
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
+                __syncthreads();
+                cur = nxt;
+            };
+            for (int i = 0; i < sp.n_edge; i += 2) {
+                edge_step(i, Even());
+                if (i + 1 < sp.n_edge)
+                    edge_step(i + 1, Odd());
+            }
         }
-        if (m + 1 < nm) {
-            mid_step(m, Even());
-            mid_last(Odd());
-        } else {
-            mid_last(Even());
-        }
-    }
 
-    // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float l = lsum[qb][0];  // non-zero in lane group 0 only
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const float inv = 1.f / l;
-        if (valid[qb]) {
-            float *orow = a.out + (((size_t)bc.b * a.Lq + tok[qb] - a.q_lo) * a.Hq + head[qb]) * D;
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db)
-                // Plain stores: L2 merges the 64-byte pieces of a row into whole lines
-                // (non-temporal stores here cost 1.5x the output bytes in HBM writes).
-                *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db][qb] * inv;
+        // Middle tiles m = 0 .. nm-1 (keys jm + 64m ..): full and mask-free.  Step m computes, with
+        // no dependence between the two halves,
+        //     matrix cores: S of tile m+1, then O += V^T P^T of tile m
+        //     vector ALUs:  probabilities of tile m, then the maxima of tile m+1
+        // so the exponentials of one tile run while the matrix cores work on the next.  K runs one
+        // tile ahead of V: step m reads K of tile m+1 and V of tile m (LDS buffers (m+1)&1 and m&1)
+        // while K of tile m+2 and V of tile m+1 load into the other two; one barrier per step.  The
+        // rescale for tile m+1 (rare) closes step m, after O has taken tile m.
+        const int nm = sp.n_mid();
+        if (nm > 0) {
+            const int jm = sp.mid_lo * kTileN;
+            const TileInfo full = {0, 0, 1, 1};  // (the fast steps read none of it)
+            issue(jm, 0, KRows());
+            issue(jm, 0, VRows());
+            if (nm > 1)
+                issue(jm + kTileN, 1, KRows());
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __syncthreads();
+            scores(sacc[0], lds[0][0], full, Fast());
+            if (__any(tile_max(sacc[0], full, Fast(), alpha)))
+                rescale(alpha);
+
+            auto mid_step = [&](const int m, auto buf_c) __attribute__((always_inline)) {  // m + 1 < nm
+                constexpr int buf = decltype(buf_c)::value;  // m & 1
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's loads of the last step landed
+                __syncthreads();                            // ... and every wave's; K buffer buf, V buffer buf^1 free
+                if (m + 2 < nm)
+                    issue(jm + (m + 2) * kTileN, buf, KRows());
+                issue(jm + (m + 1) * kTileN, buf ^ 1, VRows());
+                scores(sacc[buf ^ 1], lds[buf ^ 1][0], full, Fast());
+                bf16x8 pf[2][2];
+                probs(sacc[buf], full, Fast(), pf);
+                accumulate(pf, lds[buf][1], full, Fast());
+                const bool grow = tile_max(sacc[buf ^ 1], full, Fast(), alpha);
+                if (__any(grow))
+                    rescale(alpha);
+            };
+            // The last middle tile: its probabilities and O += V^T P^T.
+            auto mid_last = [&](auto buf_c) __attribute__((always_inline)) {
+                constexpr int buf = decltype(buf_c)::value;
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                __syncthreads();
+                bf16x8 pf[2][2];
+                probs(sacc[buf], full, Fast(), pf);
+                accumulate(pf, lds[buf][1], full, Fast());
+            };
+            int m = 0;
+            for (; m + 2 < nm; m += 2) {
+                mid_step(m, Even());
+                mid_step(m + 1, Odd());
+            }
+            if (m + 1 < nm) {
+                mid_step(m, Even());
+                mid_last(Odd());
+            } else {
+                mid_last(Even());
+            }
+        }
+
+        // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
+    #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float l = lsum[qb][0];  // non-zero in lane group 0 only
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const float inv = 1.f / l;
+            if (valid[qb]) {
+                float *orow = a.out + (((size_t)bc.b * a.Lq + tok[qb] - a.q_lo) * a.Hq + head[qb]) * D;
+    #pragma unroll
+                for (int db = 0; db < kDBlocks; ++db)
+                    // Plain stores: L2 merges the 64-byte pieces of a row into whole lines
+                    // (non-temporal stores here cost 1.5x the output bytes in HBM writes).
+                    *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db][qb] * inv;
+            }
         }
     }
 }
@@ -574,10 +680,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 // split: edge tiles through the chunk selection, mask-free classification and element
 // predicate; middle tiles whole and unmasked, as the kernel takes them.  One workgroup per
 // q-tile.
-__global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int w_loc, int s)
+__global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int resident, int w_loc, int s)
 {
     const int t0 = blockIdx.x * Tm;
     const int t1 = min(t0 + Tm - 1, L - 1);
+    if (resident) {  // the resident form's chunk walk, every chunk element-masked
+        const ChunkWalk cw = plan_chunks(t0, t1, w_loc, s, kChunkN);
+        for (int k = 0; k < cw.count(); ++k) {
+            const int k_lo = cw.chunk(k) * kChunkN;
+            for (int idx = threadIdx.x; idx < Tm * kChunkN; idx += blockDim.x) {
+                const int t = t0 + idx / kChunkN;
+                const int key = k_lo + idx % kChunkN;
+                if (t <= t1 && key < L && key_allowed(t, key, w_loc, s))
+                    mask[(size_t)t * L + key] = 1;
+            }
+        }
+        return;
+    }
     const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
     const WalkSplit sp = split_walk(tw, t0, t1, w_loc, kTileN);
     for (int n = 0; n < tw.count(); ++n) {
@@ -607,6 +726,16 @@ __global__ void fill_zero_kernel(uint8_t *p, size_t n)
 }
 
 }  // namespace
+
+bool prefill_resident(int Tm, int q_lo, int w_loc, int s)
+{
+    // With q-tiles starting on 32-key boundaries a q-tile needs at most Tm/32 + ceil((w_loc-1)/32)
+    // window chunks and ceil(s/32) sink chunks.
+    if (Tm % kChunkN != 0 || q_lo % kChunkN != 0)
+        return false;
+    const long long n = Tm / kChunkN + ((long long)w_loc - 1 + kChunkN - 1) / kChunkN + ((long long)s + kChunkN - 1) / kChunkN;
+    return n <= 4;
+}
 
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
 {
@@ -661,7 +790,9 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    void (*kern)(PrefillArgs) = d == 128 ? prefill_kernel<128> : prefill_kernel<64>;
+    const bool res = prefill_resident(g.Tm, q_lo, w_loc, s);
+    void (*kern)(PrefillArgs) = d == 128 ? (res ? prefill_kernel<128, true> : prefill_kernel<128, false>)
+                                         : (res ? prefill_kernel<64, true> : prefill_kernel<64, false>);
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
     else
@@ -679,7 +810,8 @@ hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(256), 0, stream, mask, L, g.Tm, w_loc, s);
+    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(256), 0, stream, mask, L, g.Tm,
+                       prefill_resident(g.Tm, 0, w_loc, s) ? 1 : 0, w_loc, s);
     return hipGetLastError();
 }
 
