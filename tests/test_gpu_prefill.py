@@ -79,6 +79,12 @@ PARITY = [
     (1, 1000, 16, 4, 128, 256, 0, 0, 1.0, 4),
     (1, 1100, 8, 2, 128, 512, 4, 0, 1.0, 4),
     (1, 1500, 8, 2, 128, 1000, 4, 0, 1.0, 0),
+    # the resident form (every q-tile within four 32-key chunks): two sink chunks, a full sink
+    # chunk, the total-window convention at d = 64, w = 1 with one head per kv-head
+    (1, 97, 8, 2, 128, 33, 64, 0, 1.0, 4),
+    (2, 257, 4, 1, 128, 64, 32, 0, 1.0, 4),
+    (1, 200, 16, 4, 64, 64, 4, 1, 1.0, 4),
+    (1, 130, 2, 2, 128, 1, 0, 0, 1.0, 0),
     # windows of 1000+ keys at d = 128: long runs of middle tiles, ragged tails, G = 4, 2, 1
     (1, 2600, 8, 2, 128, 1024, 4, 0, 1.0, 4),
     (2, 1300, 6, 3, 128, 1100, 0, 1, 1.0, 0),
