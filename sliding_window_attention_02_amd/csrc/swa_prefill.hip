@@ -114,6 +114,36 @@ constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // pass drop the kernel's launch stub.
 #define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
+// Output stores in whole 128-byte lines.  Lane (g, c) holds column c of a 16-column block of
+// O^T at d = 16 db + 4 g .. +3, so one plain store would write 64 bytes of each of 16 rows.  For
+// a pair of d-blocks (2m, 2m+1), instruction A writes columns 0-7 and B columns 8-15, each lane
+// 16 bytes at d = 32 m + 16 (c / 8) + 4 g, so 8 lanes fill one 128-byte line of a row: lanes
+// c >= 8 take block 2m+1 of lane c-8 for A, lanes c < 8 block 2m of lane c+8 for B (DPP row
+// shifts within each 16-lane row).  Whole lines can bypass L2 (non-temporal) without the
+// partial-line traffic that made 64-byte non-temporal stores write 1.5x the output bytes.
+__device__ __forceinline__ float dpp_shr8(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float dpp_shl8(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xf, 0xf, true));
+}
+__device__ __forceinline__ void store_pair(float *pa, float *pb, bool va, bool vb, int c16, f32x4 lo, f32x4 hi)
+{
+    f32x4 av, bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float sh = dpp_shr8(hi[i]), sl = dpp_shl8(lo[i]);
+        av[i] = c16 < 8 ? lo[i] : sh;
+        bv[i] = c16 >= 8 ? hi[i] : sl;
+    }
+    if (va)
+        __builtin_nontemporal_store(av, reinterpret_cast<f32x4 *>(pa));
+    if (vb)
+        __builtin_nontemporal_store(bv, reinterpret_cast<f32x4 *>(pb));
+}
+
 // Maps the hardware workgroup id to (b, kv-head, head slice, q-tile).
 struct BlockCoord {
     int b, hkv, hs, qt;
@@ -196,6 +226,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         }
     }
 
+
+    // Output row of column `col` of block qb (as tok/head above), offset to this lane's 16 bytes
+    // of a 128-byte line for store_pair; ok: the row exists.
+    auto row_ptr = [&](int qb, int col, bool &ok) __attribute__((always_inline)) {
+        const int r = wave * 32 + qb * 16 + col;
+        const int gh = r / a.Tm;
+        const int tk = t0 + r % a.Tm;
+        ok = gh < a.Gw && tk < a.L;
+        const int hd = bc.hkv * a.G + bc.hs * a.Gw + gh;
+        return a.out + (((size_t)bc.b * a.Lq + (ok ? tk - a.q_lo : 0)) * a.Hq + (ok ? hd : 0)) * D +
+               16 * (c16 >> 3) + 4 * g16;
+    };
     const int kv_row = a.Hkv * D;  // elements between consecutive positions
     const int L_in = a.L - a.n_cached;  // key rows held by k and v
     const uint16_t *kbase = a.k + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
@@ -373,8 +415,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
-            float *orow = a.out + (((size_t)bc.b * a.Lq + (valid[qb] ? tok[qb] - a.q_lo : 0)) * a.Hq +
-                                   (valid[qb] ? head[qb] : 0)) * D;
+            bool va, vb;
+            float *pa = row_ptr(qb, c16 & 7, va);
+            float *pb = row_ptr(qb, (c16 & 7) + 8, vb);
+            f32x4 od_lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
                 f32x4 od = {0.f, 0.f, 0.f, 0.f};
@@ -395,8 +439,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     }
                     od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[k], od, 0, 0, 0);
                 }
-                if (valid[qb])
-                    *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = od * inv;
+                if (db & 1)
+                    store_pair(pa + 16 * (db - 1), pb + 16 * (db - 1), va, vb, c16, od_lo * inv, od * inv);
+                else
+                    od_lo = od;
             }
         };
         pass(std::integral_constant<int, 0>());
@@ -664,14 +710,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
-            if (valid[qb]) {
-                float *orow = a.out + (((size_t)bc.b * a.Lq + tok[qb] - a.q_lo) * a.Hq + head[qb]) * D;
+            bool va, vb;
+            float *pa = row_ptr(qb, c16 & 7, va);
+            float *pb = row_ptr(qb, (c16 & 7) + 8, vb);
     #pragma unroll
-                for (int db = 0; db < kDBlocks; ++db)
-                    // Plain stores: L2 merges the 64-byte pieces of a row into whole lines
-                    // (non-temporal stores here cost 1.5x the output bytes in HBM writes).
-                    *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = o[db][qb] * inv;
-            }
+            for (int m = 0; m < kDBlocks / 2; ++m)
+                store_pair(pa + 32 * m, pb + 32 * m, va, vb, c16, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
         }
     }
 }
