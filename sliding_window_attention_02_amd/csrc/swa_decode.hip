@@ -132,18 +132,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             qf[kk] = __builtin_bit_cast(bf16x8, c16 < GB ? x : u32x4{0u, 0u, 0u, 0u});
         }
     }
-    const uint16_t *knew = fused ? a.kn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
-    const uint16_t *vnew = fused ? a.vn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
-    bf16x8 knf[kKSteps];  // the new token's K at this lane's fragment pieces
-    u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
-    if (fused) {
-#pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk)
-            knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
-        const int piece = min(lane, kPieces - 1);  // lanes past the row repeat its last piece
-        kn_piece = *reinterpret_cast<const u32x4 *>(knew + piece * 8);
-        vn_piece = *reinterpret_cast<const u32x4 *>(vnew + piece * 8);
-    }
     // Rows past the segment repeat its last slot (in-bounds; their scores are masked).
     const int last = seg_hi - 1;
     // K first (the scores need it first), then V, which is only needed after the softmax.
@@ -162,6 +150,24 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             }
         }
     }
+    // The position (a scalar load issued first) decides which wave holds the new token's slot:
+    // only that wave loads the new token (before V, so the scores need not wait for V).
+    const SlotMap sm(t, a.s, a.w_loc);
+    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
+    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
+    const bool owns_new = fused && slot_t >= seg_lo && slot_t < seg_hi;
+    bf16x8 knf[kKSteps];  // the new token's K at this lane's fragment pieces
+    u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
+    if (owns_new) {
+        const uint16_t *knew = a.kn + ((size_t)b * a.Hkv + hkv) * D;
+        const uint16_t *vnew = a.vn + ((size_t)b * a.Hkv + hkv) * D;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk)
+            knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
+        const int piece = min(lane, kPieces - 1);  // lanes past the row repeat its last piece
+        kn_piece = *reinterpret_cast<const u32x4 *>(knew + piece * 8);
+        vn_piece = *reinterpret_cast<const u32x4 *>(vnew + piece * 8);
+    }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         if (ch < nch) {
@@ -177,11 +183,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
     }
 
-    // ---- the position.
-    const SlotMap sm(t, a.s, a.w_loc);
-    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
-    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
-    if (fused && hs == 0 && slot_t >= seg_lo && slot_t < seg_hi && lane < kPieces) {
+    // ---- the new token's cache rows.
+    if (owns_new && hs == 0 && lane < kPieces) {
         *reinterpret_cast<u32x4 *>(a.kc + cache_base + (size_t)slot_t * D + lane * 8) = kn_piece;
         *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + lane * 8) = vn_piece;
     }
