@@ -30,7 +30,16 @@
 // V reads (ds_read_b64_tr_b16) are free of bank conflicts.  Q stays in registers for the
 // whole key loop.  Workgroups are ordered heavy-first (last q-tile first) and mapped so
 // that consecutive logical workgroups share an XCD and its L2, where neighbouring q-tiles
-// re-read the same K/V tiles.
+// re-read the same K/V tiles.  The fp32 output goes out in whole 128-byte lines with
+// non-temporal stores (store_pair).
+//
+// Two forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
+// then the middle tiles through a software pipeline.  The resident form (RES), for windows
+// whose q-tiles need at most four 32-key chunks (SWA(64,4) with 32-token q-tiles), loads all
+// of a q-tile's keys into LDS at once, takes the exact maximum, and stores O block by block
+// as it completes: no load follows any store, so the output drains under the compute (the
+// chip counts loads and stores in one in-order counter, so in the main form the output of a
+// round of workgroups is written after its compute and overlaps nothing).
 #include "swa_device.h"
 #include "swa_launch.h"
 
