@@ -150,23 +150,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             }
         }
     }
-    // The position (a scalar load issued first) decides which wave holds the new token's slot:
-    // only that wave loads the new token (before V, so the scores need not wait for V).
-    const SlotMap sm(t, a.s, a.w_loc);
-    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
-    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
-    const bool owns_new = fused && slot_t >= seg_lo && slot_t < seg_hi;
-    bf16x8 knf[kKSteps];  // the new token's K at this lane's fragment pieces
-    u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
-    if (owns_new) {
-        const uint16_t *knew = a.kn + ((size_t)b * a.Hkv + hkv) * D;
-        const uint16_t *vnew = a.vn + ((size_t)b * a.Hkv + hkv) * D;
+    // The new token's K at this lane's fragment pieces (every wave of the fused step: the scores
+    // need it and the position, which says which wave's chunk holds it, is not read yet).
+    const uint16_t *knew = fused ? a.kn + ((size_t)b * a.Hkv + hkv) * D : nullptr;
+    bf16x8 knf[kKSteps];
+    if (fused) {
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk)
             knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
-        const int piece = min(lane, kPieces - 1);  // lanes past the row repeat its last piece
-        kn_piece = *reinterpret_cast<const u32x4 *>(knew + piece * 8);
-        vn_piece = *reinterpret_cast<const u32x4 *>(vnew + piece * 8);
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
@@ -183,10 +174,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
     }
 
-    // ---- the new token's cache rows.
-    if (owns_new && hs == 0 && lane < kPieces) {
-        *reinterpret_cast<u32x4 *>(a.kc + cache_base + (size_t)slot_t * D + lane * 8) = kn_piece;
-        *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + lane * 8) = vn_piece;
+    // The position (a scalar load issued first) decides which wave holds the new token's slot;
+    // the wait for it and the slot arithmetic come after every position-independent load is in
+    // flight.  Only the owning wave loads the new token's row pieces (for its LDS row and the
+    // cache write, both after V has landed).
+    const SlotMap sm(t, a.s, a.w_loc);
+    const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
+    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
+    const bool owns_new = fused && slot_t >= seg_lo && slot_t < seg_hi;
+    u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
+    if (owns_new) {
+        const uint16_t *vnew = a.vn + ((size_t)b * a.Hkv + hkv) * D;
+        const int piece = min(lane, kPieces - 1);  // lanes past the row repeat its last piece
+        kn_piece = *reinterpret_cast<const u32x4 *>(knew + piece * 8);
+        vn_piece = *reinterpret_cast<const u32x4 *>(vnew + piece * 8);
     }
 
     // ---- scores of the whole segment (at most 96 slots, all in registers at once, so the
@@ -266,6 +267,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 
     // ---- V: wait for the rows in LDS, fix them up, O^T += V^T P^T per chunk.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): every V row is in LDS
+    // The new token's cache rows (their pieces have landed with V).
+    if (owns_new && hs == 0 && lane < kPieces) {
+        *reinterpret_cast<u32x4 *>(a.kc + cache_base + (size_t)slot_t * D + lane * 8) = kn_piece;
+        *reinterpret_cast<u32x4 *>(a.vc + cache_base + (size_t)slot_t * D + lane * 8) = vn_piece;
+    }
     // Fix-ups (LDS operations of a wave complete in order, so the transposed reads below see
     // them): before the ring wraps, zero the rows of slots outside A(t) and past the segment
     // (after it wraps, every row holds finite cache data and the masked ones get weight 0);
