@@ -350,23 +350,31 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             sc[w] = __builtin_amdgcn_exp2f(red_m[w][c16] - mm_use);  // 0 for a split with no key
             ll += red_l[w][c16] * sc[w];
         }
-        // Waves 1.. leave their scaled O^T in their own LDS rows; wave 0 adds them in order.
+        // Every wave leaves its rescaled O^T in its own LDS rows (the columns of real heads
+        // only); then wave w adds, in wave order, the d-blocks db = w, w + WAVES, ... of all
+        // waves and stores them.
         f32x4 *ored = reinterpret_cast<f32x4 *>(&vlds[0][0]);
-        if (wave > 0) {
+        if (c16 < GB) {
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db)
                 ored[db * 64 + lane] = o[db] * sc[wave];
         }
         __syncthreads();
-        if (wave > 0)
+        if (c16 >= GB)
             return;
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        float *orow = a.out + ((size_t)b * a.Hq + h0 + c16) * D;
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
-            o[db] *= sc[0];
+            if (db % WAVES != wave)
+                continue;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 1; w < WAVES; ++w)
-                o[db] += reinterpret_cast<const f32x4 *>(&vlds_all[w][0][0])[db * 64 + lane];
+            for (int w = 0; w < WAVES; ++w)
+                acc += reinterpret_cast<const f32x4 *>(&vlds_all[w][0][0])[db * 64 + lane];
+            *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = acc * inv;
         }
+        return;
     }
     if (c16 >= GB)
         return;
