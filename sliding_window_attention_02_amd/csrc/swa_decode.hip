@@ -333,11 +333,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     // the WAVES splits of this workgroup through LDS.
     float ll = sum_over_groups(lsum[0]);  // non-zero in lane group 0 only
     if constexpr (WAVES > 1) {
+        // Each wave leaves (m, l) and its unscaled O^T (the columns of real heads only) in its own
+        // LDS rows (it alone read them, so no barrier is needed first); after one barrier, wave w
+        // rescales and adds, in wave order, the d-blocks db = w, w + WAVES, ... of all waves and
+        // stores them.
+        f32x4 *ored = reinterpret_cast<f32x4 *>(&vlds[0][0]);
         if (g16 == 0) {
             red_m[wave][c16] = m_ref;
             red_l[wave][c16] = ll;
         }
-        __syncthreads();  // (also: every wave is done with its V rows, whose LDS now takes O)
+        if (c16 < GB) {
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db)
+                ored[db * 64 + lane] = o[db];
+        }
+        __syncthreads();
+        if (c16 >= GB)
+            return;
         float mm = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w)
@@ -350,18 +362,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             sc[w] = __builtin_amdgcn_exp2f(red_m[w][c16] - mm_use);  // 0 for a split with no key
             ll += red_l[w][c16] * sc[w];
         }
-        // Every wave leaves its rescaled O^T in its own LDS rows (the columns of real heads
-        // only); then wave w adds, in wave order, the d-blocks db = w, w + WAVES, ... of all
-        // waves and stores them.
-        f32x4 *ored = reinterpret_cast<f32x4 *>(&vlds[0][0]);
-        if (c16 < GB) {
-#pragma unroll
-            for (int db = 0; db < kDBlocks; ++db)
-                ored[db * 64 + lane] = o[db] * sc[wave];
-        }
-        __syncthreads();
-        if (c16 >= GB)
-            return;
         const float inv = ll > 0.f ? 1.f / ll : 0.f;
         float *orow = a.out + ((size_t)b * a.Hq + h0 + c16) * D;
 #pragma unroll
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < WAVES; ++w)
-                acc += reinterpret_cast<const f32x4 *>(&vlds_all[w][0][0])[db * 64 + lane];
+                acc += reinterpret_cast<const f32x4 *>(&vlds_all[w][0][0])[db * 64 + lane] * sc[w];
             *reinterpret_cast<f32x4 *>(orow + db * 16 + g16 * 4) = acc * inv;
         }
         return;
