@@ -675,7 +675,7 @@ def main():
         "roofline": {
             # (SWA(64,4) with 32-token q-tiles needs at most four 32-key chunks per q-tile: the
             # kernel's resident form)
-            "kernel": "prefill_kernel<128, true> (resident form)",
+            "kernel": "prefill_kernel<128, 2> (wide resident form)",
             "bound": "hbm",
             "achieved": round(achieved_gbs, 2),
             "peak": acc.PEAK_HBM_GBS,

@@ -67,8 +67,8 @@ extern "C" {
  * rounded to bf16 for the value product.
  * Errors: SWA_EINVAL for null or non-16-byte-aligned pointers, B, L, Hq, Hkv < 1,
  * Hq % Hkv != 0, w < 1, s < 0, unknown conv, w_loc < 1, non-finite or non-positive
- * scale; SWA_EUNSUPPORTED for d not in {64, 128} or a sequence of more than 2^31 - 1
- * elements in q or out; SWA_EHIP if the launch fails.
+ * scale; SWA_EUNSUPPORTED for d not in {64, 128}, a sequence of more than 2^31 - 1
+ * elements in q or out, or Hq * d >= 2^22; SWA_EHIP if the launch fails.
  */
 int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv,
                 int L, int d, int w, int s, float scale, int conv, void *stream);

@@ -107,6 +107,8 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
         return rc;
     if ((long long)L * Hq * d > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: one sequence of q holds more than 2^31-1 elements", fn);
+    if ((long long)Hq * d >= (1LL << 22))  // a q-tile's output rows must span less than 2 GiB
+        return fail(SWA_EUNSUPPORTED, "%s: Hq * d = %lld reaches 2^22", fn, (long long)Hq * d);
     return hip_status(fn, swa::launch_prefill(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale,
                                               static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start),
                                               static_cast<hipEvent_t>(stop)));
@@ -168,6 +170,8 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
         return rc;
     if ((long long)s + w_loc - 1 + C > 0x7fffffffLL || (long long)C * Hq * d > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: one sequence's keys or queries exceed 2^31-1 elements", fn);
+    if ((long long)Hq * d >= (1LL << 22))  // a q-tile's output rows must span less than 2 GiB
+        return fail(SWA_EUNSUPPORTED, "%s: Hq * d = %lld reaches 2^22", fn, (long long)Hq * d);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const swa::ChunkPlan plan = swa::chunk_plan(pos0, C, w_loc, s);
     const swa::PrefillKeySource cached = {k_cache, v_cache, plan.ns + plan.nw, plan.ns, plan.ring0};

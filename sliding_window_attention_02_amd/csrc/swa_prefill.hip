@@ -33,13 +33,16 @@
 // re-read the same K/V tiles.  The fp32 output goes out in whole 128-byte lines with
 // non-temporal stores (store_pair).
 //
-// Two forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
-// then the middle tiles through a software pipeline.  The resident form (RES), for windows
-// whose q-tiles need at most four 32-key chunks (SWA(64,4) with 32-token q-tiles), loads all
-// of a q-tile's keys into LDS at once, takes the exact maximum, and stores O block by block
-// as it completes: no load follows any store, so the output drains under the compute (the
-// chip counts loads and stores in one in-order counter, so in the main form the output of a
-// round of workgroups is written after its compute and overlaps nothing).
+// Three forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
+// then the middle tiles through a software pipeline.  The resident form, for windows whose
+// 32-token q-tiles need at most four 32-key chunks (SWA(64,4)), loads all of a q-tile's keys
+// into LDS at once, takes the exact maximum, and stores O block by block as it completes: no
+// load follows any store, so the output drains under the compute (the chip counts loads and
+// stores in one in-order counter, so in the main form the output of a round of workgroups is
+// written after its compute and overlaps nothing).  The wide resident form does the same for
+// 64-token q-tiles when four q-heads share a kv-head: five chunk slots (80 KiB, two
+// workgroups per CU) serve both 32-token halves, and each wave takes its head's two halves in
+// turn, so the keys shared by the halves are loaded once and half as many workgroups run.
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -130,6 +133,9 @@ constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // c >= 8 take block 2m+1 of lane c-8 for A, lanes c < 8 block 2m of lane c+8 for B (DPP row
 // shifts within each 16-lane row).  Whole lines can bypass L2 (non-temporal) without the
 // partial-line traffic that made 64-byte non-temporal stores write 1.5x the output bytes.
+// The stores are buffer stores over the q-tile's output rows: a row past the sequence (or a
+// padding row) gets an offset past the buffer's size and the hardware drops its store, so the
+// stores need no branch (a branch would end the compiler's scheduling region at every store).
 __device__ __forceinline__ float dpp_shr8(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
@@ -138,7 +144,9 @@ __device__ __forceinline__ float dpp_shl8(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xf, 0xf, true));
 }
-__device__ __forceinline__ void store_pair(float *pa, float *pb, bool va, bool vb, int c16, f32x4 lo, f32x4 hi)
+constexpr uint32_t kDropOffset = 0x80000000u;  // any offset at or past the buffer size
+__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t offa, uint32_t offb, int c16, f32x4 lo,
+                                           f32x4 hi)
 {
     f32x4 av, bv;
 #pragma unroll
@@ -147,10 +155,9 @@ __device__ __forceinline__ void store_pair(float *pa, float *pb, bool va, bool v
         av[i] = c16 < 8 ? lo[i] : sh;
         bv[i] = c16 >= 8 ? hi[i] : sl;
     }
-    if (va)
-        __builtin_nontemporal_store(av, reinterpret_cast<f32x4 *>(pa));
-    if (vb)
-        __builtin_nontemporal_store(bv, reinterpret_cast<f32x4 *>(pb));
+    // (aux 2: the non-temporal policy)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, av), rs, (int)offa, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bv), rs, (int)offb, 0, 2);
 }
 
 // Maps the hardware workgroup id to (b, kv-head, head slice, q-tile).
@@ -182,9 +189,14 @@ struct TileInfo {
     __device__ __forceinline__ bool full() const { return c_lo == 0 && c_hi == 1 && mask_free; }
 };
 
-template <int D, bool RES>
+// FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots), 2 wide resident
+// (64-token q-tiles taken as two 32-token halves per wave, five chunk slots).
+template <int D, int FORM>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
+    constexpr bool RES = FORM != 0;
+    constexpr bool WIDE = FORM == 2;
+    constexpr int NQB = WIDE ? 4 : 2;  // 16-column blocks per wave
     constexpr int kPieces = Lds<D>::kPieces;
     constexpr int kKSteps = D / 32;    // MFMA k-steps for S
     constexpr int kDBlocks = D / 16;   // 16-row blocks of O^T
@@ -196,6 +208,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 
     // Two buffers of (K tile, V tile), both row-major with swizzled 16-byte pieces.
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][kTileBytes];
+    // The wide form's fifth chunk slot (K, V); a token array in the other forms.
+    constexpr int kChunkBytes = kChunkN * kRowBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds5[2][WIDE ? kChunkBytes : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -208,12 +223,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const int t1 = min(t0 + a.Tm - 1, a.L - 1);
     const float c = a.scale_log2;
 
-    // This lane's query column in each of its two 16-column blocks.
-    int tok[2], head[2];
-    bool valid[2];
+    // This lane's query column in each of its 16-column blocks (the wave owns rows
+    // 16 NQB wave .. +16 NQB - 1).
+    int tok[NQB], head[NQB];
+    bool valid[NQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = wave * 32 + qb * 16 + c16;
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int r = wave * 16 * NQB + qb * 16 + c16;
         const int gh = r / a.Tm;
         tok[qb] = t0 + r % a.Tm;
         head[qb] = bc.hkv * a.G + bc.hs * a.Gw + gh;
@@ -221,9 +237,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 
     // Q^T B-operand fragments: d = kk*32 + 8*g16 .. +7 of the lane's query.
-    bf16x8 qf[2][kKSteps];
+    bf16x8 qf[NQB][kKSteps];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
         const uint16_t *qrow = a.q + (((size_t)bc.b * a.Lq + (valid[qb] ? tok[qb] - a.q_lo : 0)) * a.Hq +
                                       (valid[qb] ? head[qb] : 0)) * D;
 #pragma unroll
@@ -236,16 +252,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 
 
-    // Output row of column `col` of block qb (as tok/head above), offset to this lane's 16 bytes
-    // of a 128-byte line for store_pair; ok: the row exists.
-    auto row_ptr = [&](int qb, int col, bool &ok) __attribute__((always_inline)) {
-        const int r = wave * 32 + qb * 16 + col;
+    // Output buffer: the rows of tokens t0 .. t1, every head (fewer than 2^31 bytes: checked on
+    // the host).  row_off: byte offset of the row of column `col` of block qb (as tok/head above)
+    // plus this lane's 16 bytes of a 128-byte line for store_pair, or kDropOffset for a row that
+    // does not exist.
+    const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.out + ((size_t)bc.b * a.Lq + (t0 - a.q_lo)) * a.Hq * D, 0, (t1 - t0 + 1) * a.Hq * D * 4, 0x00020000);
+    auto row_off = [&](int qb, int col) __attribute__((always_inline)) {
+        const int r = wave * 16 * NQB + qb * 16 + col;
         const int gh = r / a.Tm;
         const int tk = t0 + r % a.Tm;
-        ok = gh < a.Gw && tk < a.L;
         const int hd = bc.hkv * a.G + bc.hs * a.Gw + gh;
-        return a.out + (((size_t)bc.b * a.Lq + (ok ? tk - a.q_lo : 0)) * a.Hq + (ok ? hd : 0)) * D +
-               16 * (c16 >> 3) + 4 * g16;
+        const uint32_t off = (uint32_t)(((tk - t0) * a.Hq + hd) * D + 16 * (c16 >> 3) + 4 * g16) * 4u;
+        return (gh < a.Gw && tk < a.L) ? off : kDropOffset;
     };
     const int kv_row = a.Hkv * D;  // elements between consecutive positions
     const int L_in = a.L - a.n_cached;  // key rows held by k and v
@@ -268,7 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
         ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
     }
-    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf.
+    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf
+    // (buf 2: the wide form's fifth chunk slot, which holds tile rows 0 .. 31, so only waves 0
+    // and 1 load into it).
     auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
         constexpr int kv = decltype(kv_c)::value;
         const uint16_t *base = kv ? vbase : kbase;
@@ -282,7 +303,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 const int j = wave_u * kLoadsPerWave + i;
                 // (the builtin takes a non-const global pointer; the source is only read)
                 __builtin_amdgcn_global_load_lds(const_cast<char *>(tile0 + (kv ? ld_voff[i] : ld_koff[i])),
-                                                 SWA_LDS_PTR(&lds[buf][kv][1024 * j]), 16, 0, 0);
+                                                 SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
+                                                 16, 0, 0);
             }
             return;
         }
@@ -303,8 +325,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 }
                 src = (kv ? a.vc : a.kc) + cache_base + (size_t)slot * D + piece * 8;
             }
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(src), SWA_LDS_PTR(&lds[buf][kv][1024 * j]), 16,
-                                             0, 0);
+            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(src),
+                                             SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
+                                             16, 0, 0);
         }
     };
     // (tags as types, passed as temporaries: named tag objects captured by the lambdas below
@@ -349,19 +372,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                              one_or_zero, one_or_zero, one_or_zero, one_or_zero};
 
     if constexpr (RES) {
-        // Resident form (windows whose q-tile needs at most four 32-key chunks): every chunk of
-        // the q-tile is loaded at once, chunk k into rows 32 (k & 1) .. of buffer k >> 1 (waves
-        // 2 (k & 1) and 2 (k & 1) + 1 load it), then one barrier, after which the workgroup
-        // issues no more loads.  The wave's two 16-column blocks are then done one after the
-        // other, each over all chunks and stored at once: the first block's stores drain while
-        // the second computes (a later wait for a load would also wait for those stores, since
-        // loads and stores share one in-order counter).
+        // Resident forms (windows whose 32-token q-tile needs at most four 32-key chunks): every
+        // chunk of the workgroup is loaded at once, slot k into rows 32 (k & 1) .. of buffer
+        // k >> 1 (waves 2 (k & 1) and 2 (k & 1) + 1 load it; buffer 2 is the wide form's fifth
+        // slot), then one barrier, after which the workgroup issues no more loads (the queries of
+        // both halves in the wide form were loaded before it).  Each 16-column block is then done
+        // over all of its chunks and stored at once: the stores of one block drain while the next
+        // computes (a later wait for a load would also wait for those stores, since loads and
+        // stores share one in-order counter).
+        constexpr int kSlots = WIDE ? 5 : 4;
         const ChunkWalk cw = plan_chunks(t0, t1, a.w_loc, a.s, kChunkN);
-        // Four chunk slots are always loaded and computed (straight-line code): a slot past the
-        // q-tile's chunks holds keys after t1 (rows past the sequence read its last row), which
-        // the element mask removes by causality.
+        // Every slot is always loaded (a slot past the workgroup's chunks holds keys after t1, and
+        // rows past the sequence read its last row), so any slot holds finite keys and values.
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kSlots; ++k) {
             if ((wave_u >> 1) == (k & 1)) {
                 const int j0 = cw.chunk(k) * kChunkN - (k & 1) * kChunkN;  // tile row 0 holds key j0
                 issue(j0, k >> 1, KRows());
@@ -370,15 +394,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
-        // With every key of the q-tile at hand the softmax needs no running maximum: all scores,
-        // the exact column maximum, the probabilities, then O^T = V^T P^T.
-        auto pass = [&](auto qb_c) __attribute__((always_inline)) {
+        // LDS rows of chunk slot k (K or V).
+        auto slot_rows = [&](int k, int kv) __attribute__((always_inline)) -> const unsigned char * {
+            if (WIDE && k == 4)
+                return &lds5[kv][0];
+            return &lds[k >> 1][kv][0] + (k & 1) * kChunkBytes;
+        };
+        // With every key of a 32-token half at hand the softmax needs no running maximum: all
+        // scores, the exact column maximum, the probabilities, then O^T = V^T P^T.  hw is the half's
+        // own chunk walk (four chunks, straight-line code: a chunk past the half's last needed one
+        // holds keys after its last token, which the element mask removes by causality), and
+        // slot[k] the slot holding chunk hw.chunk(k).
+        auto pass = [&](auto qb_c, const ChunkWalk &hw, const int (&slot)[4]) __attribute__((always_inline)) {
             constexpr int qb = decltype(qb_c)::value;
             const int t = tok[qb];
             f32x4 sr[4][2];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const unsigned char *kt = &lds[k >> 1][0][0] + (k & 1) * kChunkN * kRowBytes;
+                const unsigned char *kt = slot_rows(slot[k], 0);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     sr[k][h] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,11 +421,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         sr[k][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sr[k][h], 0, 0, 0);
                     }
                 }
+                if constexpr (WIDE)
+                    if (k & 1)
+                        __builtin_amdgcn_sched_barrier(0);
             }
             float mx = -INFINITY;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int key0 = cw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
+                const int key0 = hw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -424,16 +460,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
-            bool va, vb;
-            float *pa = row_ptr(qb, c16 & 7, va);
-            float *pb = row_ptr(qb, (c16 & 7) + 8, vb);
+            const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
             f32x4 od_lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
                 f32x4 od = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const unsigned char *vt = &lds[k >> 1][1][0] + (k & 1) * kChunkN * kRowBytes;
+                    const unsigned char *vt = slot_rows(slot[k], 1);
                     bf16x8 af;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
@@ -449,13 +483,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[k], od, 0, 0, 0);
                 }
                 if (db & 1)
-                    store_pair(pa + 16 * (db - 1), pb + 16 * (db - 1), va, vb, c16, od_lo * inv, od * inv);
+                    store_pair(out_rs, oa + 64 * (db - 1), ob + 64 * (db - 1), c16, od_lo * inv, od * inv);
                 else
                     od_lo = od;
             }
         };
-        pass(std::integral_constant<int, 0>());
-        pass(std::integral_constant<int, 1>());
+        if constexpr (!WIDE) {
+            const int slot[4] = {0, 1, 2, 3};
+            pass(std::integral_constant<int, 0>(), cw, slot);
+            pass(std::integral_constant<int, 1>(), cw, slot);
+        } else {
+            // The two 32-token halves of the q-tile, each with its own chunk walk.  A chunk the half
+            // needs is one the workgroup needs, so it has a slot: below cw.n_sink the sink slots,
+            // else the window slot counted from cw.win_lo.  A chunk past the half's needs may have
+            // none (its keys are masked whatever the slot holds): it takes the last slot.
+            auto half = [&](int h0, ChunkWalk &hw, int(&slot)[4]) __attribute__((always_inline)) {
+                hw = plan_chunks(h0, min(h0 + kChunkN - 1, t1), a.w_loc, a.s, kChunkN);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int ch = hw.chunk(k);
+                    const int sl = ch < cw.n_sink ? ch : cw.n_sink + (ch - cw.win_lo);
+                    slot[k] = min(max(sl, 0), kSlots - 1);
+                }
+            };
+            ChunkWalk hw;
+            int slot[4];
+            half(t0, hw, slot);
+            pass(std::integral_constant<int, 0>(), hw, slot);
+            pass(std::integral_constant<int, 1>(), hw, slot);
+            if (t0 + kChunkN <= t1) {
+                half(t0 + kChunkN, hw, slot);
+                pass(std::integral_constant<int, 2>(), hw, slot);
+                pass(std::integral_constant<int, 3>(), hw, slot);
+            }
+        }
     } else {
         const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
         const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
@@ -719,12 +780,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
-            bool va, vb;
-            float *pa = row_ptr(qb, c16 & 7, va);
-            float *pb = row_ptr(qb, (c16 & 7) + 8, vb);
+            const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
     #pragma unroll
             for (int m = 0; m < kDBlocks / 2; ++m)
-                store_pair(pa + 32 * m, pb + 32 * m, va, vb, c16, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
+                store_pair(out_rs, oa + 128 * m, ob + 128 * m, c16, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
         }
     }
 }
@@ -790,6 +849,20 @@ bool prefill_resident(int Tm, int q_lo, int w_loc, int s)
     return n <= 4;
 }
 
+namespace {
+
+// Kernel form of a launch: the wide resident form where a wave's 64 rows are one head's 64
+// tokens (four q-heads per kv-head slice) and each 32-token half fits the resident bound (then
+// the 64-token q-tile needs at most five chunks); else the resident form; else the main form.
+int prefill_form(const PrefillGeometry &g, int q_lo, int w_loc, int s)
+{
+    if (g.Gw == 4 && prefill_resident(g.Tm, q_lo, w_loc, s))
+        return 2;
+    return prefill_resident(g.Tm, q_lo, w_loc, s) ? 1 : 0;
+}
+
+}  // namespace
+
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
 {
     PrefillGeometry g;
@@ -815,7 +888,12 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
         Lq = L - cached->n_cached;
         q_lo = cached->n_cached;
     }
-    const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
+    PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
+    const int form = prefill_form(g, q_lo, w_loc, s);
+    if (form == 2) {  // 64-token q-tiles: twice the rows per workgroup
+        g.Tm *= 2;
+        g.n_qtiles = (Lq + g.Tm - 1) / g.Tm;
+    }
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -843,9 +921,10 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    const bool res = prefill_resident(g.Tm, q_lo, w_loc, s);
-    void (*kern)(PrefillArgs) = d == 128 ? (res ? prefill_kernel<128, true> : prefill_kernel<128, false>)
-                                         : (res ? prefill_kernel<64, true> : prefill_kernel<64, false>);
+    void (*const kernels[2][3])(PrefillArgs) = {
+        {prefill_kernel<64, 0>, prefill_kernel<64, 1>, prefill_kernel<64, 2>},
+        {prefill_kernel<128, 0>, prefill_kernel<128, 1>, prefill_kernel<128, 2>}};
+    void (*kern)(PrefillArgs) = kernels[d == 128 ? 1 : 0][form];
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
     else

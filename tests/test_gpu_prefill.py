@@ -96,6 +96,8 @@ PARITY = [
     (1, 64, 4, 1, 128, 1000, 0, 0, 1.0, 0),
     (3, 190, 6, 3, 64, 17, 2, 0, 2.0, 4),
     (1, 513, 5, 1, 128, 100, 1, 0, 1.0, 4),
+    # the wide resident form (G = 4) at d = 64: a last q-tile whose second half is one token
+    (3, 161, 8, 2, 64, 64, 4, 0, 1.0, 4),
 ]
 
 
