@@ -16,7 +16,9 @@ Printed JSON line (one):
   value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time
   decode           tokens/s of the decode leg and its HBM figures; other_batches: the same
                    decode graph timed alone at batch 1, batch 1024, and batch 64 with the steps
-                   rotating over 32 caches (570 MB, so every step reads HBM), outside the steps
+                   rotating over 32 caches (570 MB, so every step reads HBM), outside the steps;
+                   kv_* counts the K/V bytes read, all_bytes_* also q, the new token's K/V
+                   (read, and written to the cache) and the fp32 output
   prefill.cold_*   the prefill with L2 and Infinity Cache evicted before each launch
   roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
                    launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
@@ -206,8 +208,12 @@ def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 
     w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
     kv = acc.decode_kv_bytes(B, dw.Hkv, dw.d, acc.decode_keys(P, w_loc, dw.s))
     gbs = kv / (step_us * 1e-6) / 1e9
+    # every byte the step moves: the KV reads plus q, the new token's K/V (read and written to
+    # the cache) and the fp32 output
+    all_gbs = (kv + acc.decode_other_bytes(B, dw.Hq, dw.Hkv, dw.d)) / (step_us * 1e-6) / 1e9
     rec = {"B": B, "us_per_token_step": round(step_us, 3), "tokens_per_s": round(B / (step_us * 1e-6), 1),
-           "kv_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5)}
+           "kv_gb_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / acc.PEAK_HBM_GBS, 5),
+           "all_bytes_gb_per_s": round(all_gbs, 2), "all_bytes_frac_of_hbm_peak": round(all_gbs / acc.PEAK_HBM_GBS, 5)}
     if n_sets > 1:
         rec["cache_sets"] = n_sets
     return rec
@@ -696,7 +702,8 @@ def main():
             "frac": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
             "note": "the batch-64 working set stays in the Infinity Cache and the step is latency-bound; "
                     "at batch 1024 (other_batches) the same kernel streams its KV bytes from HBM",
-            "batch_1024": next(({"achieved": pt["kv_gb_per_s"], "frac": pt["frac_of_hbm_peak"]}
+            "batch_1024": next(({"achieved": pt["kv_gb_per_s"], "frac": pt["frac_of_hbm_peak"],
+                                 "all_bytes_frac": pt["all_bytes_frac_of_hbm_peak"]}
                                 for pt in points if pt.get("B") == 1024 and "cache_sets" not in pt), None),
         },
         "cpu_baseline": base,
