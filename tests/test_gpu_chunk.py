@@ -49,6 +49,9 @@ CASES = [
     (1, 32, 8, 128, 64, 4, 0, [64] * 9 + [24]),  # Llama-shaped heads, chunks of the window
     (2, 8, 8, 128, 300, 2, 0, [100, 156]),  # window longer than the sequence: full causal
     (1, 8, 2, 64, 33, 9, 0, [5, 61, 1, 1, 90]),
+    # four q-heads per kv-head, chunks starting on 32-key but not 64-key boundaries (the wide
+    # resident form's 64-token q-tiles over cached keys)
+    (1, 16, 4, 128, 64, 4, 0, [32, 96, 32, 50]),
 ]
 
 
