@@ -136,24 +136,16 @@ constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // The stores are buffer stores over the q-tile's output rows: a row past the sequence (or a
 // padding row) gets an offset past the buffer's size and the hardware drops its store, so the
 // stores need no branch (a branch would end the compiler's scheduling region at every store).
-__device__ __forceinline__ float dpp_shr8(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float dpp_shl8(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xf, 0xf, true));
-}
 constexpr uint32_t kDropOffset = 0x80000000u;  // any offset at or past the buffer size
-__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t offa, uint32_t offb, int c16, f32x4 lo,
-                                           f32x4 hi)
+__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t offa, uint32_t offb, f32x4 lo, f32x4 hi)
 {
     f32x4 av, bv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float sh = dpp_shr8(hi[i]), sl = dpp_shl8(lo[i]);
-        av[i] = c16 < 8 ? lo[i] : sh;
-        bv[i] = c16 >= 8 ? hi[i] : sl;
+        // One row shift each (row_shr:8 for A, row_shl:8 for B) with bound_ctrl off: a lane whose
+        // source lies outside its 16-lane row keeps `old`, its own value, so no select is needed.
+        av[i] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(lo[i]), __float_as_int(hi[i]), 0x118, 0xf, 0xf, false));
+        bv[i] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(hi[i]), __float_as_int(lo[i]), 0x108, 0xf, 0xf, false));
     }
     // (aux 2: the non-temporal policy)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, av), rs, (int)offa, 0, 2);
@@ -483,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[k], od, 0, 0, 0);
                 }
                 if (db & 1)
-                    store_pair(out_rs, oa + 64 * (db - 1), ob + 64 * (db - 1), c16, od_lo * inv, od * inv);
+                    store_pair(out_rs, oa + 64 * (db - 1), ob + 64 * (db - 1), od_lo * inv, od * inv);
                 else
                     od_lo = od;
             }
@@ -783,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
     #pragma unroll
             for (int m = 0; m < kDBlocks / 2; ++m)
-                store_pair(out_rs, oa + 128 * m, ob + 128 * m, c16, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
+                store_pair(out_rs, oa + 128 * m, ob + 128 * m, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
         }
     }
 }
