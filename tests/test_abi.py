@@ -63,6 +63,8 @@ def prefill(lib, q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, L=16, d=128, w=8, s=4, sc
     (dict(scale=0.0), binding.SWA_EINVAL, "scale"),
     (dict(scale=-1.0), binding.SWA_EINVAL, "scale"),
     (dict(L=1 << 20, Hq=32, Hkv=8), binding.SWA_EUNSUPPORTED, "2^31"),
+    # a q-tile's output rows would span 2 GiB (the stores' buffer offsets are 32-bit)
+    (dict(L=4, Hq=32768, Hkv=8), binding.SWA_EUNSUPPORTED, "2^22"),
 ])
 def test_prefill_rejects_on_host(lib, kw, code, msg):
     assert prefill(lib, **kw) == code
