@@ -60,6 +60,8 @@ def _load():
     lib.swa_oracle_row_weights.restype = i64
     lib.swa_oracle_prefill.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, i32]
     lib.swa_oracle_prefill.restype = i32
+    lib.swa_oracle_prefill_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, i64, i64, i32]
+    lib.swa_oracle_prefill_rows.restype = i32
     lib.swa_oracle_decode_row.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, vp]
     lib.swa_oracle_decode_row.restype = i64
     lib.swa_oracle_decode_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i64, i64, i64, i64, dbl, vp, i32]
@@ -129,6 +131,23 @@ def prefill(q, k, v, w: int, s: int, scale: float, conv: int = ADDITIVE,
                                     w_loc, s, float(scale), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"swa_oracle_prefill failed ({rc})")
+    return out
+
+
+def prefill_rows(q, k, v, t_lo: int, t_hi: int, w: int, s: int, scale: float, conv: int = ADDITIVE,
+                 nthreads: int | None = None) -> np.ndarray:
+    """Rows t_lo <= t < t_hi of prefill(q, k, v, ...): fp64 [B][t_hi - t_lo][Hq][d], each row
+    computed exactly as prefill computes it."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, L, Hkv, d) and v.shape == k.shape and 0 <= t_lo < t_hi <= L
+    w_loc = local_window(w, s, conv)
+    out = np.empty((B, t_hi - t_lo, Hq, d), dtype=np.float64)
+    rc = _load().swa_oracle_prefill_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, L, d, w_loc, s,
+                                         float(scale), t_lo, t_hi, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"swa_oracle_prefill_rows failed ({rc})")
     return out
 
 

@@ -135,6 +135,7 @@ typedef struct {
     const double *q, *k, *v;
     double *out;
     int64_t B, Hq, Hkv, L, d, w_loc, s;
+    int64_t t_lo, t_hi; /* rows computed: t_lo <= t < t_hi (out holds those rows only) */
     double scale;
     int64_t nthreads, tid;
     int status;
@@ -144,7 +145,8 @@ static void *prefill_worker(void *arg)
 {
     prefill_job *j = (prefill_job *)arg;
     const int64_t group = j->Hq / j->Hkv;
-    const int64_t rows = j->B * j->L * j->Hq;
+    const int64_t nt = j->t_hi - j->t_lo;
+    const int64_t rows = j->B * nt * j->Hq;
     const int64_t block = 16;
     double *p = (double *)malloc((size_t)j->L * sizeof(double));
     if (p == NULL) {
@@ -155,14 +157,14 @@ static void *prefill_worker(void *arg)
     for (int64_t r0 = j->tid * block; r0 < rows; r0 += j->nthreads * block) {
         for (int64_t r = r0; r < r0 + block && r < rows; ++r) {
             const int64_t h = r % j->Hq;
-            const int64_t t = (r / j->Hq) % j->L;
-            const int64_t b = r / (j->Hq * j->L);
+            const int64_t t = j->t_lo + (r / j->Hq) % nt;
+            const int64_t b = r / (j->Hq * nt);
             const int64_t kvh = h / group;
             const double *qr = j->q + ((b * j->L + t) * j->Hq + h) * j->d;
             const double *kb = j->k + (b * j->L * j->Hkv + kvh) * j->d;
             const double *vb = j->v + (b * j->L * j->Hkv + kvh) * j->d;
             const int64_t kv_stride = j->Hkv * j->d;
-            double *xr = j->out + ((b * j->L + t) * j->Hq + h) * j->d;
+            double *xr = j->out + ((b * nt + (t - j->t_lo)) * j->Hq + h) * j->d;
             swa_oracle_row_weights(qr, kb, kv_stride, (int)j->d, t, j->w_loc, j->s, j->scale, p);
             weighted_sum(p, vb, kv_stride, (int)j->d, t, j->w_loc, j->s, xr);
         }
@@ -172,15 +174,16 @@ static void *prefill_worker(void *arg)
     return NULL;
 }
 
-/* Whole-sequence SWA(w,s) attention.
- *   q:   [B][L][Hq][d]  k, v: [B][L][Hkv][d]  out: [B][L][Hq][d], all fp64, row-major.
+/* SWA(w,s) attention rows t_lo <= t < t_hi of whole sequences (every batch item and q-head).
+ *   q:   [B][L][Hq][d]  k, v: [B][L][Hkv][d]  out: [B][t_hi - t_lo][Hq][d], all fp64, row-major.
+ * Each row is computed exactly as in swa_oracle_prefill (rows are independent).
  * Returns 0, or -1 on bad arguments, -2 if a thread could not be started. */
-int swa_oracle_prefill(const double *q, const double *k, const double *v, double *out, int64_t B,
-                       int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t w_loc, int64_t s,
-                       double scale, int nthreads)
+int swa_oracle_prefill_rows(const double *q, const double *k, const double *v, double *out,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t w_loc,
+                            int64_t s, double scale, int64_t t_lo, int64_t t_hi, int nthreads)
 {
     if (!q || !k || !v || !out || B < 1 || L < 1 || d < 1 || Hkv < 1 || Hq < Hkv ||
-        Hq % Hkv != 0 || w_loc < 1 || s < 0)
+        Hq % Hkv != 0 || w_loc < 1 || s < 0 || t_lo < 0 || t_hi > L || t_lo >= t_hi)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -193,7 +196,7 @@ int swa_oracle_prefill(const double *q, const double *k, const double *v, double
     }
     int started = 0, rc = 0;
     for (int i = 0; i < nthreads; ++i) {
-        prefill_job j = {q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale, nthreads, i, -3};
+        prefill_job j = {q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, t_lo, t_hi, scale, nthreads, i, -3};
         jobs[i] = j;
         if (pthread_create(&th[i], NULL, prefill_worker, &jobs[i]) != 0) {
             rc = -2;
@@ -211,6 +214,16 @@ int swa_oracle_prefill(const double *q, const double *k, const double *v, double
     free(jobs);
     free(th);
     return rc;
+}
+
+/* Whole-sequence SWA(w,s) attention: every row t < L.
+ *   q:   [B][L][Hq][d]  k, v: [B][L][Hkv][d]  out: [B][L][Hq][d], all fp64, row-major.
+ * Returns 0, or -1 on bad arguments, -2 if a thread could not be started. */
+int swa_oracle_prefill(const double *q, const double *k, const double *v, double *out, int64_t B,
+                       int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t w_loc, int64_t s,
+                       double scale, int nthreads)
+{
+    return swa_oracle_prefill_rows(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale, 0, L, nthreads);
 }
 
 /* One decode row from an explicit set of cached positions.

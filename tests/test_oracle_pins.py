@@ -281,3 +281,39 @@ def test_inputs_are_seeded_and_sink_boost_is_exact():
     k2, v2 = inputs.kv_at(5, 262144, 2, 8, 16)
     assert torch.equal(k1, k2) and torch.equal(v1, v2) and not torch.equal(k1, v1)
     assert not torch.equal(inputs.kv_at(5, 262145, 2, 8, 16)[0], k1)
+
+
+@pytest.mark.parametrize("nthreads", [1, 2, 3, 7])
+def test_decode_rows_batch_with_mixed_positions_equals_sdpa_rows(nthreads):
+    """decode_rows over a batch whose items sit at different positions (before the sinks fill,
+    inside the first window, long after it), spread over threads: item b equals row t[b] of its
+    own sequence under torch SDPA with the recipe mask, and the thread count changes no bit.
+    Distinct data per item, so a wrong batch stride or a swapped query position fails."""
+    B, L, Hq, Hkv, d, w, s, scale = 5, 90, 6, 3, 8, 12, 3, 0.3
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=41, sink_boost_n=3, sink_boost=4.0)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), causal_recipe_mask(L, w, s), scale)
+    ts = [0, 2, 13, 47, 89]
+    pos = np.random.default_rng(5).permutation(L).astype(np.int64)  # shared candidates, shuffled
+    kq = f64(k)[:, pos]
+    vq = f64(v)[:, pos]
+    qt = np.stack([f64(q)[b, ts[b]] for b in range(B)])
+    out = orc.decode_rows(qt, pos, kq, vq, ts, w, s, scale, nthreads=nthreads)
+    for b in range(B):
+        np.testing.assert_allclose(out[b], ref[b, ts[b]], rtol=0, atol=1e-12)
+        one, used = orc.decode_row(qt[b], pos, kq[b], vq[b], ts[b], w, s, scale)
+        assert used == min(ts[b] + 1, w + s)
+        assert np.array_equal(out[b], one)
+    assert np.array_equal(out, orc.decode_rows(qt, pos, kq, vq, ts, w, s, scale, nthreads=1))
+
+
+@pytest.mark.parametrize("t_lo,t_hi,nthreads", [(0, 70, 3), (17, 18, 1), (40, 70, 4), (69, 70, 2)])
+def test_prefill_rows_equal_sdpa_rows(t_lo, t_hi, nthreads):
+    """The row-range entry (used to time a bounded sample of a large workload) equals the same
+    rows of torch SDPA with the recipe mask, and the whole-sequence prefill bit for bit."""
+    B, L, Hq, Hkv, d, w, s, scale = 2, 70, 4, 2, 16, 9, 2, 0.25
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=43, sink_boost_n=2, sink_boost=4.0)
+    ref = sdpa_reference(f64(q), f64(k), f64(v), causal_recipe_mask(L, w, s), scale)
+    got = orc.prefill_rows(f64(q), f64(k), f64(v), t_lo, t_hi, w, s, scale, nthreads=nthreads)
+    np.testing.assert_allclose(got, ref[:, t_lo:t_hi], rtol=0, atol=1e-12)
+    whole = orc.prefill(f64(q), f64(k), f64(v), w, s, scale)
+    assert np.array_equal(got, whole[:, t_lo:t_hi])
