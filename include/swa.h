@@ -85,6 +85,30 @@ int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, i
                       void *start_event, void *stop_event);
 
 /*
+ * swa_prefill_describe -- what swa_prefill launches for a shape (host only, no GPU call): the
+ * kernel form, its tile geometry and the work its matrix cores do.
+ *
+ *   form            0: the tile walk (64-key tiles; edge tiles masked, middle tiles unmasked);
+ *                   1: resident (every 32-key chunk a 32-token q-tile needs held in LDS at once,
+ *                      at most four: windows with ceil((w_loc-1)/32) + ceil(s/32) <= 3);
+ *                   2: wide resident (form 1 for 64-token q-tiles taken as two 32-token halves,
+ *                      when four q-heads share a kv-head)
+ *   tokens_per_tile query tokens per workgroup; heads_per_tile q-heads per workgroup
+ *   workgroups      grid size
+ *   executed_pairs  (query row, key) pairs whose scores and value products the matrix cores
+ *                   compute, padding rows and masked keys included (each costs 4 d flops)
+ * Errors: as swa_prefill for the sizes, window and convention; SWA_EINVAL for a null info.
+ */
+typedef struct swa_prefill_info {
+    int form;
+    int tokens_per_tile;
+    int heads_per_tile;
+    long long workgroups;
+    long long executed_pairs;
+} swa_prefill_info;
+int swa_prefill_describe(int B, int Hq, int Hkv, int L, int d, int w, int s, int conv, swa_prefill_info *info);
+
+/*
  * swa_kv_append -- write new tokens' keys and values into the bounded decode cache.
  *
  * Cache layout (per batch b and kv-head): s pinned sink slots followed by a ring of
@@ -106,10 +130,40 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
                   void *stream);
 
 /*
+ * swa_cache_slots -- slots per (sequence, kv-head) of the bounded decode cache: s + w_loc, with
+ * w_loc = w (SWA_CONV_ADDITIVE) or w - s (SWA_CONV_TOTAL).  Returns -1 (and sets the message)
+ * for w < 1, s < 0, an unknown conv or w_loc < 1.
+ */
+long long swa_cache_slots(int w, int s, int conv);
+
+/*
  * swa_decode_workspace_bytes -- device workspace that swa_decode_step needs for this
  * shape (0 when the step runs without a split).  Returns 0 for invalid arguments too.
  */
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, int conv);
+
+/*
+ * swa_decode_describe -- how swa_decode_step / swa_append_decode_step split a shape (host only):
+ *   splits               slot segments per (sequence, kv-head, head slice)
+ *   waves_per_workgroup  1, or the splits of one workgroup merged in LDS (2-4 waves, one 32-slot
+ *                        chunk each, when s + w_loc spans 2-4 chunks)
+ *   slots_per_split      slots of a segment (at most 96 for one wave)
+ *   heads_per_wave       q-heads sharing a kv-head taken as the MFMA columns of one wave (<= 16)
+ *   workgroups           grid size of the attend kernel
+ *   merge_launch         1 when a second kernel merges workgroup splits through the workspace
+ *   workspace_bytes      as swa_decode_workspace_bytes
+ * Errors: as swa_decode_step for the sizes, window and convention; SWA_EINVAL for a null info.
+ */
+typedef struct swa_decode_info {
+    int splits;
+    int waves_per_workgroup;
+    int slots_per_split;
+    int heads_per_wave;
+    long long workgroups;
+    int merge_launch;
+    size_t workspace_bytes;
+} swa_decode_info;
+int swa_decode_describe(int B, int Hq, int Hkv, int d, int w, int s, int conv, swa_decode_info *info);
 
 /*
  * swa_decode_step -- one-token GQA decode over the bounded cache.
@@ -151,6 +205,18 @@ int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const vo
                            size_t workspace_bytes, void *stream);
 
 /*
+ * swa_append_decode_step_timed -- swa_append_decode_step whose kernel dispatches also stamp two
+ * caller-created HIP events (hipEvent_t, timing enabled) with the start of the step's first
+ * kernel and the end of its last one (hipExtLaunchKernel), for callers that time the kernels
+ * rather than the stream interval around them.  Same arguments, layout and errors as
+ * swa_append_decode_step, plus SWA_EINVAL if either event is null.
+ */
+int swa_append_decode_step_timed(const void *q, void *k_cache, void *v_cache, const void *k_new,
+                                 const void *v_new, float *out, const int64_t *pos, int B, int Hq,
+                                 int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
+                                 size_t workspace_bytes, void *stream, void *start_event, void *stop_event);
+
+/*
  * swa_prefill_chunk -- prefill of one prompt chunk against the bounded cache, then the chunk
  * appended to it: the long-prompt procedure of page "从长文档摘要说起" (wiblog.cn), section
  * "长 Prompt 的分块处理与工程实现" and its flow description (a long input is processed in
@@ -181,7 +247,7 @@ int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache
 
 /*
  * Decoder-layer decode step around SWA(w,s) attention, for the multi-layer decode
- * measurement of page "滑动窗口注意力（SWA）配 sinks 比 post-training 线性注意力更划算"
+ * measurement of page "几亿Token白练了？微软实测：免训练滑动窗口，让线性注意力破防" (PaperWeekly)
  * (section "小窗口也有工程优势": decode throughput and state memory of a 4-layer Transformer
  * at batch 1 from 128 to 256K tokens of context).  The pages fix no layer recipe; this is the
  * standard pre-norm layer, with activations stored in bf16 where noted:
@@ -243,17 +309,23 @@ int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache,
 const char *swa_last_error(void);
 
 /*
- * Test hooks: dump the allowed-index sets exactly as the kernels derive them, using the
- * same device functions as the hot kernels.
+ * Test hooks: the index sets the kernels attend to, derived by the kernels' own device
+ * functions (walks, slot maps and admission tests shared with the hot kernels).
  *
- * swa_debug_prefill_mask: mask uint8 [L][L] device (out).  mask[t][i] = 1 iff the
- * prefill kernel that swa_prefill would launch for (L, Hq, Hkv, d, w, s, conv) visits key i
- * for the tile holding query t and either classifies those keys as mask-free or its element
- * predicate admits (t, i).  Requires L <= 8192.
+ * swa_debug_prefill_mask: mask uint8 [L][L] device (out).  mask[t][i] counts how often the
+ * prefill kernel that swa_prefill launches for (L, Hq, Hkv, d, w, s, conv) attends to the key
+ * held at position i for query t: the same form and q-tile geometry (swa_prefill_describe), the
+ * same tile or chunk walk, mask-free classification and element predicate, and (resident forms)
+ * the key each LDS chunk slot actually holds, through the wide form's per-half slot map.  A
+ * correct kernel gives 1 on A(t) and 0 elsewhere.  Requires L <= 8192.
  *
- * swa_debug_decode_slots: slot_pos int64 [B][s + w_loc] device (out): the position the
- * decode kernel reads from each slot for query position pos[b], or -1 if the slot is
- * skipped.
+ * swa_debug_decode_slots: slot_pos int64 [B][s + w_loc] device (out).  For every split segment
+ * of the decode plan, each slot goes through the decode kernel's admission test (once the ring
+ * has wrapped, every slot of the segment; before, the 32-bit validity test from t alone);
+ * slot_pos[b][j] = the position slot j holds for query position pos[b] if admitted (position
+ * pos[b] at the slot the fused append+decode step writes), else -1.  -2 marks an admitted slot
+ * holding no position of A(pos[b]), -3 a slot covered by two split segments (neither occurs in
+ * a correct kernel).
  */
 int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w, int s, int conv,
                            void *stream);

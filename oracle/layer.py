@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY: the test suite and the benchmark's CPU-baseline leg are the only
 callers; the GPU package never imports this module and this module imports nothing from it.
 
-The pages time decode through "a 4-layer Transformer" at batch 1 (page "滑动窗口注意力（SWA）
-配 sinks 比 post-training 线性注意力更划算", section on the engineering advantage of a small
-window: decode throughput and state memory against context length).  They give no layer
+The pages time decode through a 4-layer Transformer at batch 1 (page "几亿Token白练了？微软实测：
+免训练滑动窗口，让线性注意力破防" (PaperWeekly), section "小窗口也有工程优势": decode throughput
+and state memory against context length).  They give no layer
 dimensions or layer recipe, so this oracle takes the plainest standard pre-norm decoder layer:
 
     h   = bf16( rmsnorm(x) * g_attn )                 x: fp32 residual stream [dm]

@@ -10,9 +10,11 @@ from .binding import (  # noqa: F401
     SwaError,
     alloc_cache,
     alloc_workspace,
+    cache_slots,
     append_decode_step,
     debug_decode_slots,
     debug_prefill_mask,
+    decode_describe,
     decode_step,
     decode_workspace_bytes,
     kv_append,
@@ -23,5 +25,6 @@ from .binding import (  # noqa: F401
     local_window,
     prefill,
     prefill_chunk,
+    prefill_describe,
     rmsnorm,
 )

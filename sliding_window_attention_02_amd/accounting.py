@@ -50,19 +50,7 @@ def kv_cache_bytes(layers: int, seq: int, d_q: int, n_kv: int, bytes_per_value: 
     return 2 * layers * seq * d_q * n_kv * bytes_per_value
 
 
-def prefill_executed_pairs(L: int, Hq: int, Hkv: int, w_loc: int, s: int, tile_n: int = 64,
-                           rows: int = 128) -> int:
-    """(query row, key) pairs the tiled prefill kernel multiplies per batch item, tile waste
-    included: every visited tile costs rows x tile_n pairs (for reporting executed MFMA work)."""
-    G = Hq // Hkv
-    Gw = next(c for c in (4, 3, 2, 1) if G % c == 0)
-    Tm = rows // Gw
-    total = 0
-    for t0 in range(0, L, Tm):
-        t1 = min(t0 + Tm - 1, L - 1)
-        lo = max(0, t0 - w_loc + 1)
-        win_lo, win_hi = lo // tile_n, t1 // tile_n
-        sink_tiles = (min(s, t1 + 1) + tile_n - 1) // tile_n
-        n_tiles = min(sink_tiles, win_lo) + (win_hi - win_lo + 1)
-        total += n_tiles * tile_n * rows
-    return total * Hkv * (G // Gw)
+def attainable_tflops(useful_flops_: float, algorithmic_bytes: float) -> float:
+    """Roofline bound of a kernel doing useful_flops_ over algorithmic_bytes: the smaller of the
+    bf16 MFMA peak and arithmetic intensity x HBM peak (TFLOP/s)."""
+    return min(PEAK_BF16_TFLOPS, useful_flops_ / algorithmic_bytes * PEAK_HBM_GBS / 1e3)

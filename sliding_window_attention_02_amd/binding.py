@@ -26,10 +26,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 EXPORTS = (
     "swa_prefill",
     "swa_prefill_timed",
+    "swa_prefill_describe",
+    "swa_cache_slots",
     "swa_kv_append",
     "swa_decode_workspace_bytes",
+    "swa_decode_describe",
     "swa_decode_step",
     "swa_append_decode_step",
+    "swa_append_decode_step_timed",
     "swa_prefill_chunk",
     "swa_last_error",
     "swa_debug_prefill_mask",
@@ -41,6 +45,17 @@ EXPORTS = (
 )
 
 LINEAR_MODES = {"store": 0, "add": 1, "silu_mul": 2}
+
+
+class _PrefillInfoC(ctypes.Structure):
+    _fields_ = [("form", ctypes.c_int), ("tokens_per_tile", ctypes.c_int), ("heads_per_tile", ctypes.c_int),
+                ("workgroups", ctypes.c_longlong), ("executed_pairs", ctypes.c_longlong)]
+
+
+class _DecodeInfoC(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int), ("waves_per_workgroup", ctypes.c_int), ("slots_per_split", ctypes.c_int),
+                ("heads_per_wave", ctypes.c_int), ("workgroups", ctypes.c_longlong), ("merge_launch", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _LayerWeightsC(ctypes.Structure):
@@ -68,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.swa_prefill.restype = i32
     L.swa_prefill_timed.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
     L.swa_prefill_timed.restype = i32
+    L.swa_prefill_describe.argtypes = [i32] * 8 + [ctypes.POINTER(_PrefillInfoC)]
+    L.swa_prefill_describe.restype = i32
+    L.swa_decode_describe.argtypes = [i32] * 7 + [ctypes.POINTER(_DecodeInfoC)]
+    L.swa_decode_describe.restype = i32
+    L.swa_cache_slots.argtypes = [i32, i32, i32]
+    L.swa_cache_slots.restype = ctypes.c_longlong
     L.swa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.swa_kv_append.restype = i32
     L.swa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -77,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.swa_append_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                          vp]
     L.swa_append_decode_step.restype = i32
+    L.swa_append_decode_step_timed.argtypes = L.swa_append_decode_step.argtypes + [vp, vp]
+    L.swa_append_decode_step_timed.restype = i32
     i64 = ctypes.c_int64
     L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.swa_prefill_chunk.restype = i32
@@ -125,12 +148,25 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def cache_slots(w: int, s: int, conv: int = ADDITIVE) -> int:
+    """Slots per (sequence, kv-head) of the decode cache, s + w_loc (swa_cache_slots)."""
+    n = lib().swa_cache_slots(w, s, conv)
+    if n < 0:
+        raise SwaError(SWA_EINVAL, last_error())
+    return int(n)
+
+
 def local_window(w: int, s: int, conv: int = ADDITIVE) -> int:
-    """Local window length: w (additive convention) or w - s (total-window convention)."""
-    wl = w if conv == ADDITIVE else w - s
-    if conv not in (ADDITIVE, TOTAL) or w < 1 or s < 0 or wl < 1:
-        raise ValueError(f"no local window for w={w}, s={s}, conv={conv}")
-    return wl
+    """Local window length w_loc: w (additive convention) or w - s (total-window convention)."""
+    return cache_slots(w, s, conv) - s
+
+
+def prefill_describe(B: int, Hq: int, Hkv: int, L: int, d: int, w: int, s: int, conv: int = ADDITIVE) -> dict:
+    """What swa_prefill launches for this shape (swa_prefill_describe): kernel form, q-tile
+    geometry, grid size and the (query row, key) pairs its matrix cores compute."""
+    info = _PrefillInfoC()
+    _check(lib().swa_prefill_describe(B, Hq, Hkv, L, d, w, s, conv, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in _PrefillInfoC._fields_}
 
 
 def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADDITIVE, out=None,
@@ -161,9 +197,16 @@ def prefill(q, k, v, w: int, s: int, scale: float | None = None, conv: int = ADD
     return out
 
 
+def decode_describe(B: int, Hq: int, Hkv: int, d: int, w: int, s: int, conv: int = ADDITIVE) -> dict:
+    """How the decode step splits this shape (swa_decode_describe)."""
+    info = _DecodeInfoC()
+    _check(lib().swa_decode_describe(B, Hq, Hkv, d, w, s, conv, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in _DecodeInfoC._fields_}
+
+
 def alloc_cache(B: int, Hkv: int, d: int, w: int, s: int, conv: int = ADDITIVE, device="cuda"):
     """Empty (k_cache, v_cache), bf16 [B][Hkv][s + w_loc][d] each."""
-    n = s + local_window(w, s, conv)
+    n = cache_slots(w, s, conv)
     k = torch.zeros((B, Hkv, n, d), dtype=torch.bfloat16, device=device)
     return k, torch.zeros_like(k)
 
@@ -172,7 +215,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, pos, w: int, s: int, conv: int = A
     """Write k_new/v_new bf16 [B][n_new][Hkv][d] at positions pos[b] .. pos[b]+n_new-1."""
     B, Hkv, n_slots, d = k_cache.shape
     n_new = k_new.shape[1]
-    if n_slots != s + local_window(w, s, conv):
+    if n_slots != cache_slots(w, s, conv):
         raise ValueError("cache slot count does not match s + w_loc")
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
@@ -198,7 +241,7 @@ def decode_step(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = 
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     _need(q, "q", torch.bfloat16)
-    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, cache_slots(w, s, conv), d))
     _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
     _need(pos, "pos", torch.int64, (B,))
     if out is None:
@@ -216,13 +259,16 @@ def decode_step(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = 
 
 
 def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, scale: float | None = None,
-                       conv: int = ADDITIVE, out=None, workspace=None):
+                       conv: int = ADDITIVE, out=None, workspace=None, events=None):
     """kv_append of one token per sequence (k_new/v_new bf16 [B][Hkv][d] at positions pos[b])
-    and decode_step for the query at that position, in one launch -> fp32 [B][Hq][d]."""
+    and decode_step for the query at that position, in one launch -> fp32 [B][Hq][d].
+
+    events: optional (start, stop) torch.cuda.Event pair (timing enabled, already recorded once
+    so that the HIP events exist); the kernel dispatches stamp them (swa_append_decode_step_timed)."""
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     _need(q, "q", torch.bfloat16)
-    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, cache_slots(w, s, conv), d))
     _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
     _need(k_new, "k_new", torch.bfloat16, (B, Hkv, d))
     _need(v_new, "v_new", torch.bfloat16, (B, Hkv, d))
@@ -235,9 +281,12 @@ def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, s
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib().swa_append_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
-                                        v_new.data_ptr(), out.data_ptr(), pos.data_ptr(), B, Hq, Hkv, d, w, s, scale,
-                                        conv, ws_ptr or None, ws_bytes, _stream(q)))
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(),
+            pos.data_ptr(), B, Hq, Hkv, d, w, s, scale, conv, ws_ptr or None, ws_bytes, _stream(q))
+    if events is None:
+        _check(lib().swa_append_decode_step(*args))
+    else:
+        _check(lib().swa_append_decode_step_timed(*args, events[0].cuda_event, events[1].cuda_event))
     return out
 
 
@@ -252,7 +301,7 @@ def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: f
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, (B, C, Hkv, d))
     _need(v, "v", torch.bfloat16, (B, C, Hkv, d))
-    n_slots = s + local_window(w, s, conv)
+    n_slots = cache_slots(w, s, conv)
     _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, n_slots, d))
     _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, n_slots, d))
     if out is None:
@@ -265,7 +314,8 @@ def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: f
 
 
 def debug_prefill_mask(L: int, Hq: int, Hkv: int, w: int, s: int, conv: int = ADDITIVE, device="cuda", d: int = 128):
-    """uint8 [L][L]: the (query, key) pairs the prefill kernel for these arguments admits."""
+    """uint8 [L][L]: how often the prefill kernel launched for these arguments attends to each
+    (query, key) pair (1 on A(t) and 0 elsewhere for a correct kernel)."""
     m = torch.empty((L, L), dtype=torch.uint8, device=device)
     _check(lib().swa_debug_prefill_mask(m.data_ptr(), L, Hq, Hkv, d, w, s, conv, _stream(m)))
     return m
@@ -275,7 +325,7 @@ def debug_decode_slots(pos, w: int, s: int, conv: int = ADDITIVE):
     """int64 [B][s + w_loc]: position the decode kernel reads from each slot, -1 if skipped."""
     _need(pos, "pos", torch.int64)
     B = pos.shape[0]
-    out = torch.empty((B, s + local_window(w, s, conv)), dtype=torch.int64, device=pos.device)
+    out = torch.empty((B, cache_slots(w, s, conv)), dtype=torch.int64, device=pos.device)
     _check(lib().swa_debug_decode_slots(out.data_ptr(), pos.data_ptr(), B, w, s, conv, _stream(pos)))
     return out
 
@@ -339,7 +389,7 @@ def layer_decode_step(x, weights: dict, k_cache, v_cache, pos, Hq: int, w: int, 
     _, Hkv, n_slots, d = k_cache.shape
     f = weights["w_down"].shape[1]
     _need(x, "x", torch.float32)
-    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, s + local_window(w, s, conv), d))
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, cache_slots(w, s, conv), d))
     _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
     _need(pos, "pos", torch.int64, (B,))
     shapes = {"attn_norm": (dm,), "w_qkv": ((Hq + 2 * Hkv) * d, dm), "w_o": (dm, Hq * d), "mlp_norm": (dm,),

@@ -116,7 +116,8 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
 
 int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache, const void *k_new,
                 const void *v_new, float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,
-                float scale, int conv, void *workspace, size_t workspace_bytes, void *stream)
+                float scale, int conv, void *workspace, size_t workspace_bytes, void *stream, void *start = nullptr,
+                void *stop = nullptr)
 {
     CHECK_PTR(q);
     CHECK_PTR(k_cache);
@@ -144,7 +145,8 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
     }
     return hip_status(fn, swa::launch_decode(q, const_cast<void *>(k_cache), const_cast<void *>(v_cache), k_new,
                                              v_new, out, pos, B, Hq, Hkv, d, w_loc, s, scale, workspace, plan,
-                                             static_cast<hipStream_t>(stream)));
+                                             static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start),
+                                             static_cast<hipEvent_t>(stop)));
 }
 
 int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void *k_cache, void *v_cache, float *out,
@@ -259,6 +261,28 @@ int swa_prefill(const void *q, const void *k, const void *v, float *out, int B, 
                         nullptr);
 }
 
+int swa_prefill_describe(int B, int Hq, int Hkv, int L, int d, int w, int s, int conv, swa_prefill_info *info)
+{
+    const char *fn = "swa_prefill_describe";
+    if (info == nullptr)
+        return fail(SWA_EINVAL, "%s: info is null", fn);
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    if (L < 1)
+        return fail(SWA_EINVAL, "%s: L must be >= 1 (got %d)", fn, L);
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    const swa::PrefillPlan p = swa::prefill_plan(B, Hq, Hkv, L, w_loc, s);
+    info->form = p.form;
+    info->tokens_per_tile = p.g.Tm;
+    info->heads_per_tile = p.g.Gw;
+    info->workgroups = p.workgroups;
+    info->executed_pairs = p.executed_pairs;
+    return ok();
+}
+
 int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, int B, int Hq, int Hkv, int L,
                       int d, int w, int s, float scale, int conv, void *stream, void *start_event,
                       void *stop_event)
@@ -293,6 +317,15 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
                                                 n_new, static_cast<hipStream_t>(stream)));
 }
 
+long long swa_cache_slots(int w, int s, int conv)
+{
+    int w_loc = 0;
+    if (resolve_window("swa_cache_slots", w, s, conv, &w_loc))
+        return -1;
+    ok();
+    return (long long)s + w_loc;
+}
+
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, int conv)
 {
     const char *fn = "swa_decode_workspace_bytes";
@@ -306,6 +339,30 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, i
     return swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes;
 }
 
+
+int swa_decode_describe(int B, int Hq, int Hkv, int d, int w, int s, int conv, swa_decode_info *info)
+{
+    const char *fn = "swa_decode_describe";
+    if (info == nullptr)
+        return fail(SWA_EINVAL, "%s: info is null", fn);
+    int rc = check_heads(fn, B, Hq, Hkv, d);
+    if (rc)
+        return rc;
+    int w_loc = 0;
+    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+        return rc;
+    if ((long long)s + w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    const swa::DecodePlan p = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    info->splits = p.n_split;
+    info->waves_per_workgroup = p.wg_waves;
+    info->slots_per_split = p.slots_per_split;
+    info->heads_per_wave = p.Gb;
+    info->workgroups = (long long)B * Hkv * p.n_hslices * (p.n_split / p.wg_waves);
+    info->merge_launch = p.n_split != p.wg_waves;
+    info->workspace_bytes = p.workspace_bytes;
+    return ok();
+}
 
 int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, float *out, const int64_t *pos,
                     int B, int Hq, int Hkv, int d, int w, int s, float scale, int conv, void *workspace,
@@ -324,6 +381,20 @@ int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const vo
     CHECK_PTR(v_new);
     return decode_impl(fn, q, k_cache, v_cache, k_new, v_new, out, pos, B, Hq, Hkv, d, w, s, scale, conv,
                        workspace, workspace_bytes, stream);
+}
+
+int swa_append_decode_step_timed(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                                 float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,
+                                 float scale, int conv, void *workspace, size_t workspace_bytes, void *stream,
+                                 void *start_event, void *stop_event)
+{
+    const char *fn = "swa_append_decode_step_timed";
+    if (start_event == nullptr || stop_event == nullptr)
+        return fail(SWA_EINVAL, "%s: start_event and stop_event must not be null", fn);
+    CHECK_PTR(k_new);
+    CHECK_PTR(v_new);
+    return decode_impl(fn, q, k_cache, v_cache, k_new, v_new, out, pos, B, Hq, Hkv, d, w, s, scale, conv,
+                       workspace, workspace_bytes, stream, start_event, stop_event);
 }
 
 int swa_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w, int s, int conv, void *stream)

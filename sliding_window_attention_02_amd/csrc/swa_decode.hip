@@ -17,6 +17,7 @@
 #include "swa_device.h"
 #include "swa_launch.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace swa {
@@ -31,10 +32,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // LDS pointer in the local address space for the direct global -> LDS load (written inline:
 // a helper or an implicit conversion there makes the host pass drop the launch stub).
 #define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
-
-// V rows in LDS: 16-byte pieces XOR-swizzled so the transposed 8-byte reads of rows
-// r..r+3 (r = 0 mod 4) at pieces P, P+1 hit 8 distinct pieces.
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
 constexpr int kChunk = 32;      // slots per MFMA step
 constexpr int kMaxChunks = 3;   // slots per wave <= 96
@@ -167,7 +164,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             for (int i = 0; i < kLoads; ++i) {
                 const int r = kRowsPerLoad * i + lane / kPieces;
                 const int slot = min(c0 + r, last);
-                const int piece = (lane % kPieces) ^ swz_v(r);
+                const int piece = (lane % kPieces) ^ lds_swizzle<D>(r);
                 __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vcache + (size_t)slot * D + piece * 8),
                                                  SWA_LDS_PTR(&vlds[ch][1024 * i]), 16, 0, 0);
             }
@@ -180,7 +177,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     // cache write, both after V has landed).
     const SlotMap sm(t, a.s, a.w_loc);
     const int slot_t = t >= 0 ? sm.slot_of_t() : -1;
-    const bool wrapped = t >= (int64_t)a.s + a.w_loc - 1;  // every slot holds a position of A(t)
+    const bool wrapped = sm.wrapped();  // every slot holds a position of A(t)
     const bool owns_new = fused && slot_t >= seg_lo && slot_t < seg_hi;
     u32x4 kn_piece = {0u, 0u, 0u, 0u}, vn_piece = {0u, 0u, 0u, 0u};  // piece `lane` of the new rows
     if (owns_new) {
@@ -229,14 +226,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sj = c0 + 8 * g16 + 4 * kb + j;
-                    sacc[ch][kb][j] = ((sj < seg_hi) & sm.valid32(sj)) ? sacc[ch][kb][j] : -INFINITY;
+                    sacc[ch][kb][j] = sm.admits(sj, seg_hi, false) ? sacc[ch][kb][j] : -INFINITY;
                 }
         } else if (c0 + kChunk > seg_hi) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    sacc[ch][kb][j] = c0 + 8 * g16 + 4 * kb + j < seg_hi ? sacc[ch][kb][j] : -INFINITY;
+                    sacc[ch][kb][j] = sm.admits(c0 + 8 * g16 + 4 * kb + j, seg_hi, true) ? sacc[ch][kb][j] : -INFINITY;
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -283,7 +280,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 const int sj = c0 + kRowsPerLoad * i + lane / kPieces;
-                if (ch < nch && !((sj < seg_hi) & sm.valid32(sj)))
+                if (ch < nch && !sm.admits(sj, seg_hi, false))
                     *reinterpret_cast<u32x4 *>(&vlds[ch][1024 * i + 16 * lane]) = u32x4{0u, 0u, 0u, 0u};
             }
         }
@@ -297,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         const int r_end = slot_t == seg_hi - 1 ? kChunk : r + 1;
         for (int rr = r; rr < r_end; ++rr)
             *reinterpret_cast<u32x4 *>(&vlds[0][0] + ch * kChunk * kRowBytes + rr * kRowBytes +
-                                       16 * (lane ^ swz_v(rr))) = vn_piece;
+                                       16 * (lane ^ lds_swizzle<D>(rr))) = vn_piece;
     }
     const int vt_row0 = 8 * g16 + (c16 >> 2);
     const int vt_half = 8 * (c16 & 1);
@@ -316,7 +313,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int row = 4 * h + vt_row0;
-                const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ swz_v(row)) + vt_half;
+                const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ lds_swizzle<D>(row)) + vt_half;
                 const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s16x4 *)(&vlds[ch][off]));
                 const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -482,33 +479,68 @@ __global__ void kv_append_kernel(uint16_t *kc, uint16_t *vc, const uint16_t *kn,
     *reinterpret_cast<u32x4 *>(vc + dst) = *reinterpret_cast<const u32x4 *>(vn + src);
 }
 
-__global__ void debug_decode_slots_kernel(int64_t *slot_pos, const int64_t *pos, int B, int s, int w_loc)
+// Debug: what the decode step attends to.  For each (b, split) of the decode plan, every slot of
+// the split's segment goes through the kernel's own admission (SlotMap::admits: the wrap
+// shortcut, else the 32-bit validity test); slot_pos[b][j] = the position slot j holds (position
+// t at the slot the fused step writes, slot_of_t) if admitted, else -1.  Inconsistencies are
+// flagged instead: -2 for an admitted slot that holds no position of A(t), -3 for a slot that two
+// splits cover.  One thread per (b, split).
+__global__ void debug_decode_slots_kernel(int64_t *slot_pos, const int64_t *pos, int B, int s, int w_loc,
+                                          int n_split, int slots_per_split)
 {
     const int n_slots = s + w_loc;
-    const size_t total = (size_t)B * n_slots;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-        const int b = (int)(i / n_slots), j = (int)(i % n_slots);
-        slot_pos[i] = SlotMap(pos[b], s, w_loc).position(j);
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * n_split; i += gridDim.x * blockDim.x) {
+        const int b = i / n_split, split = i % n_split;
+        const SlotMap sm(pos[b], s, w_loc);
+        const bool wrap = sm.wrapped();
+        const int slot_t = pos[b] >= 0 ? sm.slot_of_t() : -1;
+        const int seg_lo = split * slots_per_split;
+        const int seg_hi = min(seg_lo + slots_per_split, n_slots);
+        const int nch = (seg_hi - seg_lo + kChunk - 1) / kChunk;
+        int64_t *out = slot_pos + (size_t)b * n_slots;
+        for (int sj = seg_lo; sj < seg_lo + nch * kChunk; ++sj) {
+            if (!sm.admits(sj, seg_hi, wrap))
+                continue;  // (rows past the segment are never admitted)
+            const int64_t p = sj == slot_t ? pos[b] : sm.position(sj);
+            out[sj] = out[sj] != -1 ? -3 : (sm.position(sj) < 0 ? -2 : p);
+        }
     }
 }
 
+__global__ void fill_i64_kernel(int64_t *p, size_t n, int64_t v)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// Launches kern; with start/stop events the dispatch itself stamps them (kernel-only timing).
+template <typename K>
+void launch_timed(K kern, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                  const DecodeArgs &a)
+{
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kern, grid, block, 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, a);
+}
+
 template <int D>
-void launch_decode_d(const DecodeArgs &a, int wg_waves, int B, hipStream_t stream)
+void launch_decode_d(const DecodeArgs &a, int wg_waves, int B, hipStream_t stream, hipEvent_t start, hipEvent_t stop)
 {
     const dim3 grid(a.n_split / wg_waves, a.Hkv * a.n_hslices, B);
     const int nch = (a.slots_per_split + kChunk - 1) / kChunk;
     if (wg_waves == 2)
-        hipLaunchKernelGGL((decode_kernel<D, 1, 2>), grid, dim3(128), 0, stream, a);
+        launch_timed(decode_kernel<D, 1, 2>, grid, dim3(128), stream, start, stop, a);
     else if (wg_waves == 3)
-        hipLaunchKernelGGL((decode_kernel<D, 1, 3>), grid, dim3(192), 0, stream, a);
+        launch_timed(decode_kernel<D, 1, 3>, grid, dim3(192), stream, start, stop, a);
     else if (wg_waves == 4)
-        hipLaunchKernelGGL((decode_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a);
+        launch_timed(decode_kernel<D, 1, 4>, grid, dim3(256), stream, start, stop, a);
     else if (nch <= 1)
-        hipLaunchKernelGGL((decode_kernel<D, 1, 1>), grid, dim3(64), 0, stream, a);
+        launch_timed(decode_kernel<D, 1, 1>, grid, dim3(64), stream, start, stop, a);
     else if (nch == 2)
-        hipLaunchKernelGGL((decode_kernel<D, 2, 1>), grid, dim3(64), 0, stream, a);
+        launch_timed(decode_kernel<D, 2, 1>, grid, dim3(64), stream, start, stop, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, 3, 1>), grid, dim3(64), 0, stream, a);
+        launch_timed(decode_kernel<D, 3, 1>, grid, dim3(64), stream, start, stop, a);
 }
 
 }  // namespace
@@ -569,8 +601,10 @@ hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, con
 
 hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                          float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
-                         float scale, void *workspace, const DecodePlan &plan, hipStream_t stream)
+                         float scale, void *workspace, const DecodePlan &plan, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop)
 {
+    const bool merged = plan.n_split != plan.wg_waves;  // a second kernel merges the splits
     DecodeArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.kc = static_cast<uint16_t *>(k_cache);
@@ -591,18 +625,20 @@ hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void
     a.n_split = plan.n_split;
     a.slots_per_split = plan.slots_per_split;
     a.scale_log2 = scale * 1.4426950408889634f;
+    // With a merge, the decode kernel stamps the start and the merge kernel the end.
     if (d == 128)
-        launch_decode_d<128>(a, plan.wg_waves, B, stream);
+        launch_decode_d<128>(a, plan.wg_waves, B, stream, start, merged ? nullptr : stop);
     else
-        launch_decode_d<64>(a, plan.wg_waves, B, stream);
+        launch_decode_d<64>(a, plan.wg_waves, B, stream, start, merged ? nullptr : stop);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.n_split == plan.wg_waves)
+    if (e != hipSuccess || !merged)
         return e;
-    if (d == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, dim3(Hq, B), dim3(kMergeThreads), 0, stream, a.ws, out, Hq,
-                           plan.n_split);
+    auto merge = d == 128 ? merge_kernel<128> : merge_kernel<64>;
+    if (stop != nullptr)
+        hipExtLaunchKernelGGL(merge, dim3(Hq, B), dim3(kMergeThreads), 0, stream, nullptr, stop, 0,
+                              (const float *)a.ws, out, Hq, plan.n_split);
     else
-        hipLaunchKernelGGL(merge_kernel<64>, dim3(Hq, B), dim3(kMergeThreads), 0, stream, a.ws, out, Hq,
+        hipLaunchKernelGGL(merge, dim3(Hq, B), dim3(kMergeThreads), 0, stream, (const float *)a.ws, out, Hq,
                            plan.n_split);
     return hipGetLastError();
 }
@@ -620,7 +656,15 @@ ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s)
 hipError_t launch_debug_decode_slots(int64_t *slot_pos, const int64_t *pos, int B, int w_loc, int s,
                                      hipStream_t stream)
 {
-    hipLaunchKernelGGL(debug_decode_slots_kernel, dim3(64), dim3(256), 0, stream, slot_pos, pos, B, s, w_loc);
+    // The split geometry depends on the slot count only (heads and d pick the head slices).
+    const DecodePlan plan = decode_plan(B, 1, 1, 128, w_loc, s);
+    const size_t n = (size_t)B * plan.n_slots;
+    hipLaunchKernelGGL(fill_i64_kernel, dim3(64), dim3(256), 0, stream, slot_pos, n, (int64_t)-1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(debug_decode_slots_kernel, dim3(64), dim3(256), 0, stream, slot_pos, pos, B, s, w_loc,
+                       plan.n_split, plan.slots_per_split);
     return hipGetLastError();
 }
 

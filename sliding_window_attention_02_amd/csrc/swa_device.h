@@ -14,8 +14,11 @@
 
 namespace swa {
 
+// The walk and index functions below run in the kernels and on the host (work accounting).
+#define SWA_HD __host__ __device__ __forceinline__
+
 // Element predicate of A(t).
-__device__ __forceinline__ bool key_allowed(int t, int i, int w_loc, int s)
+SWA_HD bool key_allowed(int t, int i, int w_loc, int s)
 {
     return i <= t && (i > t - w_loc || i < s);
 }
@@ -30,11 +33,11 @@ struct TileWalk {
     int n_sink;  // tiles 0 .. n_sink-1 hold sinks below the window
     int win_lo;  // first window tile
     int win_hi;  // last window tile
-    __device__ __forceinline__ int count() const { return n_sink + (win_hi - win_lo + 1); }
-    __device__ __forceinline__ int tile(int n) const { return n < n_sink ? n : win_lo + (n - n_sink); }
+    SWA_HD int count() const { return n_sink + (win_hi - win_lo + 1); }
+    SWA_HD int tile(int n) const { return n < n_sink ? n : win_lo + (n - n_sink); }
 };
 
-__device__ __forceinline__ TileWalk plan_tiles(int t0, int t1, int w_loc, int s, int tile_n)
+SWA_HD TileWalk plan_tiles(int t0, int t1, int w_loc, int s, int tile_n)
 {
     TileWalk tw;
     const int lo = (t0 - w_loc + 1 > 0) ? t0 - w_loc + 1 : 0;  // first window key of token t0
@@ -52,8 +55,8 @@ __device__ __forceinline__ TileWalk plan_tiles(int t0, int t1, int w_loc, int s,
 // its edge tiles, visited in walk order by edge_tile(i), i < n_edge.
 struct WalkSplit {
     int mid_lo, mid_hi, n_edge;
-    __device__ __forceinline__ int n_mid() const { return mid_hi >= mid_lo ? mid_hi - mid_lo + 1 : 0; }
-    __device__ __forceinline__ int edge_tile(const TileWalk &tw, int i) const
+    SWA_HD int n_mid() const { return mid_hi >= mid_lo ? mid_hi - mid_lo + 1 : 0; }
+    SWA_HD int edge_tile(const TileWalk &tw, int i) const
     {
         if (i < tw.n_sink)
             return i;
@@ -64,7 +67,7 @@ struct WalkSplit {
     }
 };
 
-__device__ __forceinline__ WalkSplit split_walk(const TileWalk &tw, int t0, int t1, int w_loc, int tile_n)
+SWA_HD WalkSplit split_walk(const TileWalk &tw, int t0, int t1, int w_loc, int tile_n)
 {
     WalkSplit sp;
     const int lo = t1 - w_loc + 1;  // first key inside the window of t1
@@ -82,11 +85,11 @@ __device__ __forceinline__ WalkSplit split_walk(const TileWalk &tw, int t0, int 
 struct ChunkWalk {
     int n_sink;          // chunks 0 .. n_sink-1 (sinks below the window)
     int win_lo, win_hi;  // window chunks
-    __device__ __forceinline__ int count() const { return n_sink + (win_hi - win_lo + 1); }
-    __device__ __forceinline__ int chunk(int k) const { return k < n_sink ? k : win_lo + (k - n_sink); }
+    SWA_HD int count() const { return n_sink + (win_hi - win_lo + 1); }
+    SWA_HD int chunk(int k) const { return k < n_sink ? k : win_lo + (k - n_sink); }
 };
 
-__device__ __forceinline__ ChunkWalk plan_chunks(int t0, int t1, int w_loc, int s, int chunk_n)
+SWA_HD ChunkWalk plan_chunks(int t0, int t1, int w_loc, int s, int chunk_n)
 {
     ChunkWalk cw;
     const int lo = (t0 - w_loc + 1 > 0) ? t0 - w_loc + 1 : 0;
@@ -104,8 +107,7 @@ __device__ __forceinline__ ChunkWalk plan_chunks(int t0, int t1, int w_loc, int 
 // chunks outside the range are skipped, loads and exp alike.
 constexpr int kChunkN = 32;
 
-__device__ __forceinline__ void tile_chunks(int j0, int n_chunks, int t0, int t1, int w_loc, int s,
-                                            int &c_lo, int &c_hi)
+SWA_HD void tile_chunks(int j0, int n_chunks, int t0, int t1, int w_loc, int s, int &c_lo, int &c_hi)
 {
     const int lo = (t0 - w_loc + 1 > 0) ? t0 - w_loc + 1 : 0;
     const int sink_end = s < t1 + 1 ? s : t1 + 1;
@@ -123,12 +125,72 @@ __device__ __forceinline__ void tile_chunks(int j0, int n_chunks, int t0, int t1
 
 // True when every (t, i) with t in [t0, t1] and i in [k_lo, k_hi] is allowed, so those
 // keys need no element mask.
-__device__ __forceinline__ bool range_mask_free(int k_lo, int k_hi, int t0, int t1, int w_loc, int s)
+SWA_HD bool range_mask_free(int k_lo, int k_hi, int t0, int t1, int w_loc, int s)
 {
     const bool causal = k_hi <= t0;
     const bool in_window = k_lo > t1 - w_loc;
     const bool all_sinks = k_hi < s;
     return causal && (in_window || all_sinks);
+}
+
+// Key tile of the main prefill walk: first key, needed chunk range, and whether every visited
+// (query, key) pair is allowed (then no element mask is applied).
+struct TileInfo {
+    int j0, c_lo, c_hi;
+    int mask_free;  // (an int: a bool member would leave padding that the copies carry)
+    SWA_HD bool full() const { return c_lo == 0 && c_hi == 1 && mask_free; }
+};
+
+SWA_HD TileInfo tile_info(int tile, int tile_n, int t0, int t1, int w_loc, int s)
+{
+    TileInfo ti;
+    ti.j0 = tile * tile_n;
+    tile_chunks(ti.j0, tile_n / kChunkN, t0, t1, w_loc, s, ti.c_lo, ti.c_hi);
+    ti.mask_free = range_mask_free(ti.j0 + ti.c_lo * kChunkN, ti.j0 + ti.c_hi * kChunkN + kChunkN - 1, t0, t1,
+                                   w_loc, s);
+    return ti;
+}
+
+// Resident prefill forms: chunk slot k of a workgroup whose chunk walk is cw holds the keys
+// resident_slot_key0(cw, k) + r, r < kChunkN (rows past the sequence hold its last key).
+SWA_HD int resident_slot_key0(const ChunkWalk &cw, int k) { return cw.chunk(k) * kChunkN; }
+
+// The wide resident form takes its q-tile as 32-token halves [h0, h1], each over its own four-chunk
+// walk hw; slot[k] is the workgroup slot holding chunk hw.chunk(k).  A chunk the half needs is one
+// the workgroup needs, so it has a slot: below cw.n_sink the sink slots, else the window slot
+// counted from cw.win_lo.  A chunk past the half's needs may have none (its keys are after the
+// half's last token, so the element mask removes them whatever the slot holds): it takes the last
+// slot.
+SWA_HD void resident_half_slots(const ChunkWalk &cw, int h0, int h1, int w_loc, int s, int n_slots,
+                               ChunkWalk &hw, int (&slot)[4])
+{
+    hw = plan_chunks(h0, h1, w_loc, s, kChunkN);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int ch = hw.chunk(k);
+        const int sl = ch < cw.n_sink ? ch : cw.n_sink + (ch - cw.win_lo);
+        slot[k] = sl < 0 ? 0 : (sl > n_slots - 1 ? n_slots - 1 : sl);
+    }
+}
+
+// ---------------------------------------------------------------------------- LDS layout
+//
+// K and V rows staged in LDS keep their 16-byte pieces XOR-swizzled (physical piece = logical
+// piece ^ lds_swizzle(row)) so that the MFMA fragment reads are free of bank conflicts (64
+// banks of 4 bytes; a 16-byte read serves 16 lanes per pass, an 8-byte read 32):
+//   * K fragment: lanes 0-15 read logical piece P of rows 8a + b + c (a, b = 0..3; c a constant
+//     with bits 2 and 5 only), which land in 16 distinct 16-byte bank groups;
+//   * V^T fragment (transposed 8-byte reads): lanes 0-15 read pieces P, P+1 (P even) of rows
+//     r .. r+3 and lanes 16-31 those of rows r+8 .. r+11 (r = 0 mod 4): the row bits 0-1 spread
+//     each quad over 8 distinct pieces and row bit 3 moves the second quad to the other half of
+//     the banks (d = 128: piece bit 3; d = 64, two rows per 256-byte bank line: piece bit 1).
+// The swizzle ignores row bits 2 and 5, so a fragment's offset is a per-lane base plus an
+// immediate for the 4-row and 32-row steps.  K and V share it, so their loads share offsets.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int r)
+{
+    const int quad = (r & 3) ^ (((r >> 3) & 1) << (D == 128 ? 2 : 0));
+    return ((r >> 4) & 1) | (quad << 1);
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -186,6 +248,16 @@ struct SlotMap {
     }
     // slot of position t itself (t >= 0)
     __device__ __forceinline__ int slot_of_t() const { return t < s ? (int)t : s + t_mod; }
+    // Once the ring has wrapped (t >= s + w_loc - 1) every slot holds a position of A(t).
+    __device__ __forceinline__ bool wrapped() const { return t >= (int64_t)s + w_loc - 1; }
+    // Whether the decode step attends to slot j of a split segment ending at seg_hi (rows past the
+    // segment repeat its last slot): after the wrap every slot of the segment, before it the
+    // slots that valid32 admits.  `wrap` is wrapped(), passed in so that a caller branching on
+    // it gets straight-line code in each branch.
+    __device__ __forceinline__ bool admits(int j, int seg_hi, bool wrap) const
+    {
+        return (j < seg_hi) & (wrap | valid32(j));
+    }
 };
 
 }  // namespace swa

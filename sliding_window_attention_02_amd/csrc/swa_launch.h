@@ -23,6 +23,18 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
 // then the prefill keeps all of a q-tile's keys in LDS at once (the resident form).
 bool prefill_resident(int Tm, int q_lo, int w_loc, int s);
 
+// What launch_prefill launches for a whole-sequence prefill: the kernel form (0 tile walk,
+// 1 resident, 2 wide resident), the geometry as launched (Tm doubled in the wide form), the grid,
+// and the (query row, key) pairs whose scores and value products the matrix cores compute (rows of
+// a workgroup times the keys of the tiles or chunks it visits, padding rows included).
+struct PrefillPlan {
+    int form;
+    PrefillGeometry g;
+    long long workgroups;
+    long long executed_pairs;
+};
+PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s);
+
 // Chunked prefill: the first n_cached of the L keys are read from a sink+ring cache
 // [B][Hkv][s + w_loc][d] (key j < ns: sink slot j; key j >= ns: ring slot
 // s + (ring0 + j - ns) mod w_loc), the rest from k and v, which hold L - n_cached rows; only
@@ -60,10 +72,12 @@ hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, con
                             hipStream_t stream, int64_t pos0 = 0);
 
 // k_new / v_new: null for a plain decode step; otherwise the new token of each sequence
-// ([B][Hkv][d]) is written to its slot and attended in the same launch.
+// ([B][Hkv][d]) is written to its slot and attended in the same launch.  start/stop: optional
+// events stamped by the dispatches themselves (the first kernel's start, the last kernel's end).
 hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                          float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w_loc, int s,
-                         float scale, void *workspace, const DecodePlan &plan, hipStream_t stream);
+                         float scale, void *workspace, const DecodePlan &plan, hipStream_t stream,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // ----------------------------------------------------------------------- chunked prefill
 //

@@ -1,8 +1,8 @@
 // swa_model.hip -- the decoder-layer pieces around SWA(w,s) decode: RMSNorm and a streaming
 // bf16 matrix-vector product for small batches with fused epilogues.
 //
-// They exist for the multi-layer decode measurement the pages describe (page "滑动窗口注意力
-// （SWA）配 sinks 比 post-training 线性注意力更划算", section "小窗口也有工程优势": decode
+// They exist for the multi-layer decode measurement the pages describe (page "几亿Token白练了？
+// 微软实测：免训练滑动窗口，让线性注意力破防" (PaperWeekly), section "小窗口也有工程优势": decode
 // throughput and state memory of a 4-layer Transformer at batch 1 from 128 to 256K tokens of
 // context).  The layer recipe (pre-norm, GQA attention, SwiGLU MLP) is the standard one; the
 // pages fix none of it.

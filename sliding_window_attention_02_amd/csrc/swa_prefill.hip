@@ -49,6 +49,7 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace swa {
@@ -90,18 +91,6 @@ struct Lds {
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 64-lane 16-byte load fills
     static constexpr int kLoadsPerTile = kTileBytes / 1024;
 };
-
-// XOR swizzles of the 16-byte pieces of a row (physical piece = logical piece ^ swizzle).
-// K: the 16 rows one S^T fragment read touches (32*kc + 8a + 4h + b, a, b = 0..3) get 16
-// distinct swizzles, so the 16-byte reads of any 8 or 16 consecutive lanes hit distinct
-// bank groups.  V: the transposed 8-byte reads take rows r..r+3 (r = 0 mod 4) at pieces
-// P, P+1 (P even); swizzles 0, 2, 4, 6 spread them over 8 distinct pieces.
-template <int D>
-__device__ __forceinline__ int swz_k(int r)
-{
-    return D == 128 ? ((((r >> 3) & 3) << 2) | (r & 3)) : ((((r >> 3) & 1) << 2) | (r & 3));
-}
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
 // Maximum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one query column,
 // with the gfx950 cross-row swaps (VALU only, no LDS round trip).  permlane32_swap on (x, x)
@@ -173,13 +162,6 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
     c.b = rest / a.Hkv;
     return c;
 }
-
-// Key tile of the walk: first key, needed chunk range, and whether no element mask is needed.
-struct TileInfo {
-    int j0, c_lo, c_hi;
-    int mask_free;  // (an int: a bool member would leave padding that the copies carry)
-    __device__ __forceinline__ bool full() const { return c_lo == 0 && c_hi == 1 && mask_free; }
-};
 
 // FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots), 2 wide resident
 // (64-token q-tiles taken as two 32-token halves per wave, five chunk slots).
@@ -271,32 +253,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     // last row (finite values; such keys are always masked).
     // The wave index as a uniform (scalar) value: the LDS destinations (M0) are then scalar.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t ld_koff[kLoadsPerWave], ld_voff[kLoadsPerWave];  // byte offsets from the tile's first row
+    uint32_t ld_off[kLoadsPerWave];  // byte offsets from the tile's first row (K and V alike)
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int row = kRowsPerLoad * (wave * kLoadsPerWave + i) + lane / kPieces;
         const int phys = lane % kPieces;
-        ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
-        ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
+        ld_off[i] = (uint32_t)(row * kv_row + (phys ^ lds_swizzle<D>(row)) * 8) * 2u;
     }
     // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf
     // (buf 2: the wide form's fifth chunk slot, which holds tile rows 0 .. 31, so only waves 0
     // and 1 load into it).
+    // Buffer resources over this (b, kv-head)'s rows of k and v (fewer than 2^32 bytes: one
+    // sequence of q holds fewer than 2^31 elements and Hkv <= Hq), for the loads of whole tiles:
+    // the tile's byte offset is a scalar operand and each lane adds its 32-bit offset, so a load
+    // costs no vector address arithmetic.
+    const uint32_t kv_bytes = (uint32_t)(((size_t)L_in * a.Hkv - bc.hkv) * D * 2);
+    const __amdgpu_buffer_rsrc_t k_rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kbase), 0, (int)kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vbase), 0, (int)kv_bytes, 0x00020000);
     auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
         constexpr int kv = decltype(kv_c)::value;
         const uint16_t *base = kv ? vbase : kbase;
         const int last = a.L - 1;
         if (j0 >= a.n_cached && j0 + kTileN - 1 <= last) {
-            // Every row of the tile is a key of k/v inside the sequence: a scalar tile base plus
-            // the per-lane offsets.
-            const char *tile0 = reinterpret_cast<const char *>(base + (size_t)(j0 - a.n_cached) * kv_row);
+            // Every row of the tile is a key of k/v inside the sequence.
+            const int tile_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - a.n_cached) * (uint32_t)kv_row * 2u));
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int j = wave_u * kLoadsPerWave + i;
-                // (the builtin takes a non-const global pointer; the source is only read)
-                __builtin_amdgcn_global_load_lds(const_cast<char *>(tile0 + (kv ? ld_voff[i] : ld_koff[i])),
-                                                 SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
-                                                 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs,
+                                                         SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
+                                                         16, (int)ld_off[i], tile_off, 0, 0);
             }
             return;
         }
@@ -304,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int j = wave_u * kLoadsPerWave + i;
             const int row = kRowsPerLoad * j + lane / kPieces;
-            const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
+            const int piece = (lane % kPieces) ^ lds_swizzle<D>(row);
             const int key = min(j0 + row, last);
             const uint16_t *src;
             if (key >= a.n_cached) {
@@ -328,24 +316,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     using VRows = std::integral_constant<int, 1>;
     // LDS read offsets (bytes, within a tile) that do not depend on the tile.
     // K fragment (kc, h, kk): row 32kc + 4h + r with r = 8(c16/4) + c16%4, logical piece
-    // 4kk + g16.  Adding 32kc + 4h to r changes neither r % 4 nor (r / 8) % 4, so the row's
+    // 4kk + g16.  Adding 32kc + 4h to r sets only row bits 2 and 5, which the swizzle ignores, so the row's
     // swizzle is that of r: the offset is k_lane[kk] plus the constant (32kc + 4h) * kRowBytes.
     int k_lane[kKSteps];
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
         const int r = 8 * (c16 >> 2) + (c16 & 3);
-        k_lane[kk] = r * kRowBytes + 16 * ((4 * kk + g16) ^ swz_k<D>(r));
+        k_lane[kk] = r * kRowBytes + 16 * ((4 * kk + g16) ^ lds_swizzle<D>(r));
     }
     // V^T fragment (db, kc) from two transposed 8-byte reads (h = 0, 1): lane 16g + s reads
     // row 32kc + 4h + 8g + s/4 at d = 16db + 4(s%4) .. +3 (byte 8(s%2) of logical piece
     // 2db + (s/2)%2); the read hands lane s the values at d = 16db + s of the four rows
-    // 32kc + 4h + 8g .. +3.  The row's swizzle is 2(s/4) whatever kc, h, and XOR with an even
-    // swizzle keeps the low piece bit, so the physical piece is 2(db ^ s/4) + (s/2)%2 and the
-    // offset is v_lane[db % 4] plus the constant (32kc + 4h) * kRowBytes + 32 (db - db % 4).
-    int v_lane[4];
+    // 32kc + 4h + 8g .. +3.  The swizzle does not see row bits 2 and 5, so the offset is
+    // v_lane[db] plus the constant (32kc + 4h) * kRowBytes.
+    int v_lane[kDBlocks];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        v_lane[m] = (8 * g16 + (c16 >> 2)) * kRowBytes + 32 * (m ^ (c16 >> 2)) + 16 * ((c16 >> 1) & 1) + 8 * (c16 & 1);
+    for (int db = 0; db < kDBlocks; ++db) {
+        const int r = 8 * g16 + (c16 >> 2);
+        v_lane[db] = r * kRowBytes + 16 * ((2 * db + ((c16 >> 1) & 1)) ^ lds_swizzle<D>(r)) + 8 * (c16 & 1);
+    }
 
     f32x4 o[kDBlocks][2];
 #pragma unroll
@@ -379,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
             if ((wave_u >> 1) == (k & 1)) {
-                const int j0 = cw.chunk(k) * kChunkN - (k & 1) * kChunkN;  // tile row 0 holds key j0
+                const int j0 = resident_slot_key0(cw, k) - (k & 1) * kChunkN;  // tile row 0 holds key j0
                 issue(j0, k >> 1, KRows());
                 issue(j0, k >> 1, VRows());
             }
@@ -463,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     bf16x8 af;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int off = v_lane[db & 3] + 4 * h * kRowBytes + 32 * (db & ~3);
+                        const int off = v_lane[db] + 4 * h * kRowBytes;
                         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(vt + off));
                         const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -485,18 +474,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             pass(std::integral_constant<int, 0>(), cw, slot);
             pass(std::integral_constant<int, 1>(), cw, slot);
         } else {
-            // The two 32-token halves of the q-tile, each with its own chunk walk.  A chunk the half
-            // needs is one the workgroup needs, so it has a slot: below cw.n_sink the sink slots,
-            // else the window slot counted from cw.win_lo.  A chunk past the half's needs may have
-            // none (its keys are masked whatever the slot holds): it takes the last slot.
+            // The two 32-token halves of the q-tile, each with its own chunk walk and slot map.
             auto half = [&](int h0, ChunkWalk &hw, int(&slot)[4]) __attribute__((always_inline)) {
-                hw = plan_chunks(h0, min(h0 + kChunkN - 1, t1), a.w_loc, a.s, kChunkN);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int ch = hw.chunk(k);
-                    const int sl = ch < cw.n_sink ? ch : cw.n_sink + (ch - cw.win_lo);
-                    slot[k] = min(max(sl, 0), kSlots - 1);
-                }
+                resident_half_slots(cw, h0, min(h0 + kChunkN - 1, t1), a.w_loc, a.s, kSlots, hw, slot);
             };
             ChunkWalk hw;
             int slot[4];
@@ -513,12 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
         const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
         auto tile_info = [&](int tile) __attribute__((always_inline)) {
-            TileInfo ti;
-            ti.j0 = tile * kTileN;
-            tile_chunks(ti.j0, 2, t0, t1, a.w_loc, a.s, ti.c_lo, ti.c_hi);
-            ti.mask_free = range_mask_free(ti.j0 + ti.c_lo * kChunkN, ti.j0 + ti.c_hi * kChunkN + kChunkN - 1, t0, t1,
-                                           a.w_loc, a.s);
-            return ti;
+            return swa::tile_info(tile, kTileN, t0, t1, a.w_loc, a.s);
         };
 
         // The steps below take `fast` as a compile-time flag: a fast tile has both chunks needed and
@@ -639,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     bf16x8 af;
     #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
+                        const int off = v_lane[db] + (kc * kChunkN + 4 * h) * kRowBytes;
                         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(vt + off));
                         const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -780,47 +755,58 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 }
 
-// Debug: the set of (query, key) pairs the prefill kernel admits, from the same tile walk and
-// split: edge tiles through the chunk selection, mask-free classification and element
-// predicate; middle tiles whole and unmasked, as the kernel takes them.  One workgroup per
-// q-tile.
-__global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int resident, int w_loc, int s)
+// Debug: how often the prefill kernel of form `form` (q-tiles of Tm tokens as launched) attends
+// each (query, key) pair: mask[t][key] counts the visits in which the kernel's walk and element
+// mask admit the pair, recorded at the key the visited LDS row actually holds.  The walks are the
+// kernel's own device functions: for the main form the edge tiles (chunk selection, mask-free
+// classification, element predicate) and the middle tiles (whole, unmasked); for the resident
+// forms the chunk walk with its slot contents and, in the wide form, each 32-token half's walk
+// and slot map.  A correct kernel gives exactly 1 on A(t) and 0 elsewhere.  One workgroup per
+// q-tile, one thread per query (no two threads write one row).
+__global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int form, int w_loc, int s)
 {
     const int t0 = blockIdx.x * Tm;
     const int t1 = min(t0 + Tm - 1, L - 1);
-    if (resident) {  // the resident form's chunk walk, every chunk element-masked
+    const int t = t0 + (int)threadIdx.x;
+    if (t > t1)
+        return;
+    uint8_t *row = mask + (size_t)t * L;
+    auto visit = [&](int key, bool admitted) {  // a key as the kernel computes it; LDS holds min(key, L-1)
+        if (admitted)
+            ++row[min(key, L - 1)];
+    };
+    if (form != 0) {
         const ChunkWalk cw = plan_chunks(t0, t1, w_loc, s, kChunkN);
-        for (int k = 0; k < cw.count(); ++k) {
-            const int k_lo = cw.chunk(k) * kChunkN;
-            for (int idx = threadIdx.x; idx < Tm * kChunkN; idx += blockDim.x) {
-                const int t = t0 + idx / kChunkN;
-                const int key = k_lo + idx % kChunkN;
-                if (t <= t1 && key < L && key_allowed(t, key, w_loc, s))
-                    mask[(size_t)t * L + key] = 1;
-            }
+        // The 32-token half holding t (the resident form's q-tile is a single half over the slots
+        // 0..3 in walk order).
+        ChunkWalk hw = cw;
+        int slot[4] = {0, 1, 2, 3};
+        if (form == 2) {
+            const int h0 = t0 + ((t - t0) / kChunkN) * kChunkN;
+            resident_half_slots(cw, h0, min(h0 + kChunkN - 1, t1), w_loc, s, 5, hw, slot);
         }
+        for (int k = 0; k < 4; ++k)
+            for (int r = 0; r < kChunkN; ++r) {
+                const int key = hw.chunk(k) * kChunkN + r;  // the key the element mask tests
+                const int held = resident_slot_key0(cw, slot[k]) + r;  // the key slot[k] holds
+                if (key_allowed(t, key, w_loc, s))
+                    ++row[min(held, L - 1)];
+            }
         return;
     }
     const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
     const WalkSplit sp = split_walk(tw, t0, t1, w_loc, kTileN);
-    for (int n = 0; n < tw.count(); ++n) {
-        const bool middle = n >= sp.n_edge;
-        const int j0 = (middle ? sp.mid_lo + (n - sp.n_edge) : sp.edge_tile(tw, n)) * kTileN;
-        int c_lo = 0, c_hi = kTileN / kChunkN - 1;
-        if (!middle)
-            tile_chunks(j0, kTileN / kChunkN, t0, t1, w_loc, s, c_lo, c_hi);
-        const int k_lo = j0 + c_lo * kChunkN, k_hi = j0 + c_hi * kChunkN + kChunkN - 1;
-        const bool mask_free = middle || range_mask_free(k_lo, k_hi, t0, t1, w_loc, s);
-        const int width = k_hi - k_lo + 1;
-        for (int idx = threadIdx.x; idx < Tm * width; idx += blockDim.x) {
-            const int t = t0 + idx / width;
-            const int key = k_lo + idx % width;
-            if (t > t1 || key >= L)
-                continue;
-            if (mask_free || key_allowed(t, key, w_loc, s))
-                mask[(size_t)t * L + key] = 1;
-        }
+    for (int i = 0; i < sp.n_edge; ++i) {
+        const TileInfo ti = tile_info(sp.edge_tile(tw, i), kTileN, t0, t1, w_loc, s);
+        for (int c = ti.c_lo; c <= ti.c_hi; ++c)
+            for (int r = 0; r < kChunkN; ++r) {
+                const int key = ti.j0 + c * kChunkN + r;
+                visit(key, ti.mask_free || key_allowed(t, key, w_loc, s));
+            }
     }
+    for (int tile = sp.mid_lo; tile < sp.mid_lo + sp.n_mid(); ++tile)
+        for (int r = 0; r < kTileN; ++r)
+            visit(tile * kTileN + r, true);
 }
 
 __global__ void fill_zero_kernel(uint8_t *p, size_t n)
@@ -869,6 +855,39 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
     g.n_hslices = g.G / g.Gw;
     g.n_qtiles = (L + g.Tm - 1) / g.Tm;
     return g;
+}
+
+PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
+{
+    PrefillPlan p;
+    p.g = prefill_geometry(L, Hq, Hkv);
+    p.form = prefill_form(p.g, 0, w_loc, s);
+    if (p.form == 2) {
+        p.g.Tm *= 2;
+        p.g.n_qtiles = (L + p.g.Tm - 1) / p.g.Tm;
+    }
+    const long long per_tile_group = (long long)B * Hkv * p.g.n_hslices;  // workgroups per q-tile
+    p.workgroups = per_tile_group * p.g.n_qtiles;
+    long long keys = 0;  // summed over the q-tiles: keys whose products one row of the tile computes
+    for (int qt = 0; qt < p.g.n_qtiles; ++qt) {
+        const int t0 = qt * p.g.Tm, t1 = std::min(t0 + p.g.Tm - 1, L - 1);
+        if (p.form == 1) {
+            keys += 4 * kChunkN;  // four chunk slots per pass
+        } else if (p.form == 2) {
+            keys += (t0 + kChunkN <= t1 ? 2 : 1) * 4 * kChunkN;  // each 32-token half: four chunks
+        } else {
+            const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
+            const WalkSplit sp = split_walk(tw, t0, t1, w_loc, kTileN);
+            for (int i = 0; i < sp.n_edge; ++i) {
+                const TileInfo ti = tile_info(sp.edge_tile(tw, i), kTileN, t0, t1, w_loc, s);
+                keys += (long long)(ti.c_hi - ti.c_lo + 1) * kChunkN;
+            }
+            keys += (long long)sp.n_mid() * kTileN;
+        }
+    }
+    // Rows per pass: 128 (the wide form's halves are passes of 128 rows each).
+    p.executed_pairs = per_tile_group * keys * kRowsPerBlock;
+    return p;
 }
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
@@ -928,14 +947,17 @@ hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int 
                                      hipStream_t stream)
 {
     (void)d;  // one tile geometry serves both head sizes
-    const PrefillGeometry g = prefill_geometry(L, Hq, Hkv);
+    // The geometry and form launch_prefill chooses for a whole-sequence prefill.
+    const PrefillPlan plan = prefill_plan(1, Hq, Hkv, L, w_loc, s);
+    const PrefillGeometry &g = plan.g;
+    const int form = plan.form;
     const size_t n = (size_t)L * L;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, mask, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(256), 0, stream, mask, L, g.Tm,
-                       prefill_resident(g.Tm, 0, w_loc, s) ? 1 : 0, w_loc, s);
+    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(kRowsPerBlock), 0, stream, mask, L, g.Tm,
+                       form, w_loc, s);
     return hipGetLastError();
 }
 

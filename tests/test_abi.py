@@ -124,10 +124,43 @@ def test_python_binding_refuses_cpu_tensors():
 
 
 def test_local_window_matches_convention():
+    """The binding takes the window convention from the library (swa_cache_slots)."""
+    assert binding.cache_slots(64, 4, binding.ADDITIVE) == 68
+    assert binding.cache_slots(64, 4, binding.TOTAL) == 64
     assert binding.local_window(64, 4, binding.ADDITIVE) == 64
     assert binding.local_window(64, 4, binding.TOTAL) == 60
-    with pytest.raises(ValueError):
+    with pytest.raises(binding.SwaError, match="no local window"):
         binding.local_window(4, 4, binding.TOTAL)
+    assert binding.lib().swa_cache_slots(0, 0, 0) == -1 and "w must be" in binding.last_error()
+
+
+def allowed_pairs(L, w_loc, s):
+    """sum_t |A(t)| = sum_t min(t + 1, w_loc + s)."""
+    return sum(min(t + 1, w_loc + s) for t in range(L))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,w,s,form,tm", [
+    (1, 32, 8, 4096, 64, 4, 2, 64),      # Llama SWA(64,4): wide resident, 64-token q-tiles
+    (4, 32, 8, 4096, 512, 4, 0, 32),     # sweep w=512: tile walk
+    (1, 32, 8, 16384, 4096, 4, 0, 32),   # Mistral w=4096: tile walk
+    (1, 8, 4, 500, 30, 2, 1, 64),        # two q-heads per kv-head, small window: resident
+    (2, 6, 6, 300, 64, 4, 0, 128),       # no GQA: 128-token q-tiles never fit four chunks
+])
+def test_prefill_describe_reports_the_launched_form(lib, B, Hq, Hkv, L, w, s, form, tm):
+    info = binding.prefill_describe(B, Hq, Hkv, L, 128, w, s)
+    assert info["form"] == form and info["tokens_per_tile"] == tm
+    assert info["workgroups"] == B * Hkv * (Hq // Hkv // info["heads_per_tile"]) * -(-L // tm)
+    # every allowed (query, key) pair of every head is computed at least once
+    assert info["executed_pairs"] >= B * Hq * allowed_pairs(L, w, s)
+    if form == 2:  # two halves of 128 rows x four 32-key chunks per workgroup (the last tile: one half)
+        assert info["executed_pairs"] == info["workgroups"] * 2 * 128 * 128
+
+
+def test_prefill_describe_rejects_on_host(lib):
+    info = binding._PrefillInfoC()
+    assert lib.swa_prefill_describe(1, 4, 2, 16, 128, 8, 4, 0, None) == binding.SWA_EINVAL
+    assert lib.swa_prefill_describe(1, 4, 2, 16, 96, 8, 4, 0, ctypes.byref(info)) == binding.SWA_EUNSUPPORTED
+    assert lib.swa_prefill_describe(1, 4, 2, 0, 128, 8, 4, 0, ctypes.byref(info)) == binding.SWA_EINVAL
 
 
 def test_prefill_timed_requires_events(lib):
@@ -143,6 +176,14 @@ def test_append_decode_step_rejects_on_host(lib):
     assert "k_new is null" in err(lib)
     assert f(A, A, A, A, MIS, A, A, 64, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EINVAL
     assert f(A, A, A, A, A, A, A, 64, 32, 8, 96, 64, 4, 0.1, 0, None, 0, None) == binding.SWA_EUNSUPPORTED
+
+
+def test_append_decode_step_timed_requires_events(lib):
+    args = (A, A, A, A, A, A, A, 1, 4, 2, 128, 8, 4, 0.1, 0, None, 0, None)
+    assert lib.swa_append_decode_step_timed(*args, None, A) == binding.SWA_EINVAL
+    assert "start_event and stop_event" in err(lib)
+    assert lib.swa_append_decode_step_timed(*args[:3], None, *args[4:], A, A) == binding.SWA_EINVAL
+    assert "k_new is null" in err(lib)
 
 
 def test_prefill_chunk_rejects_on_host(lib):

@@ -48,7 +48,10 @@ def test_workload_figures():
     assert acc.decode_kv_bytes(1, 8, 128, acc.decode_keys(262144, 64, 4)) == 278528
 
 
-def test_executed_pairs_cover_useful_pairs():
-    for L, Hq, Hkv, w, s in [(4096, 32, 8, 64, 4), (1000, 4, 4, 300, 0), (777, 12, 4, 64, 70)]:
-        useful = acc.pairs_per_head(L, w, s) * Hq
-        assert acc.prefill_executed_pairs(L, Hq, Hkv, w, s) >= useful
+def test_attainable_roofline():
+    # the Llama SWA(64,4) prefill is HBM-bound: 38.5 flop/byte x 8 TB/s
+    u, b = acc.useful_flops(1, 32, 4096, 128, 64, 4), acc.prefill_bytes(1, 4096, 32, 8, 128)
+    assert acc.attainable_tflops(u, b) == pytest.approx(u / b * 8.0)
+    # the Mistral-shaped one is MFMA-bound
+    u, b = acc.useful_flops(1, 32, 16384, 128, 4096, 4), acc.prefill_bytes(1, 16384, 32, 8, 128)
+    assert acc.attainable_tflops(u, b) == acc.PEAK_BF16_TFLOPS

@@ -33,8 +33,13 @@ def gpos(vals):
 # ------------------------------------------------------------------ slot map
 
 
-@pytest.mark.parametrize("w,s,conv", [(64, 4, 0), (16, 3, 0), (4, 0, 0), (20, 4, 1), (1, 5, 0), (7, 9, 0)])
+@pytest.mark.parametrize("w,s,conv", [(64, 4, 0), (16, 3, 0), (4, 0, 0), (20, 4, 1), (1, 5, 0), (7, 9, 0),
+                                      # wave splits at their limits (3 and 4 chunks), then workgroup splits
+                                      (96, 0, 0), (124, 4, 0), (125, 4, 0), (150, 4, 0), (300, 2, 0), (2000, 4, 0)])
 def test_decode_slot_map_equals_ring_simulation(w, s, conv):
+    """What the decode kernel's admission test (over the decode plan's split segments) admits at
+    each slot, and the slot the fused step writes, equal the ring simulation's contents: every
+    slot of A(t) exactly once, nothing else."""
     say("slots", w, s, conv)
     w_loc = orc.local_window(w, s, conv)
     ts = list(range(0, 300)) + [2 ** 18 - 1, 2 ** 18, 2 ** 18 + 67, 2 ** 18 + 255, 1_000_003]
@@ -118,7 +123,7 @@ def history(seed, T, B, Hq, Hkv, d, std=1.0, boost_n=4):
                                                  (5, 16, 1, 64, 5, 9, 0), (1, 32, 2, 128, 40, 2, 0),
                                                  # more slots than one workgroup holds: split + merge
                                                  (1, 8, 2, 128, 150, 4, 0), (2, 8, 4, 64, 200, 2, 0)])
-def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv):
+def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv, parity):
     say("decode-empty", B, Hq, Hkv, d, w, s, conv)
     T = 300
     qs, ks, vs = history(99, T, B, Hq, Hkv, d)
@@ -137,12 +142,13 @@ def test_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, conv):
     got = torch.stack(outs, dim=1).cpu().numpy()
     err = np.abs(got - ref)
     say(f"max {err.max():.3e}")
+    parity("decode from an empty cache (append, then decode)", err)
     assert np.isfinite(got).all() and err.max() <= TOL
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s", [(2, 4, 4, 64, 5, 0), (1, 8, 2, 128, 40, 0), (2, 8, 2, 128, 33, 0),
                                            (1, 8, 2, 128, 150, 0), (2, 4, 2, 64, 7, 3)])
-def test_fused_append_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s):
+def test_fused_append_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s, parity):
     """The fused step (append and attend in one launch) from a NaN-filled cache.  With s = 0
     and s + w_loc not a multiple of 32, the step that wraps the ring is the one that first
     writes the segment's last slot, which the rows past the segment also load."""
@@ -166,45 +172,111 @@ def test_fused_append_decode_from_empty_equals_prefill_rows(B, Hq, Hkv, d, w, s)
     assert np.isfinite(got).all() and err.max() <= TOL
 
 
-@pytest.mark.parametrize("B", [1, 64])
-def test_decode_workload_positions(B):
-    """SWA(64,4), Hq=32, Hkv=8, d=128 at positions 2^7 .. 2^18: the cache is seeded with the
-    state after P-1 (sinks and the last 64 positions), then decode steps t = P, P+1, ...
-    are checked against the oracle row t."""
+def seed_cache(kc, vc, known, lo, P, s, w, conv):
+    """Append the sinks 0..min(s, P)-1 and the window lo..P-1 (known[p] = (k, v) [B][Hkv][d])."""
+    B = kc.shape[0]
+    ns = min(s, P)
+    if ns > 0:
+        sk = torch.stack([known[p][0] for p in range(ns)], 1).cuda()
+        sv = torch.stack([known[p][1] for p in range(ns)], 1).cuda()
+        swa.kv_append(kc, vc, sk, sv, gpos([0] * B), w, s, conv)
+    if P > lo:
+        wk = torch.stack([known[p][0] for p in range(lo, P)], 1).cuda()
+        wv = torch.stack([known[p][1] for p in range(lo, P)], 1).cuda()
+        swa.kv_append(kc, vc, wk, wv, gpos([lo] * B), w, s, conv)
+
+
+DECODE_POINTS = inputs.decode_workloads()["decode_swa64_4_b64"].points
+
+
+@pytest.mark.parametrize("P", DECODE_POINTS)
+@pytest.mark.parametrize("B,fused,steps", [(1, False, None), (1, True, None), (64, True, None), (64, False, 24)])
+def test_decode_workload_positions(B, fused, steps, P, parity):
+    """The decode workload (SWA(64,4), Hq=32, Hkv=8, d=128) at every position point 2^7 .. 2^18:
+    the cache is seeded with the state after P-1 (sinks and the last 64 positions), then steps
+    t = P .. P+255 run back to back on the GPU (the benchmark's fused append+decode launch, or
+    kv_append + decode_step) and each is checked against the oracle row t of every sequence."""
     wl = inputs.decode_workloads()[f"decode_swa64_4_b{B}"]
-    steps = wl.steps if B == 1 else 24
+    steps = steps or wl.steps
     w_loc = orc.local_window(wl.w, wl.s, wl.conv)
     gen = dict(B=B, Hkv=wl.Hkv, d=wl.d, std=wl.std, sink_boost_n=wl.sink_boost_n, sink_boost=wl.sink_boost)
     ws = swa.alloc_workspace(B, wl.Hq, wl.Hkv, wl.d, wl.w, wl.s, wl.conv)
     worst = 0.0
-    for P in wl.points:
-        say("decode-point", B, P)
-        kc, vc = swa.alloc_cache(B, wl.Hkv, wl.d, wl.w, wl.s, wl.conv)
-        known = {}
-        for p in list(range(wl.s)) + list(range(P - w_loc - 2, P)):
-            known[p] = inputs.kv_at(wl.seed, p, **gen)
-        sk = torch.stack([known[p][0] for p in range(wl.s)], 1).cuda()
-        sv = torch.stack([known[p][1] for p in range(wl.s)], 1).cuda()
-        swa.kv_append(kc, vc, sk, sv, gpos([0] * B), wl.w, wl.s, wl.conv)
-        win = list(range(P - w_loc, P))
-        wk = torch.stack([known[p][0] for p in win], 1).cuda()
-        wv = torch.stack([known[p][1] for p in win], 1).cuda()
-        swa.kv_append(kc, vc, wk, wv, gpos([P - w_loc] * B), wl.w, wl.s, wl.conv)
-        for t in range(P, P + steps):
-            known[t] = inputs.kv_at(wl.seed, t, **gen)
-            known.pop(t - w_loc - 3, None)
-            pos = gpos([t] * B)
-            swa.kv_append(kc, vc, known[t][0][:, None].cuda(), known[t][1][:, None].cuda(), pos, wl.w, wl.s, wl.conv)
-            q = inputs.q_at(wl.seed, t, B, wl.Hq, wl.d, wl.std)
-            out = swa.decode_step(q.cuda(), kc, vc, pos, wl.w, wl.s, wl.scale, wl.conv, workspace=ws).cpu()
-            cand = sorted(known)
-            K = torch.stack([known[p][0] for p in cand], 1)
-            V = torch.stack([known[p][1] for p in cand], 1)
-            ref = orc.decode_rows(f64(q), cand, f64(K), f64(V), [t] * B, wl.w, wl.s, wl.scale, wl.conv)
-            err = float(np.abs(out.numpy() - ref).max())
-            worst = max(worst, err)
-            assert err <= TOL, (P, t, err)
+    assert P in wl.points
+    say("decode-point", B, fused, P)
+    kc, vc = swa.alloc_cache(B, wl.Hkv, wl.d, wl.w, wl.s, wl.conv)
+    lo = max(wl.s, P - w_loc)
+    cand = sorted(set(range(min(wl.s, P))) | set(range(lo, P)) | set(range(P, P + steps)))
+    known = {p: inputs.kv_at(wl.seed, p, **gen) for p in cand}
+    seed_cache(kc, vc, known, lo, P, wl.s, wl.w, wl.conv)
+    qs = torch.stack([inputs.q_at(wl.seed, t, B, wl.Hq, wl.d, wl.std) for t in range(P, P + steps)])
+    kn = torch.stack([known[t][0] for t in range(P, P + steps)]).cuda()
+    vn = torch.stack([known[t][1] for t in range(P, P + steps)]).cuda()
+    qg = qs.cuda()
+    out = torch.empty((steps, B, wl.Hq, wl.d), dtype=torch.float32, device="cuda")
+    for i in range(steps):
+        pos = gpos([P + i] * B)
+        if fused:
+            swa.append_decode_step(qg[i], kc, vc, kn[i], vn[i], pos, wl.w, wl.s, wl.scale, wl.conv,
+                                   out=out[i], workspace=ws)
+        else:
+            swa.kv_append(kc, vc, kn[i][:, None].contiguous(), vn[i][:, None].contiguous(), pos, wl.w, wl.s,
+                          wl.conv)
+            swa.decode_step(qg[i], kc, vc, pos, wl.w, wl.s, wl.scale, wl.conv, out=out[i], workspace=ws)
+    got = out.cpu().numpy()
+    K = f64(torch.stack([known[p][0] for p in cand], 1))  # [B][n][Hkv][d], every candidate position
+    V = f64(torch.stack([known[p][1] for p in cand], 1))
+    for i in range(steps):
+        t = P + i
+        ref = orc.decode_rows(f64(qs[i]), cand, K, V, [t] * B, wl.w, wl.s, wl.scale, wl.conv)
+        err = np.abs(got[i] - ref)
+        parity(f"decode_swa64_4_b{B} {'fused append+decode' if fused else 'append, then decode'}", err)
+        worst = max(worst, float(err.max()))
+        assert np.isfinite(got[i]).all() and err.max() <= TOL, (P, t, float(err.max()))
     say(f"worst {worst:.3e}")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_batch_with_mixed_positions(fused, parity):
+    """One launch over sequences at different positions: before the sinks fill, before and across
+    the step where the ring wraps (t = s + w_loc - 1 = 67), well past it, and beyond 2^31.  Each
+    sequence has its own cache history; each output is checked against its own oracle row."""
+    w, s, conv, Hq, Hkv, d = 64, 4, 0, 32, 8, 128
+    w_loc = orc.local_window(w, s, conv)
+    starts = [1, 3, 66, 70, 2 ** 18 + 3, 2 ** 31 + 5]
+    B, steps, scale = len(starts), 4, 1.0 / np.sqrt(d)
+    say("mixed", fused, starts)
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s, conv)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s, conv)
+    hist = []
+    for b, P in enumerate(starts):
+        lo = max(s, P - w_loc)
+        cand = sorted(set(range(min(s, P))) | set(range(lo, P)) | set(range(P, P + steps)))
+        known = {p: inputs.kv_at(500 + b, p, 1, Hkv, d, 1.0, 4, 4.0) for p in cand}
+        seed_cache(kc[b:b + 1], vc[b:b + 1], known, lo, P, s, w, conv)
+        hist.append((cand, known))
+    for i in range(steps):
+        ts = [P + i for P in starts]
+        q = torch.cat([inputs.q_at(500 + b, t, 1, Hq, d, 1.0) for b, t in enumerate(ts)])
+        kn = torch.cat([hist[b][1][t][0] for b, t in enumerate(ts)]).cuda()
+        vn = torch.cat([hist[b][1][t][1] for b, t in enumerate(ts)]).cuda()
+        pos = gpos(ts)
+        if fused:
+            out = swa.append_decode_step(q.cuda(), kc, vc, kn, vn, pos, w, s, scale, conv, workspace=ws)
+        else:
+            swa.kv_append(kc, vc, kn[:, None].contiguous(), vn[:, None].contiguous(), pos, w, s, conv)
+            out = swa.decode_step(q.cuda(), kc, vc, pos, w, s, scale, conv, workspace=ws)
+        out = out.cpu().numpy()
+        for b, t in enumerate(ts):
+            cand, known = hist[b]
+            ref, used = orc.decode_row(f64(q[b]), cand, f64(torch.cat([known[p][0] for p in cand])),
+                                       f64(torch.cat([known[p][1] for p in cand])), t, w, s, scale, conv)
+            assert used == min(t + 1, w_loc + s)
+            err = np.abs(out[b] - ref)
+            parity("decode mixed positions in one batch", err)
+            assert np.isfinite(out[b]).all() and err.max() <= TOL, (b, t, float(err.max()))
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s", [(1, 32, 8, 128, 64, 4), (64, 32, 8, 128, 64, 4), (2, 64, 4, 128, 100, 4),
@@ -246,8 +318,34 @@ def test_fused_append_decode_equals_two_calls(B, Hq, Hkv, d, w, s, conv):
     assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
 
 
+@pytest.mark.parametrize("B,w,s", [(64, 64, 4), (2, 300, 4)])
+def test_timed_fused_step_matches_and_stamps_kernel_time(B, w, s):
+    """swa_append_decode_step_timed gives the untimed step's output and cache bit for bit and its
+    dispatches stamp a positive interval (with a workgroup split, the merge kernel stamps the end)."""
+    Hq, Hkv, d = 32, 8, 128
+    g = torch.Generator().manual_seed(7)
+    T = w + s + 3
+    ks = torch.randn(B, T, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    kc1, vc1 = swa.alloc_cache(B, Hkv, d, w, s)
+    swa.kv_append(kc1, vc1, ks, ks.flip(1).contiguous(), gpos([0] * B), w, s)
+    kc2, vc2 = kc1.clone(), vc1.clone()
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16).cuda()
+    kn = torch.randn(B, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    vn = torch.randn(B, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s)
+    pos = gpos([T] * B)
+    a = swa.append_decode_step(q, kc1, vc1, kn, vn, pos, w, s, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    b = swa.append_decode_step(q, kc2, vc2, kn, vn, pos, w, s, workspace=ws, events=(e0, e1))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    assert e0.elapsed_time(e1) > 0
+
+
 @pytest.mark.parametrize("P,B,Hq,Hkv,d", [(5000, 1, 8, 2, 128), (3000, 2, 4, 4, 64)])
-def test_full_attention_decode_at_long_context(P, B, Hq, Hkv, d):
+def test_full_attention_decode_at_long_context(P, B, Hq, Hkv, d, parity):
     """Full causal attention as SWA with s = 0 and a window holding the whole context (the
     comparator of the SWA-versus-full measurement): the cache holds positions 0 .. P-1, the
     step appends P and attends to every position; thousands of slots, so split + merge."""
@@ -269,6 +367,7 @@ def test_full_attention_decode_at_long_context(P, B, Hq, Hkv, d):
     for b in range(B):
         ref, kept = orc.decode_row(f64(q[b]), pos, f64(k[b]), f64(v[b]), P, w, s, scale)
         assert kept == P + 1
+        parity("full-attention decode at long context", np.abs(out[b] - ref))
         worst = max(worst, float(np.abs(out[b] - ref).max()))
     say(f"max {worst:.3e}")
     assert worst <= TOL
