@@ -192,6 +192,27 @@ int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, flo
                     int conv, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * swa_decode_step_noalloc -- swa_decode_step without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, allocation-free serving loops,
+ * harnesses that forbid hipMalloc).  When the shape needs a workspace (s + w_loc > 128 slots:
+ * partial (max, sum, weighted values) per split), a static device array of 8 MiB inside the
+ * library serves as one; the library takes its address once per device (on the first call with
+ * that device current) and never allocates or frees anything.  Every partial is written before
+ * it is read within one call, so nothing needs clearing between calls.
+ *
+ * Same arguments, layout and results as swa_decode_step without workspace/workspace_bytes; runs
+ * on the current device's copy of the scratch (the stream must belong to the current device).
+ * Every call on one GPU shares that copy: calls whose work overlaps on one GPU (different
+ * streams, or different threads without ordering) race and must be ordered by the caller.
+ * Errors: as swa_decode_step; SWA_EUNSUPPORTED when the shape needs more scratch than 8 MiB
+ * (B * Hq * splits * (d + 2) * 4 bytes, see swa_decode_describe); SWA_EHIP if the scratch
+ * address cannot be obtained or the launch fails.
+ */
+int swa_decode_step_noalloc(const void *q, const void *k_cache, const void *v_cache, float *out,
+                            const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s, float scale,
+                            int conv, void *stream);
+
+/*
  * swa_append_decode_step -- swa_kv_append of one token per sequence followed by
  * swa_decode_step, in one launch.  The new token k_new[b], v_new[b] (bf16 [B][Hkv][d], the
  * token at position pos[b]) is written to its slot and attended directly from k_new/v_new;

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     debug_prefill_mask,
     decode_describe,
     decode_step,
+    decode_step_noalloc,
     decode_workspace_bytes,
     kv_append,
     last_error,

@@ -32,6 +32,7 @@ EXPORTS = (
     "swa_decode_workspace_bytes",
     "swa_decode_describe",
     "swa_decode_step",
+    "swa_decode_step_noalloc",
     "swa_append_decode_step",
     "swa_append_decode_step_timed",
     "swa_prefill_chunk",
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.swa_decode_workspace_bytes.restype = sz
     L.swa_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.swa_decode_step.restype = i32
+    L.swa_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.swa_decode_step_noalloc.restype = i32
     L.swa_append_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                          vp]
     L.swa_append_decode_step.restype = i32
@@ -255,6 +258,25 @@ def decode_step(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = 
     _check(lib().swa_decode_step(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                  pos.data_ptr(), B, Hq, Hkv, d, w, s, scale, conv, ws_ptr or None, ws_bytes,
                                  _stream(q)))
+    return out
+
+
+def decode_step_noalloc(q, k_cache, v_cache, pos, w: int, s: int, scale: float | None = None,
+                        conv: int = ADDITIVE, out=None):
+    """decode_step with the library's static scratch in place of a workspace
+    (swa_decode_step_noalloc: no device allocation by the library)."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, cache_slots(w, s, conv), d))
+    _need(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _need(pos, "pos", torch.int64, (B,))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_decode_step_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                         pos.data_ptr(), B, Hq, Hkv, d, w, s, scale, conv, _stream(q)))
     return out
 
 

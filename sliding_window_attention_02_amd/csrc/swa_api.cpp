@@ -117,7 +117,7 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
 int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache, const void *k_new,
                 const void *v_new, float *out, const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s,
                 float scale, int conv, void *workspace, size_t workspace_bytes, void *stream, void *start = nullptr,
-                void *stop = nullptr)
+                void *stop = nullptr, bool use_scratch = false)
 {
     CHECK_PTR(q);
     CHECK_PTR(k_cache);
@@ -136,6 +136,15 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
     if ((long long)s + w_loc > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
     const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    if (use_scratch && plan.workspace_bytes > 0) {  // the static scratch stands in for the workspace
+        if (plan.workspace_bytes > swa::scratch_capacity())
+            return fail(SWA_EUNSUPPORTED, "%s: needs %zu bytes of scratch, the static scratch holds %zu", fn,
+                        plan.workspace_bytes, swa::scratch_capacity());
+        const hipError_t e = swa::scratch_pointer(&workspace);
+        if (e != hipSuccess)
+            return hip_status(fn, e);
+        workspace_bytes = swa::scratch_capacity();
+    }
     if (plan.workspace_bytes > 0) {
         if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
             return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, plan.workspace_bytes,
@@ -370,6 +379,13 @@ int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, flo
 {
     return decode_impl("swa_decode_step", q, k_cache, v_cache, nullptr, nullptr, out, pos, B, Hq, Hkv, d, w, s,
                        scale, conv, workspace, workspace_bytes, stream);
+}
+
+int swa_decode_step_noalloc(const void *q, const void *k_cache, const void *v_cache, float *out, const int64_t *pos,
+                            int B, int Hq, int Hkv, int d, int w, int s, float scale, int conv, void *stream)
+{
+    return decode_impl("swa_decode_step_noalloc", q, k_cache, v_cache, nullptr, nullptr, out, pos, B, Hq, Hkv, d, w,
+                       s, scale, conv, nullptr, 0, stream, nullptr, nullptr, true);
 }
 
 int swa_append_decode_step(const void *q, void *k_cache, void *v_cache, const void *k_new, const void *v_new,

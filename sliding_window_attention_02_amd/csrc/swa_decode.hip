@@ -20,7 +20,18 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <mutex>
+
 namespace swa {
+
+// Static scratch for callers that cannot allocate (swa_decode_step_noalloc): the split partials
+// (m, l, o) live here instead of in a caller workspace.  Each GPU the library runs on holds one
+// copy for the life of the process; host code reaches it only through the per-device address
+// that scratch_pointer() takes from hipGetSymbolAddress (the array's name in host code is a
+// host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -641,6 +652,31 @@ hipError_t launch_decode(const void *q, void *k_cache, void *v_cache, const void
         hipLaunchKernelGGL(merge, dim3(Hq, B), dim3(kMergeThreads), 0, stream, (const float *)a.ws, out, Hq,
                            plan.n_split);
     return hipGetLastError();
+}
+
+size_t scratch_capacity() { return kScratchBytes; }
+
+hipError_t scratch_pointer(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {  // once per device, with that device current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        ptrs[dev] = p;
+    }
+    *ptr = ptrs[dev];
+    return hipSuccess;
 }
 
 ChunkPlan chunk_plan(int64_t pos0, int C, int w_loc, int s)

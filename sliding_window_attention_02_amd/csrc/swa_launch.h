@@ -66,6 +66,11 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int w_loc, int s);
 
+// The static scratch of swa_decode_step_noalloc: its size, and its address on the current device
+// (taken once per device with hipGetSymbolAddress, then cached).
+size_t scratch_capacity();
+hipError_t scratch_pointer(void **ptr);
+
 // pos: device [B] first positions, or null to append every sequence at pos0.
 hipError_t launch_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                             const int64_t *pos, int B, int Hkv, int d, int w_loc, int s, int n_new,
