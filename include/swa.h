@@ -256,15 +256,20 @@ int swa_append_decode_step_timed(const void *q, void *k_cache, void *v_cache, co
  *   k_cache,    bf16 [B][Hkv][s + w_loc][d] (in/out), the layout swa_kv_append writes
  *   v_cache
  *   out         fp32 [B][C][Hq][d]   (out)
+ *   lse         fp32 [B][C][Hq] (out) or NULL: ln sum_{i in A(t)} exp(scale <q_t, k_i>) of each row,
+ *               the log of its softmax denominator (for callers that merge partial attention
+ *               results); the probabilities are summed as they weight V (bf16), so it carries
+ *               their rounding (~2^-9 relative in the sum)
  *   pos0        position of the chunk's first token, >= 0 (host value)
  * Two launches on `stream` (attend, reading the cached keys in place; then append); no
  * workspace, no synchronisation.
- * Errors: as swa_prefill, plus SWA_EINVAL for C < 1 or pos0 < 0; SWA_EUNSUPPORTED when
+ * Errors: as swa_prefill, plus SWA_EINVAL for C < 1, pos0 < 0 or a non-16-byte-aligned lse;
+ * SWA_EUNSUPPORTED when
  * s + w_loc - 1 + C keys, or the C query rows, of one sequence exceed 2^31-1 elements.
  */
 int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache,
-                      float *out, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s,
-                      float scale, int conv, void *stream);
+                      float *out, float *lse, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w,
+                      int s, float scale, int conv, void *stream);
 
 /*
  * Decoder-layer decode step around SWA(w,s) attention, for the multi-layer decode

@@ -62,6 +62,8 @@ def _load():
     lib.swa_oracle_prefill.restype = i32
     lib.swa_oracle_prefill_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, i64, i64, i32]
     lib.swa_oracle_prefill_rows.restype = i32
+    lib.swa_oracle_lse_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, i64, i64]
+    lib.swa_oracle_lse_rows.restype = i32
     lib.swa_oracle_decode_row.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, vp]
     lib.swa_oracle_decode_row.restype = i64
     lib.swa_oracle_decode_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i64, i64, i64, i64, dbl, vp, i32]
@@ -148,6 +150,21 @@ def prefill_rows(q, k, v, t_lo: int, t_hi: int, w: int, s: int, scale: float, co
                                          float(scale), t_lo, t_hi, nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"swa_oracle_prefill_rows failed ({rc})")
+    return out
+
+
+def lse_rows(q, k, t_lo: int, t_hi: int, w: int, s: int, scale: float, conv: int = ADDITIVE) -> np.ndarray:
+    """ln of the softmax denominator, sum over A(t) of exp(scale <q_t, k_i>), for rows
+    t_lo <= t < t_hi: fp64 [B][t_hi - t_lo][Hq]."""
+    q, k = _f64(q), _f64(k)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, L, Hkv, d) and 0 <= t_lo < t_hi <= L
+    w_loc = local_window(w, s, conv)
+    out = np.empty((B, t_hi - t_lo, Hq), dtype=np.float64)
+    if _load().swa_oracle_lse_rows(_ptr(q), _ptr(k), _ptr(out), B, Hq, Hkv, L, d, w_loc, s, float(scale),
+                                   t_lo, t_hi) != 0:
+        raise RuntimeError("swa_oracle_lse_rows failed")
     return out
 
 

@@ -226,6 +226,47 @@ int swa_oracle_prefill(const double *q, const double *k, const double *v, double
     return swa_oracle_prefill_rows(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale, 0, L, nthreads);
 }
 
+/* Log of the softmax denominator of rows t_lo <= t < t_hi: for every (b, t, h),
+ *   lse[b][t - t_lo][h] = ln sum_{i in A(t)} exp(scale * <q[b][t][h], k[b][i][g(h)]>),
+ * taken as m + ln sum exp(l_i - m) with m the row maximum of the logits l_i (fp64).
+ *   q: [B][L][Hq][d]  k: [B][L][Hkv][d]  lse: [B][t_hi - t_lo][Hq].
+ * Returns 0, or -1 on bad arguments. */
+int swa_oracle_lse_rows(const double *q, const double *k, double *lse, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t L, int64_t d, int64_t w_loc, int64_t s, double scale,
+                        int64_t t_lo, int64_t t_hi)
+{
+    if (!q || !k || !lse || B < 1 || L < 1 || d < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 ||
+        w_loc < 1 || s < 0 || t_lo < 0 || t_hi > L || t_lo >= t_hi)
+        return -1;
+    const int64_t group = Hq / Hkv;
+    double *lg = (double *)malloc((size_t)L * sizeof(double));
+    if (!lg)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = t_lo; t < t_hi; ++t)
+            for (int64_t h = 0; h < Hq; ++h) {
+                const double *qr = q + ((b * L + t) * Hq + h) * d;
+                double m = -INFINITY, sum = 0.0;
+                for (int64_t i = 0; i <= t; ++i) {
+                    if (!swa_oracle_allowed(t, i, w_loc, s))
+                        continue;
+                    const double *ki = k + ((b * L + i) * Hkv + h / group) * d;
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        dot += qr[c] * ki[c];
+                    lg[i] = scale * dot;
+                    if (lg[i] > m)
+                        m = lg[i];
+                }
+                for (int64_t i = 0; i <= t; ++i)
+                    if (swa_oracle_allowed(t, i, w_loc, s))
+                        sum += exp(lg[i] - m);
+                lse[(b * (t_hi - t_lo) + (t - t_lo)) * Hq + h] = m + log(sum);
+            }
+    free(lg);
+    return 0;
+}
+
 /* One decode row from an explicit set of cached positions.
  *   q: [Hq][d] for the query at position t.
  *   pos: [n] distinct absolute positions; k, v: [n][Hkv][d] their keys and values.

@@ -104,7 +104,7 @@ def lib() -> ctypes.CDLL:
     L.swa_append_decode_step_timed.argtypes = L.swa_append_decode_step.argtypes + [vp, vp]
     L.swa_append_decode_step_timed.restype = i32
     i64 = ctypes.c_int64
-    L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.swa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.swa_prefill_chunk.restype = i32
     L.swa_last_error.argtypes = []
     L.swa_last_error.restype = ctypes.c_char_p
@@ -313,9 +313,10 @@ def append_decode_step(q, k_cache, v_cache, k_new, v_new, pos, w: int, s: int, s
 
 
 def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: float | None = None,
-                  conv: int = ADDITIVE, out=None):
+                  conv: int = ADDITIVE, out=None, lse=None):
     """Prefill of a chunk at positions pos0 .. pos0+C-1 against the cache (state after pos0-1),
-    then the chunk appended.  q bf16 [B][C][Hq][d], k/v bf16 [B][C][Hkv][d] -> fp32 [B][C][Hq][d]."""
+    then the chunk appended.  q bf16 [B][C][Hq][d], k/v bf16 [B][C][Hkv][d] -> fp32 [B][C][Hq][d].
+    lse: optional fp32 [B][C][Hq] that receives ln of each row's softmax denominator."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B][C][Hq][d] and k, v [B][C][Hkv][d]")
     B, C, Hq, d = q.shape
@@ -329,9 +330,12 @@ def prefill_chunk(q, k, v, k_cache, v_cache, pos0: int, w: int, s: int, scale: f
     if out is None:
         out = torch.empty((B, C, Hq, d), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (B, C, Hq, d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, C, Hq))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib().swa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                   out.data_ptr(), int(pos0), B, Hq, Hkv, C, d, w, s, scale, conv, _stream(q)))
+                                   out.data_ptr(), None if lse is None else lse.data_ptr(), int(pos0), B, Hq, Hkv, C,
+                                   d, w, s, scale, conv, _stream(q)))
     return out
 
 

@@ -159,7 +159,8 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
 }
 
 int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void *k_cache, void *v_cache, float *out,
-               int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv, void *stream)
+               float *lse, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv,
+               void *stream)
 {
     CHECK_PTR(q);
     CHECK_PTR(k);
@@ -167,6 +168,8 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
     CHECK_PTR(k_cache);
     CHECK_PTR(v_cache);
     CHECK_PTR(out);
+    if (lse != nullptr && !aligned16(lse))
+        return fail(SWA_EINVAL, "%s: lse is not 16-byte aligned", fn);
     int rc = check_heads(fn, B, Hq, Hkv, d);
     if (rc)
         return rc;
@@ -189,7 +192,7 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
     // Attend (reading the cache as it stands), then append: the chunk's slots may hold keys
     // that its first queries still need.
     hipError_t e = swa::launch_prefill(q, k, v, out, B, Hq, Hkv, plan.rows, d, w_loc, s, scale, st, nullptr,
-                                       nullptr, &cached);
+                                       nullptr, &cached, lse);
     if (e == hipSuccess)
         e = swa::launch_kv_append(k_cache, v_cache, k, v, nullptr, B, Hkv, d, w_loc, s, C, st, pos0);
     return hip_status(fn, e);
@@ -255,10 +258,10 @@ extern "C" {
 const char *swa_last_error(void) { return g_last_error.c_str(); }
 
 int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache, float *out,
-                      int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale, int conv,
-                      void *stream)
+                      float *lse, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w, int s, float scale,
+                      int conv, void *stream)
 {
-    return chunk_impl("swa_prefill_chunk", q, k, v, k_cache, v_cache, out, pos0, B, Hq, Hkv, C, d, w, s, scale,
+    return chunk_impl("swa_prefill_chunk", q, k, v, k_cache, v_cache, out, lse, pos0, B, Hq, Hkv, C, d, w, s, scale,
                       conv, stream);
 }
 

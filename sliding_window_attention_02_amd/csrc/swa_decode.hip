@@ -44,6 +44,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // a helper or an implicit conversion there makes the host pass drop the launch stub).
 #define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
+// V rows in LDS: 16-byte pieces XOR-swizzled so the transposed 8-byte reads of rows
+// r..r+3 (r = 0 mod 4) at pieces P, P+1 hit 8 distinct pieces.
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
 constexpr int kChunk = 32;      // slots per MFMA step
 constexpr int kMaxChunks = 3;   // slots per wave <= 96
 constexpr int kMaxWaveSplits = 4;  // waves (one chunk each) when a workgroup splits its slots
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             for (int i = 0; i < kLoads; ++i) {
                 const int r = kRowsPerLoad * i + lane / kPieces;
                 const int slot = min(c0 + r, last);
-                const int piece = (lane % kPieces) ^ lds_swizzle<D>(r);
+                const int piece = (lane % kPieces) ^ swz_v(r);
                 __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vcache + (size_t)slot * D + piece * 8),
                                                  SWA_LDS_PTR(&vlds[ch][1024 * i]), 16, 0, 0);
             }
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         const int r_end = slot_t == seg_hi - 1 ? kChunk : r + 1;
         for (int rr = r; rr < r_end; ++rr)
             *reinterpret_cast<u32x4 *>(&vlds[0][0] + ch * kChunk * kRowBytes + rr * kRowBytes +
-                                       16 * (lane ^ lds_swizzle<D>(rr))) = vn_piece;
+                                       16 * (lane ^ swz_v(rr))) = vn_piece;
     }
     const int vt_row0 = 8 * g16 + (c16 >> 2);
     const int vt_half = 8 * (c16 & 1);
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int row = 4 * h + vt_row0;
-                const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ lds_swizzle<D>(row)) + vt_half;
+                const int off = row * kRowBytes + 16 * ((2 * db + vt_pbit) ^ swz_v(row)) + vt_half;
                 const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s16x4 *)(&vlds[ch][off]));
                 const bf16x4 y = __builtin_bit_cast(bf16x4, x);

@@ -173,26 +173,6 @@ SWA_HD void resident_half_slots(const ChunkWalk &cw, int h0, int h1, int w_loc, 
     }
 }
 
-// ---------------------------------------------------------------------------- LDS layout
-//
-// K and V rows staged in LDS keep their 16-byte pieces XOR-swizzled (physical piece = logical
-// piece ^ lds_swizzle(row)) so that the MFMA fragment reads are free of bank conflicts (64
-// banks of 4 bytes; a 16-byte read serves 16 lanes per pass, an 8-byte read 32):
-//   * K fragment: lanes 0-15 read logical piece P of rows 8a + b + c (a, b = 0..3; c a constant
-//     with bits 2 and 5 only), which land in 16 distinct 16-byte bank groups;
-//   * V^T fragment (transposed 8-byte reads): lanes 0-15 read pieces P, P+1 (P even) of rows
-//     r .. r+3 and lanes 16-31 those of rows r+8 .. r+11 (r = 0 mod 4): the row bits 0-1 spread
-//     each quad over 8 distinct pieces and row bit 3 moves the second quad to the other half of
-//     the banks (d = 128: piece bit 3; d = 64, two rows per 256-byte bank line: piece bit 1).
-// The swizzle ignores row bits 2 and 5, so a fragment's offset is a per-lane base plus an
-// immediate for the 4-row and 32-row steps.  K and V share it, so their loads share offsets.
-template <int D>
-__device__ __forceinline__ int lds_swizzle(int r)
-{
-    const int quad = (r & 3) ^ (((r >> 3) & 1) << (D == 128 ? 2 : 0));
-    return ((r >> 4) & 1) | (quad << 1);
-}
-
 // ------------------------------------------------------------------------------ decode
 //
 // Cache of s pinned sink slots followed by a ring of w_loc slots.  Position p lives in

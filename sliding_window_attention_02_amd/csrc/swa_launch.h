@@ -45,11 +45,12 @@ struct PrefillKeySource {
 };
 
 // start/stop: optional events stamped by the kernel dispatch itself (null: plain launch).
-// cached: null for a whole-sequence prefill.
+// cached: null for a whole-sequence prefill.  lse: optional fp32 [B][L - n_cached][Hq], ln of each
+// query row's softmax denominator.
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
-                          const PrefillKeySource *cached = nullptr);
+                          const PrefillKeySource *cached = nullptr, float *lse = nullptr);
 
 hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int d, int w_loc, int s,
                                      hipStream_t stream);

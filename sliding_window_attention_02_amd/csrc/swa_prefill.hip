@@ -26,8 +26,8 @@
 //
 // Memory: K and V tiles of 64 keys go from global memory straight into LDS (direct
 // global -> LDS loads, double-buffered, one barrier per tile), both row-major with the
-// 16-byte pieces of each row XOR-swizzled so that the K fragment reads and the transposed
-// V reads (ds_read_b64_tr_b16) are free of bank conflicts.  Q stays in registers for the
+// 16-byte pieces of each row XOR-swizzled so that the K fragment reads hit distinct banks and
+// the transposed V reads (ds_read_b64_tr_b16) spread over distinct pieces.  Q stays in registers for the
 // whole key loop.  Workgroups are ordered heavy-first (last q-tile first) and mapped so
 // that consecutive logical workgroups share an XCD and its L2, where neighbouring q-tiles
 // re-read the same K/V tiles.  The fp32 output goes out in whole 128-byte lines with
@@ -60,6 +60,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = 64;     // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves
@@ -70,6 +71,7 @@ struct PrefillArgs {
     const uint16_t *k;
     const uint16_t *v;
     float *out;
+    float *lse;  // optional [B][Lq][Hq]: ln of each row's softmax denominator (null: not written)
     int L, Hq, Hkv, G, Gw, Tm, n_qtiles, n_hslices;
     int Lq, q_lo;  // queries are key positions q_lo .. q_lo + Lq - 1 (rows 0 .. Lq-1 of q, out)
     // Keys 0 .. n_cached-1 come from a sink+ring cache [B][Hkv][s + w_loc][d] instead of k, v
@@ -106,6 +108,32 @@ __device__ __forceinline__ float max_over_groups(float x)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// XOR swizzles of the 16-byte pieces of a row in LDS (physical piece = logical piece ^ swizzle).
+// K: the 16 rows one S^T fragment read touches (32*kc + 8a + 4h + b, a, b = 0..3) get 16
+// distinct swizzles, so the 16-byte reads of 16 consecutive lanes hit distinct bank groups.  V:
+// the transposed 8-byte reads take rows r..r+3 (r = 0 mod 4) at pieces P, P+1 (P even); swizzles
+// 0, 2, 4, 6 spread them over 8 distinct pieces.  (The counters charge every transposed read two
+// bank-conflict cycles whatever the layout: a swizzle that also separates the row quads of lanes
+// 0-15 and 16-31 left the count unchanged and ran 1-4% slower.)
+template <int D>
+__device__ __forceinline__ int swz_k(int r)
+{
+    return D == 128 ? ((((r >> 3) & 3) << 2) | (r & 3)) : ((((r >> 3) & 1) << 2) | (r & 3));
+}
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
+// acc + the sum of the eight bf16 values of p, in fp32 (four v_dot2 with a pair of ones).
+__device__ __forceinline__ float sum8(const bf16x8 &p, float acc)
+{
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 y = {p[2 * i], p[2 * i + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(y, one, acc, false);
+    }
+    return acc;
+}
+
 // s_waitcnt immediate that waits for at most n outstanding vector-memory operations and
 // nothing else (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
@@ -139,6 +167,13 @@ __device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t o
     // (aux 2: the non-temporal policy)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, av), rs, (int)offa, 0, 2);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bv), rs, (int)offb, 0, 2);
+}
+
+// ln of a row's softmax denominator: the probabilities were taken as exp2(score * scale * log2(e)
+// - m) with m in log2 units, so sum_i exp(scale * score_i) = 2^m * l.
+__device__ __forceinline__ void store_lse(const PrefillArgs &a, int b, int t, int h, float m, float l)
+{
+    a.lse[((size_t)b * a.Lq + (t - a.q_lo)) * a.Hq + h] = (m + log2f(l)) * 0.6931471805599453f;
 }
 
 // Maps the hardware workgroup id to (b, kv-head, head slice, q-tile).
@@ -253,12 +288,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     // last row (finite values; such keys are always masked).
     // The wave index as a uniform (scalar) value: the LDS destinations (M0) are then scalar.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t ld_off[kLoadsPerWave];  // byte offsets from the tile's first row (K and V alike)
+    uint32_t ld_koff[kLoadsPerWave], ld_voff[kLoadsPerWave];  // byte offsets from the tile's first row
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int row = kRowsPerLoad * (wave * kLoadsPerWave + i) + lane / kPieces;
         const int phys = lane % kPieces;
-        ld_off[i] = (uint32_t)(row * kv_row + (phys ^ lds_swizzle<D>(row)) * 8) * 2u;
+        ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
+        ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
     }
     // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf
     // (buf 2: the wide form's fifth chunk slot, which holds tile rows 0 .. 31, so only waves 0
@@ -284,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 const int j = wave_u * kLoadsPerWave + i;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs,
                                                          SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
-                                                         16, (int)ld_off[i], tile_off, 0, 0);
+                                                         16, (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off, 0, 0);
             }
             return;
         }
@@ -292,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int j = wave_u * kLoadsPerWave + i;
             const int row = kRowsPerLoad * j + lane / kPieces;
-            const int piece = (lane % kPieces) ^ lds_swizzle<D>(row);
+            const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
             const int key = min(j0 + row, last);
             const uint16_t *src;
             if (key >= a.n_cached) {
@@ -316,41 +352,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     using VRows = std::integral_constant<int, 1>;
     // LDS read offsets (bytes, within a tile) that do not depend on the tile.
     // K fragment (kc, h, kk): row 32kc + 4h + r with r = 8(c16/4) + c16%4, logical piece
-    // 4kk + g16.  Adding 32kc + 4h to r sets only row bits 2 and 5, which the swizzle ignores, so the row's
+    // 4kk + g16.  Adding 32kc + 4h to r changes neither r % 4 nor (r / 8) % 4, so the row's
     // swizzle is that of r: the offset is k_lane[kk] plus the constant (32kc + 4h) * kRowBytes.
     int k_lane[kKSteps];
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
         const int r = 8 * (c16 >> 2) + (c16 & 3);
-        k_lane[kk] = r * kRowBytes + 16 * ((4 * kk + g16) ^ lds_swizzle<D>(r));
+        k_lane[kk] = r * kRowBytes + 16 * ((4 * kk + g16) ^ swz_k<D>(r));
     }
     // V^T fragment (db, kc) from two transposed 8-byte reads (h = 0, 1): lane 16g + s reads
     // row 32kc + 4h + 8g + s/4 at d = 16db + 4(s%4) .. +3 (byte 8(s%2) of logical piece
     // 2db + (s/2)%2); the read hands lane s the values at d = 16db + s of the four rows
-    // 32kc + 4h + 8g .. +3.  The swizzle does not see row bits 2 and 5, so the offset is
-    // v_lane[db] plus the constant (32kc + 4h) * kRowBytes.
-    int v_lane[kDBlocks];
+    // 32kc + 4h + 8g .. +3.  The row's swizzle is 2(s/4) whatever kc, h, and XOR with an even
+    // swizzle keeps the low piece bit, so the physical piece is 2(db ^ s/4) + (s/2)%2 and the
+    // offset is v_lane[db % 4] plus the constant (32kc + 4h) * kRowBytes + 32 (db - db % 4).
+    int v_lane[4];
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
-        const int r = 8 * g16 + (c16 >> 2);
-        v_lane[db] = r * kRowBytes + 16 * ((2 * db + ((c16 >> 1) & 1)) ^ lds_swizzle<D>(r)) + 8 * (c16 & 1);
-    }
+    for (int m = 0; m < 4; ++m)
+        v_lane[m] = (8 * g16 + (c16 >> 2)) * kRowBytes + 32 * (m ^ (c16 >> 2)) + 16 * ((c16 >> 1) & 1) + 8 * (c16 & 1);
 
     f32x4 o[kDBlocks][2];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
         o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Softmax state per query column, in log2 units: the reference maximum m_ref the
-    // probabilities are taken against.  The running sum of the probabilities is computed
-    // by the matrix cores from the same bf16-rounded values that weight V: a constant
-    // A fragment whose row 0 is all ones turns one extra MFMA per chunk into
-    // lsum[0] += sum_k P^T[k][q] (lane group 0 holds it; the other rows are zero).  The
-    // dominant weight's rounding then cancels between numerator and denominator.
+    // probabilities are taken against.  The running sum of the probabilities adds the same
+    // bf16-rounded values that weight V (v_dot2 with a pair of ones, fp32 accumulation): each
+    // lane sums the keys it holds and the four lane groups of a column are added at the end, so
+    // the dominant weight's rounding cancels between numerator and denominator.
     float m_ref[2] = {-INFINITY, -INFINITY};
-    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const __bf16 one_or_zero = static_cast<__bf16>(c16 == 0 ? 1.f : 0.f);
-    const bf16x8 ones_row = {one_or_zero, one_or_zero, one_or_zero, one_or_zero,
-                             one_or_zero, one_or_zero, one_or_zero, one_or_zero};
+    float lsum[2] = {0.f, 0.f};
 
     if constexpr (RES) {
         // Resident forms (windows whose 32-token q-tile needs at most four 32-key chunks): every
@@ -427,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             // Probabilities, their column sums (the ones-row MFMA), then O^T one 16-row block at a
             // time, each stored as soon as it is complete, so the stores spread over the compute.
             bf16x8 pf[4];
-            f32x4 lq = {0.f, 0.f, 0.f, 0.f};
+            float l = 0.f;  // this lane's keys; the lane groups are added below
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -435,12 +466,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         pf[k][4 * h + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sr[k][h][j], c, -m_use)));
-                lq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[k], lq, 0, 0, 0);
+                l = sum8(pf[k], l);
             }
-            float l = lq[0];  // non-zero in lane group 0 only
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
+            if (a.lse != nullptr && g16 == 0 && valid[qb])
+                store_lse(a, bc.b, tok[qb], head[qb], m_use, l);
             const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
             f32x4 od_lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -452,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     bf16x8 af;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int off = v_lane[db] + 4 * h * kRowBytes;
+                        const int off = v_lane[db & 3] + 4 * h * kRowBytes + 32 * (db & ~3);
                         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(vt + off));
                         const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -608,13 +640,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     continue;
     #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
-                    lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[kc][qb], lsum[qb], 0, 0, 0);
+                    lsum[qb] = sum8(pf[kc][qb], lsum[qb]);
     #pragma unroll
                 for (int db = 0; db < kDBlocks; ++db) {
                     bf16x8 af;
     #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int off = v_lane[db] + (kc * kChunkN + 4 * h) * kRowBytes;
+                        const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
                         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(vt + off));
                         const bf16x4 y = __builtin_bit_cast(bf16x4, x);
@@ -743,10 +775,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
     #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            float l = lsum[qb][0];  // non-zero in lane group 0 only
+            float l = lsum[qb];  // this lane's keys; add the four lane groups of the column
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const float inv = 1.f / l;
+            if (a.lse != nullptr && g16 == 0 && valid[qb])
+                store_lse(a, bc.b, tok[qb], head[qb], m_ref[qb] == -INFINITY ? 0.f : m_ref[qb], l);
             const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
     #pragma unroll
             for (int m = 0; m < kDBlocks / 2; ++m)
@@ -892,7 +926,7 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, float *out, int B, int Hq,
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
-                          hipEvent_t start, hipEvent_t stop, const PrefillKeySource *cached)
+                          hipEvent_t start, hipEvent_t stop, const PrefillKeySource *cached, float *lse)
 {
     int Lq = L, q_lo = 0;
     if (cached != nullptr) {
@@ -910,6 +944,7 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     a.out = out;
+    a.lse = lse;
     a.L = L;
     a.Lq = Lq;
     a.q_lo = q_lo;

@@ -188,13 +188,13 @@ def test_append_decode_step_timed_requires_events(lib):
 
 def test_prefill_chunk_rejects_on_host(lib):
     f = lib.swa_prefill_chunk
-    good = dict(q=A, k=A, v=A, kc=A, vc=A, out=A, pos0=0, B=1, Hq=32, Hkv=8, C=16, d=128, w=64, s=4, scale=0.1,
-                conv=0)
+    good = dict(q=A, k=A, v=A, kc=A, vc=A, out=A, lse=None, pos0=0, B=1, Hq=32, Hkv=8, C=16, d=128, w=64, s=4,
+                scale=0.1, conv=0)
 
     def call(**kw):
         a = dict(good, **kw)
-        return f(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["out"], a["pos0"], a["B"], a["Hq"], a["Hkv"], a["C"],
-                 a["d"], a["w"], a["s"], a["scale"], a["conv"], None)
+        return f(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["out"], a["lse"], a["pos0"], a["B"], a["Hq"], a["Hkv"],
+                 a["C"], a["d"], a["w"], a["s"], a["scale"], a["conv"], None)
 
     assert call(kc=None) == binding.SWA_EINVAL and "k_cache" in err(lib)
     assert call(v=MIS) == binding.SWA_EINVAL and "aligned" in err(lib)
@@ -206,6 +206,7 @@ def test_prefill_chunk_rejects_on_host(lib):
     assert call(conv=7) == binding.SWA_EINVAL
     assert call(w=4, conv=1) == binding.SWA_EINVAL  # TOTAL window leaves nothing after the sinks
     assert call(C=2 ** 30) == binding.SWA_EUNSUPPORTED
+    assert call(lse=MIS) == binding.SWA_EINVAL and "lse is not 16-byte aligned" in err(lib)
 
 
 def test_layer_pieces_reject_on_host(lib):

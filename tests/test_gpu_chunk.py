@@ -56,24 +56,34 @@ CASES = [
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv,chunks", CASES)
-def test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks):
+def test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks, parity):
+    """Outputs and (every other chunk) the optional per-row log-sum-exp against the oracle."""
     L = sum(chunks)
     say("chunked", B, Hq, Hkv, d, w, s, conv, chunks)
     q, k, v = sequence(2024, B, L, Hq, Hkv, d)
     scale = 1.0 / np.sqrt(d)
     ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    ref_lse = orc.lse_rows(f64(q), f64(k), 0, L, w, s, scale, conv)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     kc, vc = nan_cache(B, Hkv, d, w, s, conv)
-    outs, p0 = [], 0
-    for C in chunks:
+    outs, lses, p0 = [], [], 0
+    for i, C in enumerate(chunks):
         sl = slice(p0, p0 + C)
+        lse = torch.full((B, C, Hq), float("nan"), dtype=torch.float32, device="cuda") if i % 2 == 0 else None
         outs.append(swa.prefill_chunk(qg[:, sl].contiguous(), kg[:, sl].contiguous(), vg[:, sl].contiguous(),
-                                      kc, vc, p0, w, s, scale, conv))
+                                      kc, vc, p0, w, s, scale, conv, lse=lse))
+        if lse is not None:
+            lses.append((p0, lse))
         p0 += C
     got = torch.cat(outs, dim=1).cpu().numpy()
     err = np.abs(got - ref)
     say(f"max {err.max():.3e}")
+    parity("chunked prefill outputs", err)
     assert np.isfinite(got).all() and err.max() <= TOL
+    for p0, lse in lses:
+        e = np.abs(lse.cpu().numpy() - ref_lse[:, p0:p0 + lse.shape[1]])
+        parity("chunked prefill log-sum-exp", e)
+        assert np.isfinite(e).all() and e.max() <= TOL, float(e.max())
     # The cache equals the one that appending every position one by one leaves (bitwise,
     # NaN-filled slots included).
     kc2, vc2 = nan_cache(B, Hkv, d, w, s, conv)
@@ -163,5 +173,5 @@ def _random_chunkings(n, seed):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv,chunks", _random_chunkings(6, 777))
-def test_chunked_prefill_on_drawn_chunkings(B, Hq, Hkv, d, w, s, conv, chunks):
-    test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks)
+def test_chunked_prefill_on_drawn_chunkings(B, Hq, Hkv, d, w, s, conv, chunks, parity):
+    test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks, parity)

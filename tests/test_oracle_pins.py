@@ -317,3 +317,31 @@ def test_prefill_rows_equal_sdpa_rows(t_lo, t_hi, nthreads):
     np.testing.assert_allclose(got, ref[:, t_lo:t_hi], rtol=0, atol=1e-12)
     whole = orc.prefill(f64(q), f64(k), f64(v), w, s, scale)
     assert np.array_equal(got, whole[:, t_lo:t_hi])
+
+
+def test_lse_rows_equal_logsumexp_of_masked_logits():
+    """ln of the softmax denominator equals torch.logsumexp over the allowed logits (fp64, the
+    first page's mask recipe with causality), every row, GQA heads included."""
+    B, L, Hq, Hkv, d, w, s, scale = 2, 50, 6, 2, 8, 7, 3, 0.45
+    q, k, _ = inputs.random_qkv(B, L, Hq, Hkv, d, seed=47, sink_boost_n=3, sink_boost=4.0)
+    qd = torch.as_tensor(f64(q))
+    kd = torch.as_tensor(f64(k)).repeat_interleave(Hq // Hkv, dim=2)
+    logits = torch.einsum("bthc,bihc->bhti", qd, kd) * scale
+    allowed = torch.as_tensor(causal_recipe_mask(L, w, s))
+    ref = torch.logsumexp(logits.masked_fill(~allowed, float("-inf")), dim=-1).permute(0, 2, 1).numpy()
+    got = orc.lse_rows(f64(q), f64(k), 0, L, w, s, scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(orc.lse_rows(f64(q), f64(k), 20, 35, w, s, scale), got[:, 20:35])
+
+
+@pytest.mark.parametrize("w,s", [(5, 2), (1, 0), (64, 4)])
+def test_lse_rows_closed_forms(w, s):
+    """q = 0: every allowed logit is 0, so the lse is ln |A(t)|; row 0 has the single key 0."""
+    B, L, Hq, Hkv, d = 1, 80, 2, 1, 8
+    _, k, _ = inputs.random_qkv(B, L, Hq, Hkv, d, seed=49)
+    got = orc.lse_rows(np.zeros((B, L, Hq, d)), f64(k), 0, L, w, s, 0.3)
+    counts = np.array([min(t + 1, w + s) for t in range(L)], dtype=np.float64)
+    np.testing.assert_allclose(got[0, :, 0], np.log(counts), rtol=0, atol=1e-15)
+    q, k, _ = inputs.random_qkv(B, L, Hq, Hkv, d, seed=50)
+    got = orc.lse_rows(f64(q), f64(k), 0, 1, w, s, 0.3)
+    np.testing.assert_allclose(got[0, 0], 0.3 * (f64(q)[0, 0] @ f64(k)[0, 0, 0]), rtol=0, atol=1e-14)
