@@ -1,30 +1,32 @@
 """Benchmark: SWA(w,s) prefill useful TFLOP/s + decode tokens/s on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  * prefill of the Llama-3.1-8B-shaped SWA(64,4) workload (B=1, L=4096, Hq=32, Hkv=8,
-    d=128, bf16 inputs N(0,1)*0.5, sink keys x4, fp32 output), one swa_prefill launch;
-  * 256 decode tokens of the SWA(64,4) ring-cache workload at batch 64 (Hq=32, Hkv=8,
-    d=128), each token one swa_append_decode_step (append + attend in one launch), positions
-    2^18 .. 2^18+255,
-    captured once in a HIP graph and replayed.
-Inputs are resident in HBM before the timed region.  The timed region is bracketed by
-torch.cuda.synchronize(); inside it, each prefill kernel stamps a pair of HIP events with
-its own start and end (swa_prefill_timed), and HIP events on the stream bracket every
-decode replay.
+  * prefill of the Mistral-7B-shaped workload (B=1, L=16384, Hq=32, Hkv=8, d=128, SWA(4096,4),
+    bf16 N(0,1) inputs, fp32 output), one swa_prefill launch, with L2 and the Infinity Cache
+    evicted first (a 512 MiB buffer overwritten) so that q, k and v come from HBM;
+  * 256 decode tokens of the SWA(64,4) ring-cache workload at batch 64 (Hq=32, Hkv=8, d=128),
+    each token one swa_append_decode_step (append + attend in one launch), positions
+    2^18 .. 2^18+255, the steps rotating over 32 independent caches (570 MB, over twice the
+    Infinity Cache, so every step reads its cache from HBM), captured once in a HIP graph.
+Inputs are resident in HBM before the timed region, which is bracketed by
+torch.cuda.synchronize(); inside it, the prefill kernel stamps a pair of HIP events with its own
+start and end (swa_prefill_timed), and HIP events on the stream bracket every decode replay.
 
 Printed JSON line (one):
-  value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time
-  decode           tokens/s of the decode leg and its HBM figures; other_batches: the same
-                   decode graph timed alone at batch 1, batch 1024, and batch 64 with the steps
-                   rotating over 32 caches (570 MB, so every step reads HBM), outside the steps;
-                   kv_* counts the K/V bytes read, all_bytes_* also q, the new token's K/V
-                   (read, and written to the cache) and the fp32 output
-  prefill.cold_*   the prefill with L2 and Infinity Cache evicted before each launch
-  roofline         the prefill kernel (dominant kernel of a step): algorithmic bytes per
-                   launch / mean launch time, against 8 TB/s (the workload is HBM-bound:
-                   38.5 useful flop per algorithmic byte, far below the 315 flop/byte ridge)
-  cpu_baseline     the fp64 oracle timed on host cores on the same prefill workload
-                   (whole passes, repeated for at least 10 s)
+  value            prefill useful TFLOP/s = 4*d*Hq*B*sum_t |A(t)| / mean prefill kernel time (cold)
+  roofline         the prefill kernel against the bf16 dense MFMA peak (this workload does ~2050
+                   useful flop per algorithmic byte, far above the 315 flop/byte ridge); traffic:
+                   HBM bytes per launch from the committed counter summary of the same kernel source
+  decode           tokens/s of the decode leg (graph replay) and its KV bandwidth; kernel_only: the
+                   same launches made one by one, each stamped by its own dispatch
+                   (swa_append_decode_step_timed); secondary figures: the cache-resident set, batch
+                   1 and batch 1024
+  roofline_decode  the decode kernel against HBM peak: graph step and kernel-only
+  prefill.others   the other prefill workloads (Llama SWA(64,4), the window sweep), cold and warm,
+                   with the fraction of their attainable roofline min(MFMA peak, AI x HBM peak)
+  cpu_baseline     the fp64 oracle timed on the host cores on a bounded sample of the same
+                   prefill workload (the last rows of the sequence, every head), all allowed
+                   threads and one thread
 """
 from __future__ import annotations
 
@@ -72,7 +74,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_swa64_4", help="prefill workload name")
+    ap.add_argument("--workload", default="mistral7b_w4096_s4", help="prefill workload of the step")
+    ap.add_argument("--other-workloads", default="llama8b_swa64_4,sweep_w512_s4,sweep_w256_s4,sweep_w128_s4",
+                    help="secondary prefill workloads, timed cold and warm outside the steps")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-tokens", type=int, default=256)
     ap.add_argument("--decode-start", type=int, default=2 ** 18)
@@ -88,7 +92,9 @@ def parse():
     ap.add_argument("--chunked", default="", help="only time this prefill workload fed in chunks (swa_prefill_chunk)")
     ap.add_argument("--chunk", type=int, default=4096, help="with --chunked: tokens per chunk")
     ap.add_argument("--compare-full", action="store_true", help="only time SWA against full causal attention")
-    ap.add_argument("--cache-sets", type=int, default=1, help="with --decode-only: caches the steps rotate over")
+    ap.add_argument("--cache-sets", type=int, default=32, help="caches the decode steps rotate over")
+    ap.add_argument("--eager", action="store_true",
+                    help="with --decode-only: launch the steps one by one, each stamped by its dispatch")
     ap.add_argument("--model-sweep", action="store_true",
                     help="only time decode of a 4-layer decoder (Llama-3.1-8B layer shape, batch 1) against context")
     ap.add_argument("--model-layers", type=int, default=4)
@@ -108,26 +114,54 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 3}))
 
 
-def cpu_baseline(wl, q, k, v, threads: int, min_seconds: float = 10.0):
-    """The oracle as it stands on the host cores: whole passes of the prefill workload,
-    repeated until at least min_seconds of CPU work."""
+def host_cpu():
+    """(logical CPUs the process may use, CPU model name) of this host."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
+
+
+def cpu_baseline(wl, q, k, v, threads: int, target_s: float = 10.0):
+    """The oracle as it stands on the host cores, on a bounded sample of the prefill workload:
+    the last R rows of every sequence and head (rows whose window is full), R sized from a short
+    calibration so that the sample takes about target_s; then the same with one thread on a
+    smaller sample.  Useful TFLOP/s of the sample, the workload's own unit."""
     from oracle import oracle as orc
     from sliding_window_attention_02_amd import accounting as acc
 
-    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.prefill(qd, kd, vd, wl.w, wl.s, wl.scale, wl.conv, nthreads=threads)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
     w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
-    flops = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s) * passes
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} whole passes of the {wl.name} prefill (B={wl.B}, L={wl.L}, Hq={wl.Hq}, "
-                      f"Hkv={wl.Hkv}, d={wl.d}, SWA({wl.w},{wl.s})) in fp64, {dt:.1f} s"}
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+
+    def run(rows: int, nth: int):
+        t0 = time.perf_counter()
+        orc.prefill_rows(qd, kd, vd, wl.L - rows, wl.L, wl.w, wl.s, wl.scale, wl.conv, nthreads=nth)
+        dt = time.perf_counter() - t0
+        pairs = sum(min(t + 1, w_loc + wl.s) for t in range(wl.L - rows, wl.L)) * wl.Hq * wl.B
+        return 4 * wl.d * pairs / dt / 1e12, dt
+
+    def sized(nth: int, budget: float, first: int):
+        tf, dt = run(first, nth)
+        rows = max(first, min(wl.L, int(first * budget / max(dt, 1e-3))))
+        if rows > first:
+            tf, dt = run(rows, nth)
+        return tf, dt, rows
+
+    tf_n, dt_n, rows_n = sized(threads, target_s, 32)
+    tf_1, dt_1, rows_1 = sized(1, target_s / 2, 4)
+    nproc, model = host_cpu()
+    return {"value": round(tf_n, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows {wl.L - rows_n}..{wl.L - 1} of the {wl.name} prefill (B={wl.B}, every one of "
+                      f"Hq={wl.Hq} heads, d={wl.d}, SWA({wl.w},{wl.s}), fp64 C oracle), {dt_n:.1f} s on {threads} "
+                      f"threads; useful flops of the sample / time",
+            "single_thread": {"value": round(tf_1, 6), "rows": rows_1, "seconds": round(dt_1, 2)},
+            "host_nproc": nproc, "cpu_model": model}
 
 
 def decode_graph(swa, inputs, dw, B: int, T: int, P: int, dev, n_sets: int = 1):
@@ -217,6 +251,50 @@ def decode_point(swa, inputs, acc, dw, B: int, T: int, P: int, dev, reps: int = 
     if n_sets > 1:
         rec["cache_sets"] = n_sets
     return rec
+
+
+def decode_kernel_only(swa, inputs, acc, dw, B: int, T: int, P: int, dev, n_sets: int = 32):
+    """The decode launches of decode_graph made one by one (no graph), each stamped with its own
+    kernel start and end by its dispatch (swa_append_decode_step_timed): mean kernel time and the
+    KV bandwidth it implies."""
+    import torch
+
+    w_loc = dw.w if dw.conv == 0 else dw.w - dw.s
+    gen = dict(B=B, Hkv=dw.Hkv, d=dw.d, std=dw.std, sink_boost_n=dw.sink_boost_n, sink_boost=dw.sink_boost)
+    kc, vc = swa.alloc_cache(B, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    ws = swa.alloc_workspace(B, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv, device=dev)
+    lo = max(dw.s, P - w_loc)
+    seed_pos = list(range(min(dw.s, P))) + list(range(lo, P))
+    sk, sv = inputs.kv_span(dw.seed, seed_pos, **gen)
+    n_sink = min(dw.s, P)
+    swa.kv_append(kc, vc, sk[:, :n_sink].contiguous().to(dev), sv[:, :n_sink].contiguous().to(dev),
+                  torch.zeros(B, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    swa.kv_append(kc, vc, sk[:, n_sink:].contiguous().to(dev), sv[:, n_sink:].contiguous().to(dev),
+                  torch.full((B,), lo, dtype=torch.int64, device=dev), dw.w, dw.s, dw.conv)
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n_sets - 1)]
+    n_pos = (T + n_sets - 1) // n_sets
+    dq = torch.stack([inputs.q_at(dw.seed, P + i, B, dw.Hq, dw.d, dw.std) for i in range(n_pos)]).to(dev)
+    kvs = [inputs.kv_at(dw.seed, P + i, **gen) for i in range(n_pos)]
+    dk = torch.stack([x[0] for x in kvs]).to(dev)
+    dv = torch.stack([x[1] for x in kvs]).to(dev)
+    dpos = (P + torch.arange(n_pos, dtype=torch.int64)).repeat_interleave(B).view(n_pos, B).to(dev)
+    out = torch.empty((B, dw.Hq, dw.d), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(T)] for _ in range(2)]
+    for e in evs[0] + evs[1]:
+        e.record()
+    torch.cuda.synchronize()
+    for i in range(T):
+        ck, cv = caches[i % n_sets]
+        j = i // n_sets
+        swa.append_decode_step(dq[j], ck, cv, dk[j], dv[j], dpos[j], dw.w, dw.s, dw.scale, dw.conv, out=out,
+                               workspace=ws, events=(evs[0][i], evs[1][i]))
+    torch.cuda.synchronize()
+    us = sorted(evs[0][i].elapsed_time(evs[1][i]) * 1e3 for i in range(T))
+    mean = sum(us) / T
+    kv = acc.decode_kv_bytes(B, dw.Hkv, dw.d, acc.decode_keys(P, w_loc, dw.s))
+    return {"B": B, "launches": T, "cache_sets": n_sets, "mean_kernel_us": round(mean, 3),
+            "median_kernel_us": round(us[T // 2], 3), "kv_gb_per_s": round(kv / (mean * 1e-6) / 1e9, 2),
+            "frac_of_hbm_peak": round(kv / (mean * 1e-6) / 1e9 / acc.PEAK_HBM_GBS, 5)}
 
 
 def flush_buffer(dev, mib: int = 512):
@@ -508,15 +586,79 @@ def model_sweep(args, dev):
 
 
 def decode_only(args, dev):
-    """--decode-only B: time the decode graph at batch B and print one JSON line."""
+    """--decode-only B: time the decode graph at batch B (or, with --eager, the same launches one by
+    one, each stamped by its own dispatch) and print one JSON line."""
     import sliding_window_attention_02_amd as swa
     from sliding_window_attention_02_amd import accounting as acc
     from sliding_window_attention_02_amd import inputs
 
     dw = inputs.decode_workloads()["decode_swa64_4_b64"]
-    rec = decode_point(swa, inputs, acc, dw, args.decode_only, args.decode_tokens, args.decode_start, dev,
-                       reps=args.steps, n_sets=args.cache_sets)
+    if args.eager:
+        rec = decode_kernel_only(swa, inputs, acc, dw, args.decode_only, args.decode_tokens, args.decode_start, dev,
+                                 n_sets=args.cache_sets)
+    else:
+        rec = decode_point(swa, inputs, acc, dw, args.decode_only, args.decode_tokens, args.decode_start, dev,
+                           reps=args.steps, n_sets=args.cache_sets)
     print(json.dumps(rec), flush=True)
+
+
+def decode_label(swa, dw, B: int) -> str:
+    """The decode kernel launched for workload dw at batch B (swa_decode_describe)."""
+    i = swa.decode_describe(B, dw.Hq, dw.Hkv, dw.d, dw.w, dw.s, dw.conv)
+    nch = -(-i["slots_per_split"] // 32)
+    how = (f"{i['waves_per_workgroup']} waves per workgroup, one 32-slot chunk each, merged in LDS"
+           if i["waves_per_workgroup"] > 1 else f"one wave per split of {i['slots_per_split']} slots")
+    merge = ", plus merge_kernel" if i["merge_launch"] else ""
+    return (f"decode_kernel<{dw.d}, {1 if i['waves_per_workgroup'] > 1 else nch}, {i['waves_per_workgroup']}> "
+            f"(fused append + attend; {how}; {i['workgroups']} workgroups{merge})")
+
+
+def describe(swa, wl):
+    """The prefill kernel launched for workload wl (swa_prefill_describe) and its label."""
+    info = swa.prefill_describe(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.s, wl.conv)
+    names = {0: "tile walk", 1: "resident form", 2: "wide resident form"}
+    info["kernel"] = f"prefill_kernel<{wl.d}, {info['form']}> ({names[info['form']]}, " \
+                     f"{info['tokens_per_tile']}-token q-tiles x {info['heads_per_tile']} q-heads)"
+    return info
+
+
+def prefill_figures(acc, wl, ms_list):
+    """Mean/p10/p90 launch time and the throughput figures of one prefill workload."""
+    w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+    useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+    algo = acc.prefill_bytes(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d)
+    ms = sorted(ms_list)
+    mean = sum(ms) / len(ms)
+    tf = useful / (mean * 1e-3) / 1e12
+    return {"mean_launch_us": round(mean * 1e3, 3), "p10_us": round(ms[len(ms) // 10] * 1e3, 3),
+            "p90_us": round(ms[(9 * len(ms)) // 10] * 1e3, 3), "useful_tflops": round(tf, 3),
+            "frac_of_bf16_mfma_peak": round(tf / acc.PEAK_BF16_TFLOPS, 5),
+            "algorithmic_gb_per_s": round(algo / (mean * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(algo / (mean * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 5),
+            "frac_of_attainable": round(tf / acc.attainable_tflops(useful, algo), 5)}
+
+
+def other_prefills(swa, inputs, acc, names, dev, reps: int, flush):
+    """Secondary prefill workloads, each timed cold (caches evicted before every launch) and warm."""
+    import torch
+
+    recs = []
+    for name in names:
+        wl = inputs.prefill_workloads()[name]
+        q, k, v = inputs.prefill_inputs(wl)
+        qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+        out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+        cold = prefill_timing(swa, wl, qg, kg, vg, out, reps, 2, flush)
+        warm = prefill_timing(swa, wl, qg, kg, vg, out, reps, 2)
+        w_loc = wl.w if wl.conv == 0 else wl.w - wl.s
+        useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
+        algo = acc.prefill_bytes(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d)
+        recs.append({"workload": name, "kernel": describe(swa, wl)["kernel"],
+                     "bound": "mfma" if acc.attainable_tflops(useful, algo) >= acc.PEAK_BF16_TFLOPS else "hbm",
+                     "cold": prefill_figures(acc, wl, cold), "warm": prefill_figures(acc, wl, warm)})
+        del qg, kg, vg, out
+        torch.cuda.empty_cache()
+    return recs
 
 
 def main():
@@ -540,21 +682,12 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.prefill_only:
-        prefill_only(args, dev)
-        return
-    if args.decode_only:
-        decode_only(args, dev)
-        return
-    if args.chunked:
-        chunked_only(args, dev)
-        return
-    if args.model_sweep:
-        model_sweep(args, dev)
-        return
-    if args.compare_full:
-        compare_full(args, dev)
-        return
+    modes = [(args.prefill_only, prefill_only), (args.decode_only, decode_only), (args.chunked, chunked_only),
+             (args.model_sweep, model_sweep), (args.compare_full, compare_full)]
+    for flag, fn in modes:
+        if flag:
+            fn(args, dev)
+            return
 
     # ---------------------------------------------------------------- prefill inputs
     wl = inputs.prefill_workloads()[args.workload]
@@ -564,26 +697,28 @@ def main():
     out = torch.empty((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device=dev)
     useful = acc.useful_flops(wl.B, wl.Hq, wl.L, wl.d, w_loc, wl.s)
     algo_bytes = acc.prefill_bytes(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d)
-    executed = 4 * wl.d * wl.B * acc.prefill_executed_pairs(wl.L, wl.Hq, wl.Hkv, w_loc, wl.s)
+    info = describe(swa, wl)
+    executed = 4 * wl.d * info["executed_pairs"]
+    flush = flush_buffer(dev)
 
     # ---------------------------------------------------------------- decode inputs
     dw = inputs.decode_workloads()["decode_swa64_4_b64"]
-    DB, T, P = args.decode_batch, args.decode_tokens, args.decode_start
+    DB, T, P, NS = args.decode_batch, args.decode_tokens, args.decode_start, args.cache_sets
     dw_loc = dw.w if dw.conv == 0 else dw.w - dw.s
-    graph, restore = decode_graph(swa, inputs, dw, DB, T, P, dev)
+    graph, restore = decode_graph(swa, inputs, dw, DB, T, P, dev, n_sets=NS)
+
     def step(evs=None, i=0):
-        # Decode replay first, then the prefill: the prefill's start event is always queued
-        # behind GPU work, so its interval never includes host launch latency.
+        # The decode caches back to their state after P-1, the decode graph, then the caches evicted
+        # and the prefill (its dispatch stamps its own start and end).
         restore()
         if evs is not None:
             evs[2][i].record()
         graph.replay()
         if evs is not None:
             evs[3][i].record()
-            # The prefill kernel's dispatch stamps its own start/end into these events.
-            swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out, events=(evs[0][i], evs[1][i]))
-        else:
-            swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out)
+        flush.fill_(float(i))
+        swa.prefill(qg, kg, vg, wl.w, wl.s, wl.scale, wl.conv, out=out,
+                    events=None if evs is None else (evs[0][i], evs[1][i]))
 
     for _ in range(args.warmup):
         step()
@@ -602,34 +737,30 @@ def main():
 
     pre_ms = [evs[0][i].elapsed_time(evs[1][i]) for i in range(K)]
     dec_ms = [evs[2][i].elapsed_time(evs[3][i]) for i in range(K)]
-    pre_mean = sum(pre_ms) / K
+    pre = prefill_figures(acc, wl, pre_ms)
+    tflops = pre["useful_tflops"]
+    pre_mean_s = pre["mean_launch_us"] * 1e-6
     dec_mean = sum(dec_ms) / K
-    pre_sorted = sorted(pre_ms)
-    tflops = useful / (pre_mean * 1e-3) / 1e12
-    achieved_gbs = algo_bytes / (pre_mean * 1e-3) / 1e9
+    dec_step_us = dec_mean * 1e3 / T
+    dec_kv_bytes = acc.decode_kv_bytes(DB, dw.Hkv, dw.d, acc.decode_keys(P, dw_loc, dw.s))
+    dec_gbs = dec_kv_bytes / (dec_step_us * 1e-6) / 1e9
+    dec_all_gbs = (dec_kv_bytes + acc.decode_other_bytes(DB, dw.Hq, dw.Hkv, dw.d)) / (dec_step_us * 1e-6) / 1e9
     traffic = measured_traffic(wl.name)
 
-    dec_tokens_s = T * DB / (dec_mean * 1e-3)
-    n_keys = acc.decode_keys(P, dw_loc, dw.s)
-    dec_kv_bytes = acc.decode_kv_bytes(DB, dw.Hkv, dw.d, n_keys)
-    dec_step_us = dec_mean * 1e3 / T
-    dec_gbs = dec_kv_bytes / (dec_step_us * 1e-6) / 1e9
-
-    # Other batch sizes of the same decode workload, outside the timed steps: batch 1 (the
-    # other configured batch) and batch 1024, where the cache (285 MB) no longer fits the
-    # Infinity Cache and the step is bound by HBM rather than by latency.
-    points = []
-    cold_mean = None
+    warm = kernel_only = None
+    points, others = [], []
     if not args.no_extras:
-        for b, t in ((1, 256), (1024, 32)):
-            points.append(decode_point(swa, inputs, acc, dw, b, t, P, dev))
-        # Batch 64 with the steps rotating over 32 caches (570 MB, over twice the Infinity
-        # Cache): every step reads its cache from HBM.
-        points.append(decode_point(swa, inputs, acc, dw, DB, T, P, dev, n_sets=32))
-        # The same prefill with the caches evicted (a 512 MiB buffer overwritten) before each
-        # launch, so its inputs come from HBM rather than from the Infinity Cache.
-        cold_ms = prefill_timing(swa, wl, qg, kg, vg, out, max(10, K // 2), 2, flush_buffer(dev))
-        cold_mean = sum(cold_ms) / len(cold_ms)
+        warm = prefill_figures(acc, wl, prefill_timing(swa, wl, qg, kg, vg, out, K, 3))
+        kernel_only = decode_kernel_only(swa, inputs, acc, dw, DB, T, P, dev, n_sets=NS)
+        for b, t, n in ((DB, T, 1), (1, 256, 1), (1024, 32, 1)):
+            rec = decode_point(swa, inputs, acc, dw, b, t, P, dev, n_sets=n)
+            rec["note"] = {DB: "one cache set: the working set stays in the 256 MB Infinity Cache",
+                           1: "one sequence: launch-latency bound", 1024: "285 MB of KV per step, read from HBM"}[b]
+            points.append(rec)
+        del qg, kg, vg, out
+        torch.cuda.empty_cache()
+        others = other_prefills(swa, inputs, acc, [n for n in args.other_workloads.split(",") if n], dev,
+                                max(10, K // 2), flush)
 
     base = None
     if not args.no_cpu_baseline:
@@ -650,61 +781,56 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name} prefill + decode_swa64_4_b{DB} ({T} tokens per step)",
+            "workload": f"{wl.name} prefill (caches evicted first) + decode_swa64_4_b{DB} ({T} tokens per step "
+                        f"over {NS} rotating caches)",
             "prefill": {"B": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "w": wl.w, "s": wl.s,
                         "conv": "additive" if wl.conv == 0 else "total", "inputs": f"bf16 N(0,1)*{wl.std}",
                         "out": "fp32"},
             "decode": {"B": DB, "Hq": dw.Hq, "Hkv": dw.Hkv, "d": dw.d, "w": dw.w, "s": dw.s,
-                       "positions": [P, P + T - 1], "tokens_per_step": T, "hip_graph": True},
+                       "positions": [P, P + (T + NS - 1) // NS - 1], "tokens_per_step": T, "cache_sets": NS,
+                       "hip_graph": True},
         },
-        "prefill": {
-            "mean_launch_us": round(pre_mean * 1e3, 3),
-            "p10_us": round(pre_sorted[K // 10] * 1e3, 3),
-            "p90_us": round(pre_sorted[(9 * K) // 10] * 1e3, 3),
-            "useful_tflops": round(tflops, 3),
-            "frac_of_bf16_mfma_peak": round(tflops / acc.PEAK_BF16_TFLOPS, 5),
-            "executed_mfma_tflops": round(executed / (pre_mean * 1e-3) / 1e12, 3),
-            "cold_mean_launch_us": round(cold_mean * 1e3, 3) if cold_mean else None,
-            "cold_useful_tflops": round(useful / (cold_mean * 1e-3) / 1e12, 3) if cold_mean else None,
+        "prefill": dict(pre, **{
+            "kernel": info["kernel"],
+            "caches": "evicted before every launch",
+            "executed_mfma_tflops": round(executed / pre_mean_s / 1e12, 3),
+            "executed_over_useful": round(executed / useful, 4),
             "useful_gflop_per_launch": round(useful / 1e9, 4),
             "algorithmic_mb_per_launch": round(algo_bytes / 1e6, 3),
-        },
+            "warm": warm,
+            "others": others,
+        }),
         "decode": {
-            "tokens_per_s": round(dec_tokens_s, 1),
+            "tokens_per_s": round(T * DB / (dec_mean * 1e-3), 1),
             "us_per_token_step": round(dec_step_us, 3),
             "kv_bytes_per_step": dec_kv_bytes,
             "kv_gb_per_s": round(dec_gbs, 2),
             "frac_of_hbm_peak": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
-            "note": "the 17.8 MB working set stays in the 256 MB Infinity Cache across steps",
-            "other_batches": points,
+            "all_bytes_frac_of_hbm_peak": round(dec_all_gbs / acc.PEAK_HBM_GBS, 5),
+            "kernel_only": kernel_only,
+            "other_points": points,
         },
         "roofline": {
-            # (SWA(64,4) with 32-token q-tiles needs at most four 32-key chunks per q-tile: the
-            # kernel's resident form)
-            "kernel": "prefill_kernel<128, 2> (wide resident form)",
-            "bound": "hbm",
-            "achieved": round(achieved_gbs, 2),
-            "peak": acc.PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / acc.PEAK_HBM_GBS, 5),
+            "kernel": info["kernel"],
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": acc.PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / acc.PEAK_BF16_TFLOPS, 5),
             "traffic": traffic,
         },
-        # The decode kernel takes most of the step's GPU time (256 one-token launches against one
-        # prefill), so its roofline is reported beside the prefill's: KV bytes per step over the
-        # per-step time of the graph (launch gap included).
+        # The decode half of the metric: KV bytes per step against HBM peak, over the per-step time
+        # of the graph (dispatch gaps included) and over the kernel alone.
         "roofline_decode": {
-            "kernel": "decode_kernel<128, 1, 3> (fused append + attend; three waves, one 32-slot chunk each)",
+            "kernel": decode_label(swa, dw, DB),
             "bound": "hbm",
             "batch": DB,
             "achieved": round(dec_gbs, 2),
             "peak": acc.PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / acc.PEAK_HBM_GBS, 5),
-            "note": "the batch-64 working set stays in the Infinity Cache and the step is latency-bound; "
-                    "at batch 1024 (other_batches) the same kernel streams its KV bytes from HBM",
-            "batch_1024": next(({"achieved": pt["kv_gb_per_s"], "frac": pt["frac_of_hbm_peak"],
-                                 "all_bytes_frac": pt["all_bytes_frac_of_hbm_peak"]}
-                                for pt in points if pt.get("B") == 1024 and "cache_sets" not in pt), None),
+            "kernel_only_achieved": None if kernel_only is None else kernel_only["kv_gb_per_s"],
+            "kernel_only_frac": None if kernel_only is None else kernel_only["frac_of_hbm_peak"],
         },
         "cpu_baseline": base,
     }

@@ -17,10 +17,10 @@ namespace swa {
 // The walk and index functions below run in the kernels and on the host (work accounting).
 #define SWA_HD __host__ __device__ __forceinline__
 
-// Element predicate of A(t).
+// Element predicate of A(t) (bitwise on the comparisons: no branches in the kernels' masks).
 SWA_HD bool key_allowed(int t, int i, int w_loc, int s)
 {
-    return i <= t && (i > t - w_loc || i < s);
+    return (i <= t) & ((i > t - w_loc) | (i < s));
 }
 
 // ----------------------------------------------------------------------------- prefill

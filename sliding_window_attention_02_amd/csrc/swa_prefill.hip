@@ -142,6 +142,18 @@ constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // cast is written inline: an implicit conversion (or a helper function) there makes the host
 // pass drop the kernel's launch stub.
 #define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+// The same pointer, opaque to the compiler: a direct load given it carries no alias information
+// about its LDS destination, so the compiler does not order later LDS reads after it.  Without
+// this, a read from one stage of a double buffer while loads into the other stage are in flight
+// (or any such read at a loop head) gets a wait for every outstanding vector-memory operation.
+// Every kernel here orders its loads and reads itself: counted waits on this wave's loads, then
+// a barrier for the other waves' loads.
+#define SWA_LDS_DMA_DST(p)                                                                        \
+    ({                                                                                           \
+        __attribute__((address_space(3))) void *lds_dma_dst_ = SWA_LDS_PTR(p);                   \
+        asm volatile("" : "+s"(lds_dma_dst_));                                                   \
+        lds_dma_dst_;                                                                            \
+    })
 
 // Output stores in whole 128-byte lines.  Lane (g, c) holds column c of a 16-column block of
 // O^T at d = 16 db + 4 g .. +3, so one plain store would write 64 bytes of each of 16 rows.  For
@@ -215,8 +227,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     constexpr int kLoadsPerWave = Lds<D>::kLoadsPerTile / (kThreads / 64);
     static_assert(kLoadsPerWave >= 1, "tile load split");
 
-    // Two buffers of (K tile, V tile), both row-major with swizzled 16-byte pieces.
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][kTileBytes];
+    // Two buffers of (K tile, V tile), both row-major with swizzled 16-byte pieces, one variable
+    // each: the reads then carry alias information that tells the compiler they do not depend on
+    // the loads in flight (whose LDS destinations are opaque to it).
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[2][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[2][kTileBytes];
+    auto ldsbuf = [&](int buf) __attribute__((always_inline)) -> unsigned char(*)[kTileBytes] {
+        return buf == 0 ? lds_b0 : lds_b1;  // (buf is a constant after inlining)
+    };
     // The wide form's fifth chunk slot (K, V); a token array in the other forms.
     constexpr int kChunkBytes = kChunkN * kRowBytes;
     __shared__ __attribute__((aligned(1024))) unsigned char lds5[2][WIDE ? kChunkBytes : 16];
@@ -308,9 +326,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kbase), 0, (int)kv_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t v_rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vbase), 0, (int)kv_bytes, 0x00020000);
+    // ... and over this (b, kv-head)'s sink and ring slots of the cache (chunked prefill).
+    const uint32_t cache_bytes = (uint32_t)(((size_t)a.s + a.w_loc) * D * 2);
+    const __amdgpu_buffer_rsrc_t kc_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.kc != nullptr ? a.kc + cache_base : a.k), 0, (int)cache_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vc_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.vc != nullptr ? a.vc + cache_base : a.v), 0, (int)cache_bytes, 0x00020000);
+    // Every load is a buffer load (a flat-encoded global load may, as far as the compiler knows,
+    // also touch LDS, after which it waits for all outstanding memory operations wherever it
+    // cannot prove otherwise) into an opaque LDS destination (SWA_LDS_DMA_DST): the kernel orders
+    // loads and LDS reads itself, with counted waits and barriers.
     auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
         constexpr int kv = decltype(kv_c)::value;
-        const uint16_t *base = kv ? vbase : kbase;
         const int last = a.L - 1;
         if (j0 >= a.n_cached && j0 + kTileN - 1 <= last) {
             // Every row of the tile is a key of k/v inside the sequence.
@@ -319,31 +346,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int j = wave_u * kLoadsPerWave + i;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs,
-                                                         SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
+                                                         SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]),
                                                          16, (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off, 0, 0);
             }
             return;
         }
+        // A tile past the sequence's end (rows past it read its last row: finite values, and such
+        // keys are always masked) or holding cached keys (their sink or ring slots): per-lane
+        // offsets, a cached key's lanes through the cache's resource (one more load instruction
+        // when the tile mixes the two, which only makes the counted waits stricter).
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int j = wave_u * kLoadsPerWave + i;
             const int row = kRowsPerLoad * j + lane / kPieces;
             const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
             const int key = min(j0 + row, last);
-            const uint16_t *src;
+            // (made opaque outside the per-lane branch, where it is still a scalar)
+            auto *const dst = SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]);
             if (key >= a.n_cached) {
-                src = base + (key - a.n_cached) * kv_row + piece * 8;
-            } else {  // a cached key: its sink or ring slot
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs, dst, 16,
+                                                         (int)((uint32_t)((key - a.n_cached) * kv_row + piece * 8) * 2u),
+                                                         0, 0, 0);
+            } else {
                 int slot = key;
                 if (key >= a.ns) {
                     const int r = a.ring0 + key - a.ns;
                     slot = a.s + (r >= a.w_loc ? r - a.w_loc : r);
                 }
-                src = (kv ? a.vc : a.kc) + cache_base + (size_t)slot * D + piece * 8;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? vc_rs : kc_rs, dst, 16,
+                                                         (int)((uint32_t)(slot * D + piece * 8) * 2u), 0, 0, 0);
             }
-            __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(src),
-                                             SWA_LDS_PTR(buf == 2 ? &lds5[kv][1024 * j] : &lds[buf][kv][1024 * j]),
-                                             16, 0, 0);
         }
     };
     // (tags as types, passed as temporaries: named tag objects captured by the lambdas below
@@ -410,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         auto slot_rows = [&](int k, int kv) __attribute__((always_inline)) -> const unsigned char * {
             if (WIDE && k == 4)
                 return &lds5[kv][0];
-            return &lds[k >> 1][kv][0] + (k & 1) * kChunkBytes;
+            return &ldsbuf(k >> 1)[kv][0] + (k & 1) * kChunkBytes;
         };
         // With every key of a 32-token half at hand the softmax needs no running maximum: all
         // scores, the exact column maximum, the probabilities, then O^T = V^T P^T.  hw is the half's
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int key = key0 + 4 * h + j;
-                        const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
+                        const bool ok = key_allowed(t, key, a.w_loc, a.s);
                         sr[k][h][j] = ok ? sr[k][h][j] : -INFINITY;
                     }
                     mx = fmaxf(fmaxf(mx, sr[k][h][0]), sr[k][h][1]);
@@ -580,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                             for (int j = 0; j < 4; ++j) {
                                 const int key = ti.j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
                                 const int t = tok[qb];
-                                const bool ok = (key <= t) & ((key > t - a.w_loc) | (key < a.s));
+                                const bool ok = key_allowed(t, key, a.w_loc, a.s);
                                 sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
                             }
                 }
@@ -696,12 +728,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     issue(nxt.j0, buf ^ 1, KRows());
                     issue(nxt.j0, buf ^ 1, VRows());
                 }
-                scores(sacc[0], lds[buf][0], cur, Generic());
+                scores(sacc[0], ldsbuf(buf)[0], cur, Generic());
                 if (__any(tile_max(sacc[0], cur, Generic(), alpha)))
                     rescale(alpha);
                 bf16x8 pf[2][2];
                 probs(sacc[0], cur, Generic(), pf);
-                accumulate(pf, lds[buf][1], cur, Generic());
+                accumulate(pf, ldsbuf(buf)[1], cur, Generic());
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
                 __syncthreads();
                 cur = nxt;
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 issue(jm + kTileN, 1, KRows());
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();
-            scores(sacc[0], lds[0][0], full, Fast());
+            scores(sacc[0], ldsbuf(0)[0], full, Fast());
             if (__any(tile_max(sacc[0], full, Fast(), alpha)))
                 rescale(alpha);
 
@@ -742,10 +774,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 if (m + 2 < nm)
                     issue(jm + (m + 2) * kTileN, buf, KRows());
                 issue(jm + (m + 1) * kTileN, buf ^ 1, VRows());
-                scores(sacc[buf ^ 1], lds[buf ^ 1][0], full, Fast());
+                scores(sacc[buf ^ 1], ldsbuf(buf ^ 1)[0], full, Fast());
                 bf16x8 pf[2][2];
                 probs(sacc[buf], full, Fast(), pf);
-                accumulate(pf, lds[buf][1], full, Fast());
+                accumulate(pf, ldsbuf(buf)[1], full, Fast());
                 const bool grow = tile_max(sacc[buf ^ 1], full, Fast(), alpha);
                 if (__any(grow))
                     rescale(alpha);
@@ -757,7 +789,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 __syncthreads();
                 bf16x8 pf[2][2];
                 probs(sacc[buf], full, Fast(), pf);
-                accumulate(pf, lds[buf][1], full, Fast());
+                accumulate(pf, ldsbuf(buf)[1], full, Fast());
             };
             int m = 0;
             for (; m + 2 < nm; m += 2) {

@@ -41,6 +41,9 @@ MASK_CASES = [
     (2000, 4, 1, 68, 4, 1), (161, 8, 2, 64, 4, 0),
     # the resident form (two q-heads per kv-head, 64-token q-tiles as one pass)
     (700, 8, 4, 30, 2, 0), (333, 2, 1, 1, 32, 0), (1025, 6, 3, 33, 0, 0),
+    # the wide resident form over 2,000+ tokens and 8-16 kv-heads (three window chunks and no
+    # sinks, the total-window convention, sinks in a chunk of their own)
+    (2085, 32, 8, 96, 0, 0), (2048, 32, 8, 68, 4, 1), (2100, 64, 16, 33, 30, 0),
 ]
 
 
@@ -122,6 +125,17 @@ PARITY = [
     (3, 161, 8, 2, 64, 64, 4, 0, 1.0, 4),
 ]
 
+# Many 32- and 64-token q-tiles per kv-head in the resident forms: ragged last q-tiles, both head
+# sizes, both window conventions, sinks in a chunk of their own, batches.
+RESIDENT_LARGE = [
+    # B, L, Hq, Hkv, d, w, s, conv, std, boost_n
+    (1, 4113, 32, 8, 128, 64, 4, 0, 1.0, 4),
+    (4, 1100, 16, 4, 64, 40, 8, 0, 1.0, 4),
+    (2, 2053, 32, 8, 128, 96, 0, 0, 1.0, 0),
+    (1, 2048, 32, 8, 128, 68, 4, 1, 1.0, 4),
+    (2, 4096, 32, 8, 64, 33, 30, 0, 0.5, 4),
+]
+
 
 def check_close(got, ref, what, parity=None):
     err = np.abs(got - ref)
@@ -140,6 +154,18 @@ def test_prefill_matches_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost, parity
     out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, scale, conv).cpu().numpy()
     ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
     check_close(out, ref, "prefill parity cases (all elements)", parity)
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,w,s,conv,std,boost", RESIDENT_LARGE)
+def test_resident_forms_large_match_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost, parity):
+    info = swa.prefill_describe(B, Hq, Hkv, L, d, w, s, conv)
+    say("resident large", B, L, Hq, Hkv, d, w, s, conv, info)
+    assert info["form"] == 2
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=L + 31 * w + s, std=std, sink_boost_n=boost, sink_boost=4.0)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, scale, conv).cpu().numpy()
+    ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
+    check_close(out, ref, "prefill resident forms, large (all elements)", parity)
 
 
 def test_tiny_workload_full_parity(parity):
