@@ -211,8 +211,10 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
 }
 
 // FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots), 2 wide resident
-// (64-token q-tiles taken as two 32-token halves per wave, five chunk slots).
-template <int D, int FORM>
+// (64-token q-tiles taken as two 32-token halves per wave, five chunk slots).  CACHED: the key
+// sequence begins with a.n_cached keys held in the sink+ring cache (chunked prefill); the
+// whole-sequence instantiation has no cache code at all.
+template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     constexpr bool RES = FORM != 0;
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         return (gh < a.Gw && tk < a.L) ? off : kDropOffset;
     };
     const int kv_row = a.Hkv * D;  // elements between consecutive positions
-    const int L_in = a.L - a.n_cached;  // key rows held by k and v
+    const int L_in = a.L - (CACHED ? a.n_cached : 0);  // key rows held by k and v
     const uint16_t *kbase = a.k + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
     const uint16_t *vbase = a.v + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
     const size_t cache_base = ((size_t)bc.b * a.Hkv + bc.hkv) * ((size_t)a.s + a.w_loc) * D;
@@ -329,9 +331,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     // ... and over this (b, kv-head)'s sink and ring slots of the cache (chunked prefill).
     const uint32_t cache_bytes = (uint32_t)(((size_t)a.s + a.w_loc) * D * 2);
     const __amdgpu_buffer_rsrc_t kc_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.kc != nullptr ? a.kc + cache_base : a.k), 0, (int)cache_bytes, 0x00020000);
+        const_cast<uint16_t *>(CACHED ? a.kc + cache_base : a.k), 0, (int)cache_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vc_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.vc != nullptr ? a.vc + cache_base : a.v), 0, (int)cache_bytes, 0x00020000);
+        const_cast<uint16_t *>(CACHED ? a.vc + cache_base : a.v), 0, (int)cache_bytes, 0x00020000);
     // Every load is a buffer load (a flat-encoded global load may, as far as the compiler knows,
     // also touch LDS, after which it waits for all outstanding memory operations wherever it
     // cannot prove otherwise) into an opaque LDS destination (SWA_LDS_DMA_DST): the kernel orders
@@ -339,9 +341,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
         constexpr int kv = decltype(kv_c)::value;
         const int last = a.L - 1;
-        if (j0 >= a.n_cached && j0 + kTileN - 1 <= last) {
+        const int n_cached = CACHED ? a.n_cached : 0;
+        if (j0 >= n_cached && j0 + kTileN - 1 <= last) {
             // Every row of the tile is a key of k/v inside the sequence.
-            const int tile_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - a.n_cached) * (uint32_t)kv_row * 2u));
+            const int tile_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - n_cached) * (uint32_t)kv_row * 2u));
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int j = wave_u * kLoadsPerWave + i;
@@ -350,6 +353,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                                                          16, (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off, 0, 0);
             }
             return;
+        }
+        if (CACHED && j0 >= a.ns && j0 + kTileN - 1 < n_cached) {
+            // Every row of the tile is a cached window key.  When their ring slots run on without
+            // wrapping, the tile is consecutive cache rows: the same lane offsets with the cache's
+            // row stride (d elements instead of Hkv d), the first slot as the scalar offset.
+            int r0 = a.ring0 + (j0 - a.ns);
+            r0 = r0 >= a.w_loc ? r0 - a.w_loc : r0;
+            if (r0 + kTileN <= a.w_loc) {
+                const int slot_off = __builtin_amdgcn_readfirstlane((a.s + r0) * D * 2);
+#pragma unroll
+                for (int i = 0; i < kLoadsPerWave; ++i) {
+                    const int j = wave_u * kLoadsPerWave + i;
+                    const uint32_t row = (uint32_t)(kRowsPerLoad * j + lane / kPieces);
+                    const uint32_t off = (kv ? ld_voff[i] : ld_koff[i]) - row * (uint32_t)((kv_row - D) * 2);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]),
+                        16, (int)off, slot_off, 0, 0);
+                }
+                return;
+            }
         }
         // A tile past the sequence's end (rows past it read its last row: finite values, and such
         // keys are always masked) or holding cached keys (their sink or ring slots): per-lane
@@ -363,9 +386,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             const int key = min(j0 + row, last);
             // (made opaque outside the per-lane branch, where it is still a scalar)
             auto *const dst = SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]);
-            if (key >= a.n_cached) {
+            if (!CACHED || key >= n_cached) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs, dst, 16,
-                                                         (int)((uint32_t)((key - a.n_cached) * kv_row + piece * 8) * 2u),
+                                                         (int)((uint32_t)((key - n_cached) * kv_row + piece * 8) * 2u),
                                                          0, 0, 0);
             } else {
                 int slot = key;
@@ -999,10 +1022,12 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    void (*const kernels[2][3])(PrefillArgs) = {
-        {prefill_kernel<64, 0>, prefill_kernel<64, 1>, prefill_kernel<64, 2>},
-        {prefill_kernel<128, 0>, prefill_kernel<128, 1>, prefill_kernel<128, 2>}};
-    void (*kern)(PrefillArgs) = kernels[d == 128 ? 1 : 0][form];
+    void (*const kernels[2][2][3])(PrefillArgs) = {
+        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>, prefill_kernel<64, 2, false>},
+         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>, prefill_kernel<128, 2, false>}},
+        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>, prefill_kernel<64, 2, true>},
+         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>, prefill_kernel<128, 2, true>}}};
+    void (*kern)(PrefillArgs) = kernels[a.n_cached > 0 ? 1 : 0][d == 128 ? 1 : 0][form];
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
     else

@@ -52,6 +52,12 @@ CASES = [
     # four q-heads per kv-head, chunks starting on 32-key but not 64-key boundaries (the wide
     # resident form's 64-token q-tiles over cached keys)
     (1, 16, 4, 128, 64, 4, 0, [32, 96, 32, 50]),
+    # windows over 64 keys: whole 64-key tiles of cached window keys, read as consecutive ring
+    # slots, next to tiles whose slots wrap around the ring's end (both head sizes, both window
+    # conventions, chunks longer and shorter than the window)
+    (1, 8, 2, 128, 200, 4, 0, [300, 150, 200, 77]),
+    (2, 16, 4, 64, 160, 8, 1, [70, 200, 130, 100]),
+    (1, 16, 4, 128, 512, 4, 0, [512, 512, 300]),
 ]
 
 
