@@ -89,10 +89,8 @@ int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, i
  * kernel form, its tile geometry and the work its matrix cores do.
  *
  *   form            0: the tile walk (64-key tiles; edge tiles masked, middle tiles unmasked);
- *                   1: resident (every 32-key chunk a 32-token q-tile needs held in LDS at once,
- *                      at most four: windows with ceil((w_loc-1)/32) + ceil(s/32) <= 3);
- *                   2: wide resident (form 1 for 64-token q-tiles taken as two 32-token halves,
- *                      when four q-heads share a kv-head)
+ *                   1: resident (every 32-key chunk a q-tile needs held in LDS at once, at most
+ *                      four: Tm/32 + ceil((w_loc-1)/32) + ceil(s/32) <= 4 for Tm-token q-tiles)
  *   tokens_per_tile query tokens per workgroup; heads_per_tile q-heads per workgroup
  *   workgroups      grid size
  *   executed_pairs  (query row, key) pairs whose scores and value products the matrix cores
@@ -341,8 +339,8 @@ const char *swa_last_error(void);
  * swa_debug_prefill_mask: mask uint8 [L][L] device (out).  mask[t][i] counts how often the
  * prefill kernel that swa_prefill launches for (L, Hq, Hkv, d, w, s, conv) attends to the key
  * held at position i for query t: the same form and q-tile geometry (swa_prefill_describe), the
- * same tile or chunk walk, mask-free classification and element predicate, and (resident forms)
- * the key each LDS chunk slot actually holds, through the wide form's per-half slot map.  A
+ * same tile or chunk walk, mask-free classification and element predicate, and (resident form)
+ * the key each LDS chunk slot actually holds.  A
  * correct kernel gives 1 on A(t) and 0 elsewhere.  Requires L <= 8192.
  *
  * swa_debug_decode_slots: slot_pos int64 [B][s + w_loc] device (out).  For every split segment

@@ -155,24 +155,6 @@ SWA_HD TileInfo tile_info(int tile, int tile_n, int t0, int t1, int w_loc, int s
 // resident_slot_key0(cw, k) + r, r < kChunkN (rows past the sequence hold its last key).
 SWA_HD int resident_slot_key0(const ChunkWalk &cw, int k) { return cw.chunk(k) * kChunkN; }
 
-// The wide resident form takes its q-tile as 32-token halves [h0, h1], each over its own four-chunk
-// walk hw; slot[k] is the workgroup slot holding chunk hw.chunk(k).  A chunk the half needs is one
-// the workgroup needs, so it has a slot: below cw.n_sink the sink slots, else the window slot
-// counted from cw.win_lo.  A chunk past the half's needs may have none (its keys are after the
-// half's last token, so the element mask removes them whatever the slot holds): it takes the last
-// slot.
-SWA_HD void resident_half_slots(const ChunkWalk &cw, int h0, int h1, int w_loc, int s, int n_slots,
-                               ChunkWalk &hw, int (&slot)[4])
-{
-    hw = plan_chunks(h0, h1, w_loc, s, kChunkN);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int ch = hw.chunk(k);
-        const int sl = ch < cw.n_sink ? ch : cw.n_sink + (ch - cw.win_lo);
-        slot[k] = sl < 0 ? 0 : (sl > n_slots - 1 ? n_slots - 1 : sl);
-    }
-}
-
 // ------------------------------------------------------------------------------ decode
 //
 // Cache of s pinned sink slots followed by a ring of w_loc slots.  Position p lives in

@@ -24,7 +24,7 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv);
 bool prefill_resident(int Tm, int q_lo, int w_loc, int s);
 
 // What launch_prefill launches for a whole-sequence prefill: the kernel form (0 tile walk,
-// 1 resident, 2 wide resident), the geometry as launched (Tm doubled in the wide form), the grid,
+// 1 resident), the geometry as launched, the grid,
 // and the (query row, key) pairs whose scores and value products the matrix cores compute (rows of
 // a workgroup times the keys of the tiles or chunks it visits, padding rows included).
 struct PrefillPlan {

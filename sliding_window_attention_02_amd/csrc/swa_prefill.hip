@@ -33,16 +33,13 @@
 // re-read the same K/V tiles.  The fp32 output goes out in whole 128-byte lines with
 // non-temporal stores (store_pair).
 //
-// Three forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
+// Two forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
 // then the middle tiles through a software pipeline.  The resident form, for windows whose
 // 32-token q-tiles need at most four 32-key chunks (SWA(64,4)), loads all of a q-tile's keys
 // into LDS at once, takes the exact maximum, and stores O block by block as it completes: no
 // load follows any store, so the output drains under the compute (the chip counts loads and
 // stores in one in-order counter, so in the main form the output of a round of workgroups is
-// written after its compute and overlaps nothing).  The wide resident form does the same for
-// 64-token q-tiles when four q-heads share a kv-head: five chunk slots (80 KiB, two
-// workgroups per CU) serve both 32-token halves, and each wave takes its head's two halves in
-// turn, so the keys shared by the halves are loaded once and half as many workgroups run.
+// written after its compute and overlaps nothing).
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -210,16 +207,14 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
     return c;
 }
 
-// FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots), 2 wide resident
-// (64-token q-tiles taken as two 32-token halves per wave, five chunk slots).  CACHED: the key
+// FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots).  CACHED: the key
 // sequence begins with a.n_cached keys held in the sink+ring cache (chunked prefill); the
 // whole-sequence instantiation has no cache code at all.
 template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     constexpr bool RES = FORM != 0;
-    constexpr bool WIDE = FORM == 2;
-    constexpr int NQB = WIDE ? 4 : 2;  // 16-column blocks per wave
+    constexpr int NQB = 2;  // 16-column blocks per wave
     constexpr int kPieces = Lds<D>::kPieces;
     constexpr int kKSteps = D / 32;    // MFMA k-steps for S
     constexpr int kDBlocks = D / 16;   // 16-row blocks of O^T
@@ -237,9 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     auto ldsbuf = [&](int buf) __attribute__((always_inline)) -> unsigned char(*)[kTileBytes] {
         return buf == 0 ? lds_b0 : lds_b1;  // (buf is a constant after inlining)
     };
-    // The wide form's fifth chunk slot (K, V); a token array in the other forms.
     constexpr int kChunkBytes = kChunkN * kRowBytes;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds5[2][WIDE ? kChunkBytes : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -316,9 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
         ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
     }
-    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf
-    // (buf 2: the wide form's fifth chunk slot, which holds tile rows 0 .. 31, so only waves 0
-    // and 1 load into it).
+    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf.
     // Buffer resources over this (b, kv-head)'s rows of k and v (fewer than 2^32 bytes: one
     // sequence of q holds fewer than 2^31 elements and Hkv <= Hq), for the loads of whole tiles:
     // the tile's byte offset is a scalar operand and each lane adds its 32-bit offset, so a load
@@ -349,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int j = wave_u * kLoadsPerWave + i;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs,
-                                                         SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]),
+                                                         SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]),
                                                          16, (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off, 0, 0);
             }
             return;
@@ -368,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     const uint32_t row = (uint32_t)(kRowsPerLoad * j + lane / kPieces);
                     const uint32_t off = (kv ? ld_voff[i] : ld_koff[i]) - row * (uint32_t)((kv_row - D) * 2);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]),
+                        kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]),
                         16, (int)off, slot_off, 0, 0);
                 }
                 return;
@@ -385,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
             const int key = min(j0 + row, last);
             // (made opaque outside the per-lane branch, where it is still a scalar)
-            auto *const dst = SWA_LDS_DMA_DST(buf == 2 ? &lds5[kv][1024 * j] : &ldsbuf(buf)[kv][1024 * j]);
+            auto *const dst = SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]);
             if (!CACHED || key >= n_cached) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs, dst, 16,
                                                          (int)((uint32_t)((key - n_cached) * kv_row + piece * 8) * 2u),
@@ -439,15 +430,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     float lsum[2] = {0.f, 0.f};
 
     if constexpr (RES) {
-        // Resident forms (windows whose 32-token q-tile needs at most four 32-key chunks): every
+        // Resident form (windows whose 32-token q-tile needs at most four 32-key chunks): every
         // chunk of the workgroup is loaded at once, slot k into rows 32 (k & 1) .. of buffer
-        // k >> 1 (waves 2 (k & 1) and 2 (k & 1) + 1 load it; buffer 2 is the wide form's fifth
-        // slot), then one barrier, after which the workgroup issues no more loads (the queries of
-        // both halves in the wide form were loaded before it).  Each 16-column block is then done
-        // over all of its chunks and stored at once: the stores of one block drain while the next
-        // computes (a later wait for a load would also wait for those stores, since loads and
-        // stores share one in-order counter).
-        constexpr int kSlots = WIDE ? 5 : 4;
+        // k >> 1 (waves 2 (k & 1) and 2 (k & 1) + 1 load it), then one barrier, after which the
+        // workgroup issues no more loads.  Each 16-column block is then done over all of its
+        // chunks and stored at once: the stores of one block drain while the next computes (a
+        // later wait for a load would also wait for those stores, since loads and stores share
+        // one in-order counter).
+        constexpr int kSlots = 4;
         const ChunkWalk cw = plan_chunks(t0, t1, a.w_loc, a.s, kChunkN);
         // Every slot is always loaded (a slot past the workgroup's chunks holds keys after t1, and
         // rows past the sequence read its last row), so any slot holds finite keys and values.
@@ -463,22 +453,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         __syncthreads();
         // LDS rows of chunk slot k (K or V).
         auto slot_rows = [&](int k, int kv) __attribute__((always_inline)) -> const unsigned char * {
-            if (WIDE && k == 4)
-                return &lds5[kv][0];
             return &ldsbuf(k >> 1)[kv][0] + (k & 1) * kChunkBytes;
         };
-        // With every key of a 32-token half at hand the softmax needs no running maximum: all
-        // scores, the exact column maximum, the probabilities, then O^T = V^T P^T.  hw is the half's
-        // own chunk walk (four chunks, straight-line code: a chunk past the half's last needed one
-        // holds keys after its last token, which the element mask removes by causality), and
-        // slot[k] the slot holding chunk hw.chunk(k).
-        auto pass = [&](auto qb_c, const ChunkWalk &hw, const int (&slot)[4]) __attribute__((always_inline)) {
+        // With every key of the q-tile at hand the softmax needs no running maximum: all scores,
+        // the exact column maximum, the probabilities, then O^T = V^T P^T.  Slot k holds chunk
+        // cw.chunk(k) (four chunks, straight-line code: a chunk past the q-tile's last needed one
+        // holds keys after its last token, which the element mask removes by causality).
+        auto pass = [&](auto qb_c) __attribute__((always_inline)) {
             constexpr int qb = decltype(qb_c)::value;
             const int t = tok[qb];
             f32x4 sr[4][2];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const unsigned char *kt = slot_rows(slot[k], 0);
+                const unsigned char *kt = slot_rows(k, 0);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     sr[k][h] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -488,14 +475,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         sr[k][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sr[k][h], 0, 0, 0);
                     }
                 }
-                if constexpr (WIDE)
-                    if (k & 1)
-                        __builtin_amdgcn_sched_barrier(0);
             }
             float mx = -INFINITY;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int key0 = hw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
+                const int key0 = cw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -535,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 f32x4 od = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const unsigned char *vt = slot_rows(slot[k], 1);
+                    const unsigned char *vt = slot_rows(k, 1);
                     bf16x8 af;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
@@ -556,26 +540,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     od_lo = od;
             }
         };
-        if constexpr (!WIDE) {
-            const int slot[4] = {0, 1, 2, 3};
-            pass(std::integral_constant<int, 0>(), cw, slot);
-            pass(std::integral_constant<int, 1>(), cw, slot);
-        } else {
-            // The two 32-token halves of the q-tile, each with its own chunk walk and slot map.
-            auto half = [&](int h0, ChunkWalk &hw, int(&slot)[4]) __attribute__((always_inline)) {
-                resident_half_slots(cw, h0, min(h0 + kChunkN - 1, t1), a.w_loc, a.s, kSlots, hw, slot);
-            };
-            ChunkWalk hw;
-            int slot[4];
-            half(t0, hw, slot);
-            pass(std::integral_constant<int, 0>(), hw, slot);
-            pass(std::integral_constant<int, 1>(), hw, slot);
-            if (t0 + kChunkN <= t1) {
-                half(t0 + kChunkN, hw, slot);
-                pass(std::integral_constant<int, 2>(), hw, slot);
-                pass(std::integral_constant<int, 3>(), hw, slot);
-            }
-        }
+        pass(std::integral_constant<int, 0>());
+        pass(std::integral_constant<int, 1>());
     } else {
         const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
         const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
@@ -849,9 +815,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 // mask admit the pair, recorded at the key the visited LDS row actually holds.  The walks are the
 // kernel's own device functions: for the main form the edge tiles (chunk selection, mask-free
 // classification, element predicate) and the middle tiles (whole, unmasked); for the resident
-// forms the chunk walk with its slot contents and, in the wide form, each 32-token half's walk
-// and slot map.  A correct kernel gives exactly 1 on A(t) and 0 elsewhere.  One workgroup per
-// q-tile, one thread per query (no two threads write one row).
+// form the chunk walk with the keys its slots hold.  A correct kernel gives exactly 1 on A(t) and
+// 0 elsewhere.  One workgroup per q-tile, one thread per query (no two threads write one row).
 __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int form, int w_loc, int s)
 {
     const int t0 = blockIdx.x * Tm;
@@ -866,18 +831,10 @@ __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int form
     };
     if (form != 0) {
         const ChunkWalk cw = plan_chunks(t0, t1, w_loc, s, kChunkN);
-        // The 32-token half holding t (the resident form's q-tile is a single half over the slots
-        // 0..3 in walk order).
-        ChunkWalk hw = cw;
-        int slot[4] = {0, 1, 2, 3};
-        if (form == 2) {
-            const int h0 = t0 + ((t - t0) / kChunkN) * kChunkN;
-            resident_half_slots(cw, h0, min(h0 + kChunkN - 1, t1), w_loc, s, 5, hw, slot);
-        }
         for (int k = 0; k < 4; ++k)
             for (int r = 0; r < kChunkN; ++r) {
-                const int key = hw.chunk(k) * kChunkN + r;  // the key the element mask tests
-                const int held = resident_slot_key0(cw, slot[k]) + r;  // the key slot[k] holds
+                const int key = cw.chunk(k) * kChunkN + r;        // the key the element mask tests
+                const int held = resident_slot_key0(cw, k) + r;  // the key slot k holds
                 if (key_allowed(t, key, w_loc, s))
                     ++row[min(held, L - 1)];
             }
@@ -918,13 +875,9 @@ bool prefill_resident(int Tm, int q_lo, int w_loc, int s)
 
 namespace {
 
-// Kernel form of a launch: the wide resident form where a wave's 64 rows are one head's 64
-// tokens (four q-heads per kv-head slice) and each 32-token half fits the resident bound (then
-// the 64-token q-tile needs at most five chunks); else the resident form; else the main form.
+// Kernel form of a launch: the resident form where its bound holds, else the main form.
 int prefill_form(const PrefillGeometry &g, int q_lo, int w_loc, int s)
 {
-    if (g.Gw == 4 && prefill_resident(g.Tm, q_lo, w_loc, s))
-        return 2;
     return prefill_resident(g.Tm, q_lo, w_loc, s) ? 1 : 0;
 }
 
@@ -951,10 +904,6 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
     PrefillPlan p;
     p.g = prefill_geometry(L, Hq, Hkv);
     p.form = prefill_form(p.g, 0, w_loc, s);
-    if (p.form == 2) {
-        p.g.Tm *= 2;
-        p.g.n_qtiles = (L + p.g.Tm - 1) / p.g.Tm;
-    }
     const long long per_tile_group = (long long)B * Hkv * p.g.n_hslices;  // workgroups per q-tile
     p.workgroups = per_tile_group * p.g.n_qtiles;
     long long keys = 0;  // summed over the q-tiles: keys whose products one row of the tile computes
@@ -962,8 +911,6 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
         const int t0 = qt * p.g.Tm, t1 = std::min(t0 + p.g.Tm - 1, L - 1);
         if (p.form == 1) {
             keys += 4 * kChunkN;  // four chunk slots per pass
-        } else if (p.form == 2) {
-            keys += (t0 + kChunkN <= t1 ? 2 : 1) * 4 * kChunkN;  // each 32-token half: four chunks
         } else {
             const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
             const WalkSplit sp = split_walk(tw, t0, t1, w_loc, kTileN);
@@ -974,7 +921,6 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
             keys += (long long)sp.n_mid() * kTileN;
         }
     }
-    // Rows per pass: 128 (the wide form's halves are passes of 128 rows each).
     p.executed_pairs = per_tile_group * keys * kRowsPerBlock;
     return p;
 }
@@ -990,10 +936,6 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     }
     PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
     const int form = prefill_form(g, q_lo, w_loc, s);
-    if (form == 2) {  // 64-token q-tiles: twice the rows per workgroup
-        g.Tm *= 2;
-        g.n_qtiles = (Lq + g.Tm - 1) / g.Tm;
-    }
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -1022,11 +964,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    void (*const kernels[2][2][3])(PrefillArgs) = {
-        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>, prefill_kernel<64, 2, false>},
-         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>, prefill_kernel<128, 2, false>}},
-        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>, prefill_kernel<64, 2, true>},
-         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>, prefill_kernel<128, 2, true>}}};
+    void (*const kernels[2][2][2])(PrefillArgs) = {
+        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>},
+         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>}},
+        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>},
+         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>}}};
     void (*kern)(PrefillArgs) = kernels[a.n_cached > 0 ? 1 : 0][d == 128 ? 1 : 0][form];
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);

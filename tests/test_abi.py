@@ -140,7 +140,7 @@ def allowed_pairs(L, w_loc, s):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,w,s,form,tm", [
-    (1, 32, 8, 4096, 64, 4, 2, 64),      # Llama SWA(64,4): wide resident, 64-token q-tiles
+    (1, 32, 8, 4096, 64, 4, 1, 32),      # Llama SWA(64,4): resident, 32-token q-tiles
     (4, 32, 8, 4096, 512, 4, 0, 32),     # sweep w=512: tile walk
     (1, 32, 8, 16384, 4096, 4, 0, 32),   # Mistral w=4096: tile walk
     (1, 8, 4, 500, 30, 2, 1, 64),        # two q-heads per kv-head, small window: resident
@@ -152,8 +152,8 @@ def test_prefill_describe_reports_the_launched_form(lib, B, Hq, Hkv, L, w, s, fo
     assert info["workgroups"] == B * Hkv * (Hq // Hkv // info["heads_per_tile"]) * -(-L // tm)
     # every allowed (query, key) pair of every head is computed at least once
     assert info["executed_pairs"] >= B * Hq * allowed_pairs(L, w, s)
-    if form == 2:  # two halves of 128 rows x four 32-key chunks per workgroup (the last tile: one half)
-        assert info["executed_pairs"] == info["workgroups"] * 2 * 128 * 128
+    if form == 1:  # 128 rows x four 32-key chunks per workgroup
+        assert info["executed_pairs"] == info["workgroups"] * 128 * 128
 
 
 def test_prefill_describe_rejects_on_host(lib):

@@ -35,14 +35,14 @@ MASK_CASES = [
     (300, 32, 8, 64, 4, 0), (300, 12, 4, 33, 70, 0), (333, 6, 1, 100, 63, 0), (500, 16, 2, 200, 65, 0),
     (1000, 4, 4, 5000, 0, 0), (1000, 32, 8, 128, 4, 1), (1025, 4, 1, 256, 200, 1), (777, 5, 1, 96, 1, 0),
     (4096, 32, 8, 64, 4, 0), (2048, 32, 8, 512, 4, 0),
-    # the wide resident form (four q-heads per kv-head) over many 64-token q-tiles, ragged tails,
+    # the resident form (four q-heads per kv-head) over many 32-token q-tiles, ragged tails,
     # windows and sinks at its limits (three window chunks, or sinks spanning a chunk)
     (1000, 32, 8, 33, 0, 0), (777, 8, 2, 20, 30, 0), (257, 4, 1, 64, 32, 0), (555, 16, 4, 1, 64, 0),
     (2000, 4, 1, 68, 4, 1), (161, 8, 2, 64, 4, 0),
     # the resident form (two q-heads per kv-head, 64-token q-tiles as one pass)
     (700, 8, 4, 30, 2, 0), (333, 2, 1, 1, 32, 0), (1025, 6, 3, 33, 0, 0),
-    # the wide resident form over 2,000+ tokens and 8-16 kv-heads (three window chunks and no
-    # sinks, the total-window convention, sinks in a chunk of their own)
+    # the resident form over 2,000+ tokens and 8-16 kv-heads (three window chunks and no sinks,
+    # the total-window convention, sinks in a chunk of their own)
     (2085, 32, 8, 96, 0, 0), (2048, 32, 8, 68, 4, 1), (2100, 64, 16, 33, 30, 0),
 ]
 
@@ -53,9 +53,9 @@ def launched_form(L, Hq, Hkv, w, s, conv, d=128):
 
 def test_index_set_cases_cover_every_kernel_form():
     forms = {launched_form(L, Hq, Hkv, w, s, conv) for L, Hq, Hkv, w, s, conv in MASK_CASES}
-    assert forms == {0, 1, 2}
-    wide = [c for c in MASK_CASES if launched_form(*c) == 2 and c[0] > 640]
-    assert len(wide) >= 3  # more than ten 64-token q-tiles each
+    assert forms == {0, 1}
+    resident = [c for c in MASK_CASES if launched_form(*c) == 1 and c[0] > 640]
+    assert len(resident) >= 3  # more than twenty 32-token q-tiles each
 
 
 @pytest.mark.parametrize("L,Hq,Hkv,w,s,conv", MASK_CASES)
@@ -72,7 +72,7 @@ def test_prefill_index_set_white_box(L, Hq, Hkv, w, s, conv):
 @pytest.mark.parametrize("d,L,Hq,Hkv,w,s,conv", [
     (128, 128, 4, 2, 5, 3, 0), (128, 100, 8, 2, 64, 4, 0), (64, 64, 4, 4, 7, 0, 0), (128, 128, 3, 1, 1, 0, 0),
     (128, 128, 4, 4, 128, 0, 0), (64, 64, 2, 1, 10, 70, 0), (128, 97, 32, 8, 20, 4, 1), (64, 61, 16, 2, 3, 2, 0),
-    # the wide resident form over several q-tiles (L up to the one-hot width d)
+    # the resident form over several q-tiles (L up to the one-hot width d)
     (128, 128, 8, 2, 33, 4, 0), (128, 121, 4, 1, 10, 32, 0), (64, 64, 16, 4, 17, 9, 1),
 ])
 def test_prefill_index_set_black_box(d, L, Hq, Hkv, w, s, conv):
@@ -121,11 +121,11 @@ PARITY = [
     (1, 64, 4, 1, 128, 1000, 0, 0, 1.0, 0),
     (3, 190, 6, 3, 64, 17, 2, 0, 2.0, 4),
     (1, 513, 5, 1, 128, 100, 1, 0, 1.0, 4),
-    # the wide resident form (G = 4) at d = 64: a last q-tile whose second half is one token
+    # the resident form (G = 4) at d = 64: a last q-tile of one token
     (3, 161, 8, 2, 64, 64, 4, 0, 1.0, 4),
 ]
 
-# Many 32- and 64-token q-tiles per kv-head in the resident forms: ragged last q-tiles, both head
+# Many 32-token q-tiles per kv-head in the resident form: ragged last q-tiles, both head
 # sizes, both window conventions, sinks in a chunk of their own, batches.
 RESIDENT_LARGE = [
     # B, L, Hq, Hkv, d, w, s, conv, std, boost_n
@@ -157,15 +157,15 @@ def test_prefill_matches_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost, parity
 
 
 @pytest.mark.parametrize("B,L,Hq,Hkv,d,w,s,conv,std,boost", RESIDENT_LARGE)
-def test_resident_forms_large_match_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost, parity):
+def test_resident_form_large_matches_oracle(B, L, Hq, Hkv, d, w, s, conv, std, boost, parity):
     info = swa.prefill_describe(B, Hq, Hkv, L, d, w, s, conv)
     say("resident large", B, L, Hq, Hkv, d, w, s, conv, info)
-    assert info["form"] == 2
+    assert info["form"] == 1
     q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=L + 31 * w + s, std=std, sink_boost_n=boost, sink_boost=4.0)
     scale = 1.0 / np.sqrt(d)
     out = swa.prefill(q.cuda(), k.cuda(), v.cuda(), w, s, scale, conv).cpu().numpy()
     ref = orc.prefill(f64(q), f64(k), f64(v), w, s, scale, conv)
-    check_close(out, ref, "prefill resident forms, large (all elements)", parity)
+    check_close(out, ref, "prefill resident form, large (all elements)", parity)
 
 
 def test_tiny_workload_full_parity(parity):
