@@ -72,11 +72,12 @@ struct PrefillArgs {
     int L, Hq, Hkv, G, Gw, Tm, n_qtiles, n_hslices;
     int Lq, q_lo;  // queries are key positions q_lo .. q_lo + Lq - 1 (rows 0 .. Lq-1 of q, out)
     // Keys 0 .. n_cached-1 come from a sink+ring cache [B][Hkv][s + w_loc][d] instead of k, v
-    // (chunked prefill): key j < ns is sink slot j; key j >= ns is ring slot
-    // s + (ring0 + j - ns) mod w_loc, with ring0 < w_loc and j - ns < w_loc.  k and v then hold
-    // keys n_cached .. L-1.  n_cached = 0 for a whole-sequence prefill.
+    // (chunked prefill): key j < ns is sink slot j; keys ns .. w0-1 are padding that no query
+    // admits (read from slot 0); key j >= w0 is ring slot s + (ring0 + j - w0) mod w_loc, with
+    // ring0 < w_loc and j - w0 < w_loc.  k and v then hold keys n_cached .. L-1.  n_cached = 0
+    // for a whole-sequence prefill.
     const uint16_t *kc, *vc;
-    int n_cached, ns, ring0;
+    int n_cached, ns, w0, ring0;
     int w_loc, s;
     float scale_log2;
     int nblocks;
@@ -345,11 +346,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             }
             return;
         }
-        if (CACHED && j0 >= a.ns && j0 + kTileN - 1 < n_cached) {
+        if (CACHED && j0 >= a.w0 && j0 + kTileN - 1 < n_cached) {
             // Every row of the tile is a cached window key.  When their ring slots run on without
             // wrapping, the tile is consecutive cache rows: the same lane offsets with the cache's
             // row stride (d elements instead of Hkv d), the first slot as the scalar offset.
-            int r0 = a.ring0 + (j0 - a.ns);
+            int r0 = a.ring0 + (j0 - a.w0);
             r0 = r0 >= a.w_loc ? r0 - a.w_loc : r0;
             if (r0 + kTileN <= a.w_loc) {
                 const int slot_off = __builtin_amdgcn_readfirstlane((a.s + r0) * D * 2);
@@ -383,9 +384,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                                                          0, 0, 0);
             } else {
                 int slot = key;
-                if (key >= a.ns) {
-                    const int r = a.ring0 + key - a.ns;
+                if (key >= a.w0) {
+                    const int r = a.ring0 + key - a.w0;
                     slot = a.s + (r >= a.w_loc ? r - a.w_loc : r);
+                } else if (key >= a.ns) {
+                    slot = 0;  // padding between the sinks and the window: never admitted
                 }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? vc_rs : kc_rs, dst, 16,
                                                          (int)((uint32_t)(slot * D + piece * 8) * 2u), 0, 0, 0);
@@ -929,12 +932,22 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
                           int Hkv, int L, int d, int w_loc, int s, float scale, hipStream_t stream,
                           hipEvent_t start, hipEvent_t stop, const PrefillKeySource *cached, float *lse)
 {
-    int Lq = L, q_lo = 0;
+    int Lq = L, q_lo = 0, gap = 0;
     if (cached != nullptr) {
         Lq = L - cached->n_cached;
         q_lo = cached->n_cached;
     }
-    PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
+    const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
+    // A chunk after the cache has filled (all s sinks and w_loc - 1 window keys cached) whose
+    // queries start off a 32-key boundary: padding rows between the sinks and the window move
+    // them onto one, so the resident form can take the chunk (all of a q-tile's keys in one
+    // load instead of a chain of dependent tile steps).  No query admits a padding row: the
+    // first query's window starts right after the padding, and the padding lies past the sinks.
+    if (cached != nullptr && cached->ns == s && cached->n_cached - cached->ns == w_loc - 1 &&
+        q_lo % kChunkN != 0 && prefill_resident(g.Tm, 0, w_loc, s))
+        gap = kChunkN - q_lo % kChunkN;
+    L += gap;
+    q_lo += gap;
     const int form = prefill_form(g, q_lo, w_loc, s);
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -947,8 +960,9 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     a.q_lo = q_lo;
     a.kc = cached ? static_cast<const uint16_t *>(cached->k_cache) : nullptr;
     a.vc = cached ? static_cast<const uint16_t *>(cached->v_cache) : nullptr;
-    a.n_cached = cached ? cached->n_cached : 0;
+    a.n_cached = cached ? cached->n_cached + gap : 0;
     a.ns = cached ? cached->ns : 0;
+    a.w0 = cached ? cached->ns + gap : 0;
     a.ring0 = cached ? cached->ring0 : 0;
     a.Hq = Hq;
     a.Hkv = Hkv;
