@@ -263,7 +263,8 @@ int swa_append_decode_step_timed(const void *q, void *k_cache, void *v_cache, co
  * workspace, no synchronisation.
  * Errors: as swa_prefill, plus SWA_EINVAL for C < 1, pos0 < 0 or a non-16-byte-aligned lse;
  * SWA_EUNSUPPORTED when
- * s + w_loc - 1 + C keys, or the C query rows, of one sequence exceed 2^31-1 elements.
+ * s + w_loc + 30 + C key rows (the cached and the chunk's keys, plus up to 31 padding rows), or the
+ * C query rows, of one sequence exceed 2^31-1 elements.
  */
 int swa_prefill_chunk(const void *q, const void *k, const void *v, void *k_cache, void *v_cache,
                       float *out, float *lse, int64_t pos0, int B, int Hq, int Hkv, int C, int d, int w,

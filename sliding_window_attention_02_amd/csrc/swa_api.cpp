@@ -182,7 +182,8 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
         return rc;
     if ((rc = check_scale(fn, scale)))
         return rc;
-    if ((long long)s + w_loc - 1 + C > 0x7fffffffLL || (long long)C * Hq * d > 0x7fffffffLL)
+    // (the key rows may grow by up to 31 padding rows between the sinks and the window)
+    if ((long long)s + w_loc - 1 + C + 31 > 0x7fffffffLL || (long long)C * Hq * d > 0x7fffffffLL)
         return fail(SWA_EUNSUPPORTED, "%s: one sequence's keys or queries exceed 2^31-1 elements", fn);
     if ((long long)Hq * d >= (1LL << 22))  // a q-tile's output rows must span less than 2 GiB
         return fail(SWA_EUNSUPPORTED, "%s: Hq * d = %lld reaches 2^22", fn, (long long)Hq * d);
