@@ -40,10 +40,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// LDS pointer in the local address space for the direct global -> LDS load (written inline:
-// a helper or an implicit conversion there makes the host pass drop the launch stub).
-#define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
-
 // V rows in LDS: 16-byte pieces XOR-swizzled so the transposed 8-byte reads of rows
 // r..r+3 (r = 0 mod 4) at pieces P, P+1 hit 8 distinct pieces.
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
@@ -171,18 +167,25 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         for (int kk = 0; kk < kKSteps; ++kk)
             knf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(knew + kk * 32 + g16 * 8));
     }
+    // V by buffer loads (a flat-encoded global load may, as far as the compiler knows, also
+    // touch LDS, after which it would wait for every outstanding load, V included, before the
+    // first score) into opaque LDS destinations (this wave reads only its own rows, after the
+    // explicit wait below), so the scores and the softmax run while V lands.  Every chunk slot
+    // is loaded (one past the segment repeats its last chunk and is never read): the same number
+    // of loads on every path keeps the compiler's count of outstanding loads exact, so its waits
+    // for Q and K do not also wait for V.
+    const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(vcache), 0, a.n_slots * kRowBytes, 0x00020000);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        if (ch < nch) {
-            const int c0 = seg_lo + ch * kChunk;
+        const int c0 = seg_lo + min(ch, nch - 1) * kChunk;
 #pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                const int r = kRowsPerLoad * i + lane / kPieces;
-                const int slot = min(c0 + r, last);
-                const int piece = (lane % kPieces) ^ swz_v(r);
-                __builtin_amdgcn_global_load_lds(const_cast<uint16_t *>(vcache + (size_t)slot * D + piece * 8),
-                                                 SWA_LDS_PTR(&vlds[ch][1024 * i]), 16, 0, 0);
-            }
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = kRowsPerLoad * i + lane / kPieces;
+            const int slot = min(c0 + r, last);
+            const int piece = (lane % kPieces) ^ swz_v(r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, SWA_LDS_DMA_DST(&vlds[ch][1024 * i]), 16,
+                                                     (slot * D + piece * 8) * 2, 0, 0, 0);
         }
     }
 

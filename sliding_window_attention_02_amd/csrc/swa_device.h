@@ -12,6 +12,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// LDS pointer in the local address space, as the direct global -> LDS load takes it.  The
+// cast is written inline: an implicit conversion (or a helper function) there makes the host
+// pass drop the kernel's launch stub.
+#define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+// The same pointer, opaque to the compiler: a direct load given it carries no alias information
+// about its LDS destination, so the compiler does not order later LDS reads after it.  Without
+// this, a read from one stage of a double buffer while loads into the other stage are in flight
+// (or any such read at a loop head) gets a wait for every outstanding vector-memory operation.
+// Every kernel here orders its loads and reads itself: counted waits on this wave's loads, then
+// a barrier for the other waves' loads.
+#define SWA_LDS_DMA_DST(p)                                                                        \
+    ({                                                                                           \
+        __attribute__((address_space(3))) void *lds_dma_dst_ = SWA_LDS_PTR(p);                   \
+        asm volatile("" : "+s"(lds_dma_dst_));                                                   \
+        lds_dma_dst_;                                                                            \
+    })
+
 namespace swa {
 
 // The walk and index functions below run in the kernels and on the host (work accounting).

@@ -136,22 +136,6 @@ __device__ __forceinline__ float sum8(const bf16x8 &p, float acc)
 // nothing else (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
-// LDS pointer in the local address space, as the direct global -> LDS load takes it.  The
-// cast is written inline: an implicit conversion (or a helper function) there makes the host
-// pass drop the kernel's launch stub.
-#define SWA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
-// The same pointer, opaque to the compiler: a direct load given it carries no alias information
-// about its LDS destination, so the compiler does not order later LDS reads after it.  Without
-// this, a read from one stage of a double buffer while loads into the other stage are in flight
-// (or any such read at a loop head) gets a wait for every outstanding vector-memory operation.
-// Every kernel here orders its loads and reads itself: counted waits on this wave's loads, then
-// a barrier for the other waves' loads.
-#define SWA_LDS_DMA_DST(p)                                                                        \
-    ({                                                                                           \
-        __attribute__((address_space(3))) void *lds_dma_dst_ = SWA_LDS_PTR(p);                   \
-        asm volatile("" : "+s"(lds_dma_dst_));                                                   \
-        lds_dma_dst_;                                                                            \
-    })
 
 // Output stores in whole 128-byte lines.  Lane (g, c) holds column c of a 16-column block of
 // O^T at d = 16 db + 4 g .. +3, so one plain store would write 64 bytes of each of 16 rows.  For
