@@ -61,7 +61,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = 64;     // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kRowsPerBlock = 128;
+// 16-column MFMA blocks per wave: a workgroup holds 64 NQB query rows.
+constexpr int kMainNQB = 2;  // tile walk: 128 rows
+constexpr int kResNQB = 2;   // resident form: 128 rows
+constexpr int rows_per_block(int form) { return 64 * (form != 0 ? kResNQB : kMainNQB); }
 
 struct PrefillArgs {
     const uint16_t *q;
@@ -102,6 +105,15 @@ __device__ __forceinline__ float max_over_groups(float x)
     x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
     const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Sum over the same four lane groups, as (x_l + x_l^16) + (x_l^32 + x_l^48), with the same swaps.
+__device__ __forceinline__ float sum_over_groups(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -199,15 +211,15 @@ template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     constexpr bool RES = FORM != 0;
-    constexpr int NQB = 2;  // 16-column blocks per wave
+    constexpr int NQB = RES ? kResNQB : kMainNQB;  // 16-column blocks per wave
     constexpr int kPieces = Lds<D>::kPieces;
     constexpr int kKSteps = D / 32;    // MFMA k-steps for S
     constexpr int kDBlocks = D / 16;   // 16-row blocks of O^T
     constexpr int kRowBytes = Lds<D>::kRowBytes;
     constexpr int kTileBytes = Lds<D>::kTileBytes;
     constexpr int kRowsPerLoad = Lds<D>::kRowsPerLoad;
-    constexpr int kLoadsPerWave = Lds<D>::kLoadsPerTile / (kThreads / 64);
-    static_assert(kLoadsPerWave >= 1, "tile load split");
+    constexpr int kHalfLoads = Lds<D>::kLoadsPerTile / 2 / (kThreads / 64);  // per wave and 32-row half
+    static_assert(kHalfLoads >= 1, "tile load split");
 
     // Two buffers of (K tile, V tile), both row-major with swizzled 16-byte pieces, one variable
     // each: the reads then carry alias information that tells the compiler they do not depend on
@@ -279,26 +291,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const uint16_t *vbase = a.v + ((size_t)bc.b * L_in * a.Hkv + bc.hkv) * D;
     const size_t cache_base = ((size_t)bc.b * a.Hkv + bc.hkv) * ((size_t)a.s + a.w_loc) * D;
 
-    // Direct global -> LDS loads: load j of a tile fills LDS bytes [1024 j, 1024 j + 1024),
-    // lane l the 16 bytes at 16 l: row kRowsPerLoad*j + l / kPieces, physical piece
-    // l % kPieces, which holds logical piece (physical ^ swizzle).  This wave issues loads
-    // j = wave*kLoadsPerWave .. +kLoadsPerWave-1.  Rows past the end of the sequence read the
-    // last row (finite values; such keys are always masked).
+    // Direct global -> LDS loads of 32-row halves of a tile: load j of a half fills its LDS bytes
+    // [1024 j, 1024 j + 1024), lane l the 16 bytes at 16 l: row kRowsPerLoad*j + l / kPieces of
+    // the half, physical piece l % kPieces, which holds logical piece (physical ^ swizzle).  A
+    // row's swizzle depends on its index mod 32 only, so both halves take the same offsets.  This
+    // wave issues loads j = wave*kHalfLoads .. +kHalfLoads-1 of each half.  Rows past the end of
+    // the sequence read the last row (finite values; such keys are always masked).
     // The wave index as a uniform (scalar) value: the LDS destinations (M0) are then scalar.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t ld_koff[kLoadsPerWave], ld_voff[kLoadsPerWave];  // byte offsets from the tile's first row
+    uint32_t ld_koff[kHalfLoads], ld_voff[kHalfLoads];  // byte offsets from the half's first row
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int row = kRowsPerLoad * (wave * kLoadsPerWave + i) + lane / kPieces;
+    for (int i = 0; i < kHalfLoads; ++i) {
+        const int row = kRowsPerLoad * (wave * kHalfLoads + i) + lane / kPieces;
         const int phys = lane % kPieces;
         ld_koff[i] = (uint32_t)(row * kv_row + (phys ^ swz_k<D>(row)) * 8) * 2u;
         ld_voff[i] = (uint32_t)(row * kv_row + (phys ^ swz_v(row)) * 8) * 2u;
     }
-    // Loads the K rows (kv = 0) or the V rows (kv = 1) of the tile at key j0 into LDS buffer buf.
     // Buffer resources over this (b, kv-head)'s rows of k and v (fewer than 2^32 bytes: one
-    // sequence of q holds fewer than 2^31 elements and Hkv <= Hq), for the loads of whole tiles:
-    // the tile's byte offset is a scalar operand and each lane adds its 32-bit offset, so a load
-    // costs no vector address arithmetic.
+    // sequence of q holds fewer than 2^31 elements and Hkv <= Hq): a half's byte offset is a
+    // scalar operand and each lane adds its 32-bit offset, so a load costs no vector address
+    // arithmetic.
     const uint32_t kv_bytes = (uint32_t)(((size_t)L_in * a.Hkv - bc.hkv) * D * 2);
     const __amdgpu_buffer_rsrc_t k_rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kbase), 0, (int)kv_bytes, 0x00020000);
@@ -310,58 +322,59 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         const_cast<uint16_t *>(CACHED ? a.kc + cache_base : a.k), 0, (int)cache_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vc_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(CACHED ? a.vc + cache_base : a.v), 0, (int)cache_bytes, 0x00020000);
-    // Every load is a buffer load (a flat-encoded global load may, as far as the compiler knows,
-    // also touch LDS, after which it waits for all outstanding memory operations wherever it
-    // cannot prove otherwise) into an opaque LDS destination (SWA_LDS_DMA_DST): the kernel orders
-    // loads and LDS reads itself, with counted waits and barriers.
-    auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
+    // Loads the K rows (kv = 0) or the V rows (kv = 1) of keys j0 .. j0+31 into half `half` of LDS
+    // buffer buf.  Every load is a buffer load (a flat-encoded global load may, as far as the
+    // compiler knows, also touch LDS, after which it waits for all outstanding memory operations
+    // wherever it cannot prove otherwise) into an opaque LDS destination (SWA_LDS_DMA_DST): the
+    // kernel orders loads and LDS reads itself, with counted waits and barriers.
+    auto issue_half = [&](int j0, int buf, int half, auto kv_c) __attribute__((always_inline)) {
         constexpr int kv = decltype(kv_c)::value;
         const int last = a.L - 1;
         const int n_cached = CACHED ? a.n_cached : 0;
-        if (j0 >= n_cached && j0 + kTileN - 1 <= last) {
-            // Every row of the tile is a key of k/v inside the sequence.
-            const int tile_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - n_cached) * (uint32_t)kv_row * 2u));
+        if (j0 >= n_cached && j0 + kChunkN - 1 <= last) {
+            // Every row is a key of k/v inside the sequence.
+            const int half_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - n_cached) * (uint32_t)kv_row * 2u));
 #pragma unroll
-            for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int j = wave_u * kLoadsPerWave + i;
+            for (int i = 0; i < kHalfLoads; ++i) {
+                const int j = wave_u * kHalfLoads + i;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs,
-                                                         SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]),
-                                                         16, (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off, 0, 0);
+                                                         SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][half * kChunkBytes + 1024 * j]),
+                                                         16, (int)(kv ? ld_voff[i] : ld_koff[i]), half_off, 0, 0);
             }
             return;
         }
-        if (CACHED && j0 >= a.w0 && j0 + kTileN - 1 < n_cached) {
-            // Every row of the tile is a cached window key.  When their ring slots run on without
-            // wrapping, the tile is consecutive cache rows: the same lane offsets with the cache's
-            // row stride (d elements instead of Hkv d), the first slot as the scalar offset.
+        if (CACHED && j0 >= a.w0 && j0 + kChunkN - 1 < n_cached) {
+            // Every row is a cached window key.  When their ring slots run on without wrapping,
+            // the rows are consecutive cache rows: the same lane offsets with the cache's row
+            // stride (d elements instead of Hkv d), the first slot as the scalar offset.
             int r0 = a.ring0 + (j0 - a.w0);
             r0 = r0 >= a.w_loc ? r0 - a.w_loc : r0;
-            if (r0 + kTileN <= a.w_loc) {
+            if (r0 + kChunkN <= a.w_loc) {
                 const int slot_off = __builtin_amdgcn_readfirstlane((a.s + r0) * D * 2);
 #pragma unroll
-                for (int i = 0; i < kLoadsPerWave; ++i) {
-                    const int j = wave_u * kLoadsPerWave + i;
+                for (int i = 0; i < kHalfLoads; ++i) {
+                    const int j = wave_u * kHalfLoads + i;
                     const uint32_t row = (uint32_t)(kRowsPerLoad * j + lane / kPieces);
                     const uint32_t off = (kv ? ld_voff[i] : ld_koff[i]) - row * (uint32_t)((kv_row - D) * 2);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]),
+                        kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][half * kChunkBytes + 1024 * j]),
                         16, (int)off, slot_off, 0, 0);
                 }
                 return;
             }
         }
-        // A tile past the sequence's end (rows past it read its last row: finite values, and such
-        // keys are always masked) or holding cached keys (their sink or ring slots): per-lane
-        // offsets, a cached key's lanes through the cache's resource (one more load instruction
-        // when the tile mixes the two, which only makes the counted waits stricter).
+        // Rows past the sequence's end (they read its last row: finite values, and such keys are
+        // always masked) or holding cached keys (their sink or ring slots): per-lane offsets, a
+        // cached key's lanes through the cache's resource (one more load instruction when the
+        // half mixes the two, which only makes the counted waits stricter).
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int j = wave_u * kLoadsPerWave + i;
+        for (int i = 0; i < kHalfLoads; ++i) {
+            const int j = wave_u * kHalfLoads + i;
             const int row = kRowsPerLoad * j + lane / kPieces;
             const int piece = (lane % kPieces) ^ (kv ? swz_v(row) : swz_k<D>(row));
             const int key = min(j0 + row, last);
             // (made opaque outside the per-lane branch, where it is still a scalar)
-            auto *const dst = SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][1024 * j]);
+            auto *const dst = SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][half * kChunkBytes + 1024 * j]);
             if (!CACHED || key >= n_cached) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? v_rs : k_rs, dst, 16,
                                                          (int)((uint32_t)((key - n_cached) * kv_row + piece * 8) * 2u),
@@ -378,6 +391,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                                                          (int)((uint32_t)(slot * D + piece * 8) * 2u), 0, 0, 0);
             }
         }
+    };
+    // A whole 64-key tile: both halves, with one test for each common case (a tile of k/v rows
+    // inside the sequence, a tile of cached window keys in consecutive ring slots), so the middle
+    // tiles' path takes one branch per tile.
+    auto issue = [&](int j0, int buf, auto kv_c) __attribute__((always_inline)) {
+        constexpr int kv = decltype(kv_c)::value;
+        const int n_cached = CACHED ? a.n_cached : 0;
+        if (j0 >= n_cached && j0 + kTileN - 1 <= a.L - 1) {
+            const int tile_off = __builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 - n_cached) * (uint32_t)kv_row * 2u));
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int i = 0; i < kHalfLoads; ++i) {
+                    const int j = wave_u * kHalfLoads + i;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        kv ? v_rs : k_rs, SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][half * kChunkBytes + 1024 * j]), 16,
+                        (int)(kv ? ld_voff[i] : ld_koff[i]), tile_off + half * kChunkN * kv_row * 2, 0, 0);
+                }
+            return;
+        }
+        if (CACHED && j0 >= a.w0 && j0 + kTileN - 1 < n_cached) {
+            int r0 = a.ring0 + (j0 - a.w0);
+            r0 = r0 >= a.w_loc ? r0 - a.w_loc : r0;
+            if (r0 + kTileN <= a.w_loc) {
+                const int slot_off = __builtin_amdgcn_readfirstlane((a.s + r0) * D * 2);
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < kHalfLoads; ++i) {
+                        const int j = wave_u * kHalfLoads + i;
+                        const uint32_t row = (uint32_t)(kRowsPerLoad * j + lane / kPieces);
+                        const uint32_t off = (kv ? ld_voff[i] : ld_koff[i]) - row * (uint32_t)((kv_row - D) * 2);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            kv ? vc_rs : kc_rs, SWA_LDS_DMA_DST(&ldsbuf(buf)[kv][half * kChunkBytes + 1024 * j]),
+                            16, (int)off, slot_off + half * kChunkN * D * 2, 0, 0);
+                    }
+                return;
+            }
+        }
+        issue_half(j0, buf, 0, kv_c);
+        issue_half(j0 + kChunkN, buf, 1, kv_c);
     };
     // (tags as types, passed as temporaries: named tag objects captured by the lambdas below
     // end up in private memory)
@@ -404,23 +458,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     for (int m = 0; m < 4; ++m)
         v_lane[m] = (8 * g16 + (c16 >> 2)) * kRowBytes + 32 * (m ^ (c16 >> 2)) + 16 * ((c16 >> 1) & 1) + 8 * (c16 & 1);
 
-    f32x4 o[kDBlocks][2];
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Softmax state per query column, in log2 units: the reference maximum m_ref the
-    // probabilities are taken against.  The running sum of the probabilities adds the same
-    // bf16-rounded values that weight V (v_dot2 with a pair of ones, fp32 accumulation): each
-    // lane sums the keys it holds and the four lane groups of a column are added at the end, so
-    // the dominant weight's rounding cancels between numerator and denominator.
-    float m_ref[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};
-
     if constexpr (RES) {
         // Resident form (windows whose 32-token q-tile needs at most four 32-key chunks): every
-        // chunk of the workgroup is loaded at once, slot k into rows 32 (k & 1) .. of buffer
-        // k >> 1 (waves 2 (k & 1) and 2 (k & 1) + 1 load it), then one barrier, after which the
-        // workgroup issues no more loads.  Each 16-column block is then done over all of its
+        // chunk of the workgroup is loaded at once, slot k into half k & 1 of buffer k >> 1, then
+        // one barrier, after which the workgroup issues no more loads.  Each 16-column block is then done over all of its
         // chunks and stored at once: the stores of one block drain while the next computes (a
         // later wait for a load would also wait for those stores, since loads and stores share
         // one in-order counter).
@@ -430,11 +471,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // rows past the sequence read its last row), so any slot holds finite keys and values.
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
-            if ((wave_u >> 1) == (k & 1)) {
-                const int j0 = resident_slot_key0(cw, k) - (k & 1) * kChunkN;  // tile row 0 holds key j0
-                issue(j0, k >> 1, KRows());
-                issue(j0, k >> 1, VRows());
-            }
+            issue_half(resident_slot_key0(cw, k), k >> 1, k & 1, KRows());
+            issue_half(resident_slot_key0(cw, k), k >> 1, k & 1, VRows());
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
@@ -494,8 +532,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         pf[k][4 * h + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sr[k][h][j], c, -m_use)));
                 l = sum8(pf[k], l);
             }
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+            l = sum_over_groups(l);
             const float inv = 1.f / l;
             if (a.lse != nullptr && g16 == 0 && valid[qb])
                 store_lse(a, bc.b, tok[qb], head[qb], m_use, l);
@@ -536,160 +573,141 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             return swa::tile_info(tile, kTileN, t0, t1, a.w_loc, a.s);
         };
 
-        // The steps below take `fast` as a compile-time flag: a fast tile has both chunks needed and
-        // no element mask, so its code is straight-line; otherwise chunks outside [c_lo, c_hi] are
-        // skipped (loads aside: a tile is always loaded whole) and the mask is applied.
+        f32x4 o[kDBlocks][NQB];
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+                o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Softmax state per query column, in log2 units: the reference maximum m_ref the
+        // probabilities are taken against.  The running sum of the probabilities adds the same
+        // bf16-rounded values that weight V (v_dot2 with a pair of ones, fp32 accumulation): each
+        // lane sums the keys it holds and the four lane groups of a column are added at the end,
+        // so the dominant weight's rounding cancels between numerator and denominator.
+        float m_ref[NQB], lsum[NQB], alpha[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            m_ref[qb] = -INFINITY;
+            lsum[qb] = 0.f;
+        }
 
-        // S^T = K Q^T of one tile, K from LDS.  Row m of 16-key block (kc, h) holds key
-        // 32*kc + 8*(m/4) + 4*h + m%4, so lane group g later owns keys 32*kc + 8g .. +7.
-        // (Skipped chunks are set to zero all the same: every element of sacc is then written by
-        // each call, so the compiler does not keep the previous tile's scores alive.)
-        auto scores = [&](f32x4(&sacc)[2][2][2], const unsigned char *kt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
-            constexpr bool fast = decltype(fast_c)::value;
-    #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-    #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    sacc[kc][h][0] = sacc[kc][h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                    continue;
-    #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-    #pragma unroll
-                    for (int kk = 0; kk < kKSteps; ++kk) {
-                        const bf16x8 af =
-                            *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + (kc * kChunkN + 4 * h) * kRowBytes);
-    #pragma unroll
-                        for (int qb = 0; qb < 2; ++qb)
-                            sacc[kc][h][qb] =
-                                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sacc[kc][h][qb], 0, 0, 0);
-                    }
+        // S^T = K Q^T of one chunk, K rows from LDS at kt.  Row m of 16-key block h holds key
+        // 8*(m/4) + 4*h + m%4 of the chunk, so lane group g later owns keys 8g .. 8g+7.
+        auto scores = [&](f32x4(&sc)[2][NQB], const unsigned char *kt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    sc[h][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < kKSteps; ++kk) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + 4 * h * kRowBytes);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+                        sc[h][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][kk], sc[h][qb], 0, 0, 0);
                 }
             }
         };
 
-        // Element mask of one tile (when some visited pair is outside A(t)), its column maxima, and
-        // the lazy move of the reference maximum: m_ref only moves (and O and the sums are rescaled
-        // by alpha) when the column maximum exceeds it by more than 8 in log2 units, so the
-        // probabilities stay below 256 and most tiles need no rescale.  Returns whether any column
-        // of this lane moved.
-        auto tile_max = [&](f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, float(&alpha)[2]) __attribute__((always_inline)) {
-            constexpr bool fast = decltype(fast_c)::value;
-            if (!fast && !ti.mask_free) {
-    #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    if (kc < ti.c_lo || kc > ti.c_hi)
-                        continue;
-    #pragma unroll
-                    for (int h = 0; h < 2; ++h)
-    #pragma unroll
-                        for (int qb = 0; qb < 2; ++qb)
-    #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int key = ti.j0 + kc * kChunkN + 8 * g16 + 4 * h + j;
-                                const int t = tok[qb];
-                                const bool ok = key_allowed(t, key, a.w_loc, a.s);
-                                sacc[kc][h][qb][j] = ok ? sacc[kc][h][qb][j] : -INFINITY;
-                            }
-                }
-            }
+        // Element mask of one chunk whose first key is key0 (when some pair in it is outside A(t)).
+        auto mask_chunk = [&](f32x4(&sc)[2][NQB], int key0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool ok = key_allowed(tok[qb], key0 + 8 * g16 + 4 * h + j, a.w_loc, a.s);
+                        sc[h][qb][j] = ok ? sc[h][qb][j] : -INFINITY;
+                    }
+        };
+        // Column maxima of NC chunks and the lazy move of the reference maximum: m_ref only moves
+        // (and O and the sums are rescaled by alpha) when the column maximum exceeds it by more
+        // than 8 in log2 units, so the probabilities stay below 256 and most steps need no
+        // rescale.  Returns whether any column of this lane moved.
+        auto col_max = [&](const f32x4(*sc)[2][NQB], auto nc_c) __attribute__((always_inline)) {
+            constexpr int NC = decltype(nc_c)::value;
             bool grow_any = false;
-    #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
                 // (pairs folded into the running maximum: three-input maxima)
                 float mx = -INFINITY;
-    #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                        continue;
-    #pragma unroll
+#pragma unroll
+                for (int kc = 0; kc < NC; ++kc)
+#pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][0]), sacc[kc][h][qb][1]);
-                        mx = fmaxf(fmaxf(mx, sacc[kc][h][qb][2]), sacc[kc][h][qb][3]);
+                        mx = fmaxf(fmaxf(mx, sc[kc][h][qb][0]), sc[kc][h][qb][1]);
+                        mx = fmaxf(fmaxf(mx, sc[kc][h][qb][2]), sc[kc][h][qb][3]);
                     }
-                }
-                mx = max_over_groups(mx);
-                const float m_tile = mx * c;
-                const bool grow = m_tile > m_ref[qb] + 8.f;
+                const float m_new = max_over_groups(mx) * c;
+                const bool grow = m_new > m_ref[qb] + 8.f;
                 // (a column with no allowed key so far keeps m_ref = -inf and alpha = 1)
-                alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile) : 1.f;
-                m_ref[qb] = grow ? m_tile : m_ref[qb];
+                alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new) : 1.f;
+                m_ref[qb] = grow ? m_new : m_ref[qb];
                 grow_any |= grow;
             }
             return grow_any;
         };
 
-        // Probabilities of one tile against the reference maximum, as P^T B-operand fragments.
-        auto probs = [&](const f32x4(&sacc)[2][2][2], const TileInfo &ti, auto fast_c, bf16x8(&pf)[2][2]) __attribute__((always_inline)) {
-            constexpr bool fast = decltype(fast_c)::value;
-    #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+        auto rescale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+                for (int db = 0; db < kDBlocks; ++db)
+                    o[db][qb] *= alpha[qb];
+                lsum[qb] *= alpha[qb];
+            }
+        };
+
+        // Probabilities of one chunk against the reference maximum, as P^T B-operand fragments.
+        auto probs = [&](const f32x4(&sc)[2][NQB], bf16x8(&pf)[NQB]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
                 const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
-    #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                        continue;
-    #pragma unroll
-                    for (int h = 0; h < 2; ++h)
-    #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            pf[kc][qb][4 * h + j] =
-                                static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc][h][qb][j], c, -m_use)));
-                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pf[qb][4 * h + j] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[h][qb][j], c, -m_use)));
             }
         };
 
-        // O^T += V^T P^T over the tile's needed chunks, V from LDS, and the probability sums.
-        auto accumulate = [&](const bf16x8(&pf)[2][2], const unsigned char *vt, const TileInfo &ti, auto fast_c) __attribute__((always_inline)) {
-            constexpr bool fast = decltype(fast_c)::value;
-    #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                if (!fast && (kc < ti.c_lo || kc > ti.c_hi))
-                    continue;
-    #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    lsum[qb] = sum8(pf[kc][qb], lsum[qb]);
-    #pragma unroll
-                for (int db = 0; db < kDBlocks; ++db) {
-                    bf16x8 af;
-    #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int off = v_lane[db & 3] + (kc * kChunkN + 4 * h) * kRowBytes + 32 * (db & ~3);
-                        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)(vt + off));
-                        const bf16x4 y = __builtin_bit_cast(bf16x4, x);
-                        af[4 * h + 0] = y[0];
-                        af[4 * h + 1] = y[1];
-                        af[4 * h + 2] = y[2];
-                        af[4 * h + 3] = y[3];
-                    }
-    #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[kc][qb], o[db][qb], 0, 0, 0);
-                }
-            }
-        };
-
-        auto rescale = [&](const float(&alpha)[2]) __attribute__((always_inline)) {
-    #pragma unroll
+        // O^T += V^T P^T of one chunk, V rows from LDS at vt, and the probability sums.
+        auto accumulate = [&](const bf16x8(&pf)[NQB], const unsigned char *vt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+                lsum[qb] = sum8(pf[qb], lsum[qb]);
+#pragma unroll
             for (int db = 0; db < kDBlocks; ++db) {
-                o[db][0] *= alpha[0];
-                o[db][1] *= alpha[1];
+                bf16x8 af;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int off = v_lane[db & 3] + 4 * h * kRowBytes + 32 * (db & ~3);
+                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vt + off));
+                    const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+                    af[4 * h + 0] = y[0];
+                    af[4 * h + 1] = y[1];
+                    af[4 * h + 2] = y[2];
+                    af[4 * h + 3] = y[3];
+                }
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[qb], o[db][qb], 0, 0, 0);
             }
-            lsum[0] *= alpha[0];
-            lsum[1] *= alpha[1];
         };
 
-        // The online softmax takes the tiles in any order: the edge tiles first, one per step,
+        // The online softmax takes the chunks in any order: the edge tiles first, one per step,
         // then the middle tiles through a software pipeline.
-        f32x4 sacc[2][2][2][2];  // [tile parity][kc][h][qb]
-        float alpha[2];
-        using Generic = std::integral_constant<bool, false>;
-        using Fast = std::integral_constant<bool, true>;
+        f32x4 sc[2][2][2][NQB];  // scores of two tiles: [parity][chunk][h][qb]
         using Even = std::integral_constant<int, 0>;
         using Odd = std::integral_constant<int, 1>;
+        using One = std::integral_constant<int, 1>;
+        using Two = std::integral_constant<int, 2>;
 
-        // Edge tiles: step i computes tile i while K and V of tile i+1 load into the other buffer.
+        // Edge tiles: step i computes tile i's needed chunks while K and V of tile i+1 load into
+        // the other buffer.  The scores of both chunks come first, so the second chunk's matrix
+        // work runs beside the first chunk's softmax.
         if (sp.n_edge > 0) {
             TileInfo cur = tile_info(sp.edge_tile(tw, 0));
             issue(cur.j0, 0, KRows());
@@ -704,12 +722,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     issue(nxt.j0, buf ^ 1, KRows());
                     issue(nxt.j0, buf ^ 1, VRows());
                 }
-                scores(sacc[0], ldsbuf(buf)[0], cur, Generic());
-                if (__any(tile_max(sacc[0], cur, Generic(), alpha)))
-                    rescale(alpha);
-                bf16x8 pf[2][2];
-                probs(sacc[0], cur, Generic(), pf);
-                accumulate(pf, ldsbuf(buf)[1], cur, Generic());
+                // Each needed chunk takes its own maximum, so the first chunk's products with V
+                // run beside the second chunk's softmax.
+                f32x4(&es)[2][2][NQB] = sc[0];
+                const bool need0 = cur.c_lo == 0, need1 = cur.c_hi == 1;
+                if (need0)
+                    scores(es[0], ldsbuf(buf)[0]);
+                if (need1)
+                    scores(es[1], ldsbuf(buf)[0] + kChunkBytes);
+                bf16x8 pf[NQB];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    if (!(kc == 0 ? need0 : need1))
+                        continue;
+                    if (!cur.mask_free)
+                        mask_chunk(es[kc], cur.j0 + kc * kChunkN);
+                    if (__any(col_max(&es[kc], One())))
+                        rescale();
+                    probs(es[kc], pf);
+                    accumulate(pf, ldsbuf(buf)[1] + kc * kChunkBytes);
+                }
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
                 __syncthreads();
                 cur = nxt;
@@ -728,20 +760,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // so the exponentials of one tile run while the matrix cores work on the next.  K runs one
         // tile ahead of V: step m reads K of tile m+1 and V of tile m (LDS buffers (m+1)&1 and m&1)
         // while K of tile m+2 and V of tile m+1 load into the other two; one barrier per step.  The
-        // rescale for tile m+1 (rare) closes step m, after O has taken tile m.
+        // rescale for tile m+1 (rare) closes step m, after O has taken tile m.  (A pipeline over
+        // 32-key chunks, one barrier per tile, measured 6% slower at w = 4096.)
         const int nm = sp.n_mid();
         if (nm > 0) {
             const int jm = sp.mid_lo * kTileN;
-            const TileInfo full = {0, 0, 1, 1};  // (the fast steps read none of it)
+            auto tile_scores = [&](f32x4(&st)[2][2][NQB], const unsigned char *kt) __attribute__((always_inline)) {
+                scores(st[0], kt);
+                scores(st[1], kt + kChunkBytes);
+            };
+            auto tile_pv = [&](const f32x4(&st)[2][2][NQB], const unsigned char *vt) __attribute__((always_inline)) {
+                bf16x8 pf[2][NQB];
+                probs(st[0], pf[0]);
+                probs(st[1], pf[1]);
+                accumulate(pf[0], vt);
+                accumulate(pf[1], vt + kChunkBytes);
+            };
             issue(jm, 0, KRows());
             issue(jm, 0, VRows());
             if (nm > 1)
                 issue(jm + kTileN, 1, KRows());
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();
-            scores(sacc[0], ldsbuf(0)[0], full, Fast());
-            if (__any(tile_max(sacc[0], full, Fast(), alpha)))
-                rescale(alpha);
+            tile_scores(sc[0], ldsbuf(0)[0]);
+            if (__any(col_max(sc[0], Two())))
+                rescale();
 
             auto mid_step = [&](const int m, auto buf_c) __attribute__((always_inline)) {  // m + 1 < nm
                 constexpr int buf = decltype(buf_c)::value;  // m & 1
@@ -750,22 +793,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 if (m + 2 < nm)
                     issue(jm + (m + 2) * kTileN, buf, KRows());
                 issue(jm + (m + 1) * kTileN, buf ^ 1, VRows());
-                scores(sacc[buf ^ 1], ldsbuf(buf ^ 1)[0], full, Fast());
-                bf16x8 pf[2][2];
-                probs(sacc[buf], full, Fast(), pf);
-                accumulate(pf, ldsbuf(buf)[1], full, Fast());
-                const bool grow = tile_max(sacc[buf ^ 1], full, Fast(), alpha);
-                if (__any(grow))
-                    rescale(alpha);
+                tile_scores(sc[buf ^ 1], ldsbuf(buf ^ 1)[0]);
+                tile_pv(sc[buf], ldsbuf(buf)[1]);
+                if (__any(col_max(sc[buf ^ 1], Two())))
+                    rescale();
             };
             // The last middle tile: its probabilities and O += V^T P^T.
             auto mid_last = [&](auto buf_c) __attribute__((always_inline)) {
                 constexpr int buf = decltype(buf_c)::value;
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 __syncthreads();
-                bf16x8 pf[2][2];
-                probs(sacc[buf], full, Fast(), pf);
-                accumulate(pf, ldsbuf(buf)[1], full, Fast());
+                tile_pv(sc[buf], ldsbuf(buf)[1]);
             };
             int m = 0;
             for (; m + 2 < nm; m += 2) {
@@ -781,16 +819,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         }
 
         // Epilogue: finish the row sums across the four lane groups, normalise, store fp32.
-    #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float l = lsum[qb];  // this lane's keys; add the four lane groups of the column
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const float l = sum_over_groups(lsum[qb]);  // this lane's keys, then the column's
             const float inv = 1.f / l;
             if (a.lse != nullptr && g16 == 0 && valid[qb])
                 store_lse(a, bc.b, tok[qb], head[qb], m_ref[qb] == -INFINITY ? 0.f : m_ref[qb], l);
             const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
-    #pragma unroll
+#pragma unroll
             for (int m = 0; m < kDBlocks / 2; ++m)
                 store_pair(out_rs, oa + 128 * m, ob + 128 * m, o[2 * m][qb] * inv, o[2 * m + 1][qb] * inv);
         }
@@ -860,17 +896,7 @@ bool prefill_resident(int Tm, int q_lo, int w_loc, int s)
     return n <= 4;
 }
 
-namespace {
-
-// Kernel form of a launch: the resident form where its bound holds, else the main form.
-int prefill_form(const PrefillGeometry &g, int q_lo, int w_loc, int s)
-{
-    return prefill_resident(g.Tm, q_lo, w_loc, s) ? 1 : 0;
-}
-
-}  // namespace
-
-PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
+PrefillGeometry prefill_geometry(int L, int Hq, int Hkv, int form)
 {
     PrefillGeometry g;
     g.G = Hq / Hkv;
@@ -880,17 +906,23 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv)
             g.Gw = c;
             break;
         }
-    g.Tm = kRowsPerBlock / g.Gw;
+    g.rows = rows_per_block(form);
+    g.Tm = g.rows / g.Gw;
     g.n_hslices = g.G / g.Gw;
     g.n_qtiles = (L + g.Tm - 1) / g.Tm;
     return g;
 }
 
+int prefill_form(int Hq, int Hkv, int q_lo, int w_loc, int s)
+{
+    return prefill_resident(prefill_geometry(1, Hq, Hkv, 1).Tm, q_lo, w_loc, s) ? 1 : 0;
+}
+
 PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
 {
     PrefillPlan p;
-    p.g = prefill_geometry(L, Hq, Hkv);
-    p.form = prefill_form(p.g, 0, w_loc, s);
+    p.form = prefill_form(Hq, Hkv, 0, w_loc, s);
+    p.g = prefill_geometry(L, Hq, Hkv, p.form);
     const long long per_tile_group = (long long)B * Hkv * p.g.n_hslices;  // workgroups per q-tile
     p.workgroups = per_tile_group * p.g.n_qtiles;
     long long keys = 0;  // summed over the q-tiles: keys whose products one row of the tile computes
@@ -908,7 +940,7 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
             keys += (long long)sp.n_mid() * kTileN;
         }
     }
-    p.executed_pairs = per_tile_group * keys * kRowsPerBlock;
+    p.executed_pairs = per_tile_group * keys * p.g.rows;
     return p;
 }
 
@@ -921,18 +953,18 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
         Lq = L - cached->n_cached;
         q_lo = cached->n_cached;
     }
-    const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv);
     // A chunk after the cache has filled (all s sinks and w_loc - 1 window keys cached) whose
     // queries start off a 32-key boundary: padding rows between the sinks and the window move
     // them onto one, so the resident form can take the chunk (all of a q-tile's keys in one
     // load instead of a chain of dependent tile steps).  No query admits a padding row: the
     // first query's window starts right after the padding, and the padding lies past the sinks.
     if (cached != nullptr && cached->ns == s && cached->n_cached - cached->ns == w_loc - 1 &&
-        q_lo % kChunkN != 0 && prefill_resident(g.Tm, 0, w_loc, s))
+        q_lo % kChunkN != 0 && prefill_form(Hq, Hkv, 0, w_loc, s) == 1)
         gap = kChunkN - q_lo % kChunkN;
     L += gap;
     q_lo += gap;
-    const int form = prefill_form(g, q_lo, w_loc, s);
+    const int form = prefill_form(Hq, Hkv, q_lo, w_loc, s);
+    const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv, form);
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -988,7 +1020,7 @@ hipError_t launch_debug_prefill_mask(uint8_t *mask, int L, int Hq, int Hkv, int 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(kRowsPerBlock), 0, stream, mask, L, g.Tm,
+    hipLaunchKernelGGL(debug_prefill_mask_kernel, dim3(g.n_qtiles), dim3(g.Tm), 0, stream, mask, L, g.Tm,
                        form, w_loc, s);
     return hipGetLastError();
 }
