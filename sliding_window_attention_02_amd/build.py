@@ -21,8 +21,11 @@ SOURCES = ["swa_api.cpp", "swa_prefill.hip", "swa_decode.hip", "swa_model.hip"]
 # it AGPRs; keeping MFMA results in arch VGPRs spares the AGPR -> VGPR copies before the
 # softmax reads the scores.  Its latency-bound step also gains ~1% at batch 1, 64 and 1024
 # from the scheduler's max-ilp strategy (the default, max-occupancy, targets waves it never
-# has); the prefill keeps the default, which was best there.
-EXTRA_FLAGS = {"swa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# has); the prefill keeps the default, which was best there.  The prefill is built assuming no
+# NaNs (its inputs are finite and it makes none; masked scores are -inf): the maxima of values
+# exchanged between lanes then need no quieting of signalling NaNs first.
+EXTRA_FLAGS = {"swa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+               "swa_prefill.hip": ["-fno-honor-nans"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

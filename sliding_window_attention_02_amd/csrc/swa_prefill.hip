@@ -98,7 +98,9 @@ struct Lds {
 // Maximum over the four lane groups (lanes l, l^16, l^32, l^48) that hold one query column,
 // with the gfx950 cross-row swaps (VALU only, no LDS round trip).  permlane32_swap on (x, x)
 // hands each lane the value of lane l^32 in one of its two results and its own in the other;
-// permlane16_swap does the same for lane l^16.
+// permlane16_swap does the same for lane l^16.  (This file is built assuming no NaNs: fmaxf on
+// the swapped bits would otherwise first quiet them as possible signalling NaNs, one more
+// instruction per operand.)
 __device__ __forceinline__ float max_over_groups(float x)
 {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -584,12 +586,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // bf16-rounded values that weight V (v_dot2 with a pair of ones, fp32 accumulation): each
         // lane sums the keys it holds and the four lane groups of a column are added at the end,
         // so the dominant weight's rounding cancels between numerator and denominator.
-        float m_ref[NQB], lsum[NQB], alpha[NQB];
+        // thr is m_ref + 8 in score units: a column maximum above it moves m_ref (below).
+        float m_ref[NQB], thr[NQB], lsum[NQB], cmx[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             m_ref[qb] = -INFINITY;
+            thr[qb] = -INFINITY;
             lsum[qb] = 0.f;
         }
+        const float inv_c = 1.f / c;
 
         // S^T = K Q^T of one chunk, K rows from LDS at kt.  Row m of 16-key block h holds key
         // 8*(m/4) + 4*h + m%4 of the chunk, so lane group g later owns keys 8g .. 8g+7.
@@ -621,10 +626,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         sc[h][qb][j] = ok ? sc[h][qb][j] : -INFINITY;
                     }
         };
-        // Column maxima of NC chunks and the lazy move of the reference maximum: m_ref only moves
-        // (and O and the sums are rescaled by alpha) when the column maximum exceeds it by more
-        // than 8 in log2 units, so the probabilities stay below 256 and most steps need no
-        // rescale.  Returns whether any column of this lane moved.
+        // Column maxima of NC chunks (into cmx) and whether any column of this lane passed its
+        // threshold: the reference maximum only moves (move_ref, O and the sums rescaled) when the
+        // column maximum exceeds it by more than 8 in log2 units, so the probabilities stay below
+        // 256 and most steps take one compare per column.
         auto col_max = [&](const f32x4(*sc)[2][NQB], auto nc_c) __attribute__((always_inline)) {
             constexpr int NC = decltype(nc_c)::value;
             bool grow_any = false;
@@ -639,31 +644,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         mx = fmaxf(fmaxf(mx, sc[kc][h][qb][0]), sc[kc][h][qb][1]);
                         mx = fmaxf(fmaxf(mx, sc[kc][h][qb][2]), sc[kc][h][qb][3]);
                     }
-                const float m_new = max_over_groups(mx) * c;
-                const bool grow = m_new > m_ref[qb] + 8.f;
-                // (a column with no allowed key so far keeps m_ref = -inf and alpha = 1)
-                alpha[qb] = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new) : 1.f;
-                m_ref[qb] = grow ? m_new : m_ref[qb];
-                grow_any |= grow;
+                cmx[qb] = max_over_groups(mx);
+                grow_any |= cmx[qb] > thr[qb];
             }
             return grow_any;
         };
 
-        auto rescale = [&]() __attribute__((always_inline)) {
+        // The move: each column above its threshold takes its maximum as the new m_ref, and O and
+        // the sums are rescaled by alpha = 2^(old - new).  (A column with no allowed key so far
+        // keeps m_ref = -inf and alpha = 1.)
+        auto move_ref = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
+                const bool grow = cmx[qb] > thr[qb];
+                const float m_new = cmx[qb] * c;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new) : 1.f;
+                m_ref[qb] = grow ? m_new : m_ref[qb];
+                thr[qb] = grow ? (m_new + 8.f) * inv_c : thr[qb];
 #pragma unroll
                 for (int db = 0; db < kDBlocks; ++db)
-                    o[db][qb] *= alpha[qb];
-                lsum[qb] *= alpha[qb];
+                    o[db][qb] *= alpha;
+                lsum[qb] *= alpha;
             }
         };
 
         // Probabilities of one chunk against the reference maximum, as P^T B-operand fragments.
-        auto probs = [&](const f32x4(&sc)[2][NQB], bf16x8(&pf)[NQB]) __attribute__((always_inline)) {
+        // `finite`: every column already has a finite m_ref (the middle tiles, which follow a
+        // tile whose keys every query sees).
+        auto probs = [&](const f32x4(&sc)[2][NQB], bf16x8(&pf)[NQB], auto finite_c) __attribute__((always_inline)) {
+            constexpr bool finite = decltype(finite_c)::value;
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
-                const float m_use = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+                const float m_use = finite ? m_ref[qb] : (m_ref[qb] == -INFINITY ? 0.f : m_ref[qb]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -738,8 +750,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     if (!cur.mask_free)
                         mask_chunk(es[kc], cur.j0 + kc * kChunkN);
                     if (__any(col_max(&es[kc], One())))
-                        rescale();
-                    probs(es[kc], pf);
+                        move_ref();
+                    probs(es[kc], pf, std::false_type());
                     accumulate(pf, ldsbuf(buf)[1] + kc * kChunkBytes);
                 }
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile has landed
@@ -771,8 +783,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             };
             auto tile_pv = [&](const f32x4(&st)[2][2][NQB], const unsigned char *vt) __attribute__((always_inline)) {
                 bf16x8 pf[2][NQB];
-                probs(st[0], pf[0]);
-                probs(st[1], pf[1]);
+                probs(st[0], pf[0], std::true_type());
+                probs(st[1], pf[1], std::true_type());
                 accumulate(pf[0], vt);
                 accumulate(pf[1], vt + kChunkBytes);
             };
@@ -784,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             __syncthreads();
             tile_scores(sc[0], ldsbuf(0)[0]);
             if (__any(col_max(sc[0], Two())))
-                rescale();
+                move_ref();
 
             auto mid_step = [&](const int m, auto buf_c) __attribute__((always_inline)) {  // m + 1 < nm
                 constexpr int buf = decltype(buf_c)::value;  // m & 1
@@ -796,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 tile_scores(sc[buf ^ 1], ldsbuf(buf ^ 1)[0]);
                 tile_pv(sc[buf], ldsbuf(buf)[1]);
                 if (__any(col_max(sc[buf ^ 1], Two())))
-                    rescale();
+                    move_ref();
             };
             // The last middle tile: its probabilities and O += V^T P^T.
             auto mid_last = [&](auto buf_c) __attribute__((always_inline)) {
