@@ -109,6 +109,21 @@ __device__ __forceinline__ float max_over_groups(float x)
     return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// max_over_groups of two values at once, x0 and x1 (two 16-column blocks): one swap puts the
+// l / l^32 pairs of x0 in lanes 0-31 and those of x1 in lanes 32-63, so one maximum and one
+// 16-lane swap finish both, and a last swap hands every lane both results.  Three swaps and two
+// maxima instead of four and four.
+__device__ __forceinline__ void max_over_groups2(float &x0, float &x1)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+    float z = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+    z = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+    x0 = __uint_as_float(r[0]);
+    x1 = __uint_as_float(r[1]);
+}
+
 // Sum over the same four lane groups, as (x_l + x_l^16) + (x_l^32 + x_l^48), with the same swaps.
 __device__ __forceinline__ float sum_over_groups(float x)
 {
@@ -632,7 +647,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // 256 and most steps take one compare per column.
         auto col_max = [&](const f32x4(*sc)[2][NQB], auto nc_c) __attribute__((always_inline)) {
             constexpr int NC = decltype(nc_c)::value;
-            bool grow_any = false;
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
                 // (pairs folded into the running maximum: three-input maxima)
@@ -644,9 +658,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                         mx = fmaxf(fmaxf(mx, sc[kc][h][qb][0]), sc[kc][h][qb][1]);
                         mx = fmaxf(fmaxf(mx, sc[kc][h][qb][2]), sc[kc][h][qb][3]);
                     }
-                cmx[qb] = max_over_groups(mx);
-                grow_any |= cmx[qb] > thr[qb];
+                cmx[qb] = mx;
             }
+#pragma unroll
+            for (int qb = 0; qb + 1 < NQB; qb += 2)
+                max_over_groups2(cmx[qb], cmx[qb + 1]);
+            if (NQB % 2 != 0)
+                cmx[NQB - 1] = max_over_groups(cmx[NQB - 1]);
+            bool grow_any = false;
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+                grow_any |= cmx[qb] > thr[qb];
             return grow_any;
         };
 
