@@ -501,8 +501,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         // the exact column maximum, the probabilities, then O^T = V^T P^T.  Slot k holds chunk
         // cw.chunk(k) (four chunks, straight-line code: a chunk past the q-tile's last needed one
         // holds keys after its last token, which the element mask removes by causality).
-        auto pass = [&](auto qb_c) __attribute__((always_inline)) {
+        // The usual q-tile (all but the first few): slot 0 holds chunk 0, which lies below the
+        // window of every query of the q-tile, and the other slots hold chunks free of sinks.  Then
+        // slot 0's mask is key < s for both passes, applied through the initial value of its score
+        // accumulators (0 or -inf: K Q^T + (-inf) = -inf), and another slot's is the one unsigned
+        // compare t - key < w_loc (exact for keys >= s: causal and window bound at once), three
+        // vector instructions per score instead of five.  Other q-tiles test the whole predicate.
+        const bool usual = cw.n_sink == 1 && a.s <= kChunkN && t0 - a.w_loc + 1 >= kChunkN;
+        f32x4 sink_init[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sink_init[h][j] = 8 * g16 + 4 * h + j < a.s ? 0.f : -INFINITY;
+        auto pass = [&](auto qb_c, auto usual_c) __attribute__((always_inline)) {
             constexpr int qb = decltype(qb_c)::value;
+            constexpr bool USUAL = decltype(usual_c)::value;
             const int t = tok[qb];
             f32x4 sr[4][2];
 #pragma unroll
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 const unsigned char *kt = slot_rows(k, 0);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    sr[k][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sr[k][h] = USUAL && k == 0 ? sink_init[h] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < kKSteps; ++kk) {
                         const bf16x8 af = *reinterpret_cast<const bf16x8 *>(kt + k_lane[kk] + 4 * h * kRowBytes);
@@ -524,11 +538,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 const int key0 = cw.chunk(k) * kChunkN + 8 * g16;  // key of (h, j) = (0, 0)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
+                    if (!USUAL) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int key = key0 + 4 * h + j;
-                        const bool ok = key_allowed(t, key, a.w_loc, a.s);
-                        sr[k][h][j] = ok ? sr[k][h][j] : -INFINITY;
+                        for (int j = 0; j < 4; ++j) {
+                            const bool ok = key_allowed(t, key0 + 4 * h + j, a.w_loc, a.s);
+                            sr[k][h][j] = ok ? sr[k][h][j] : -INFINITY;
+                        }
+                    } else if (k > 0) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const bool ok = (uint32_t)(t - key0 - (4 * h + j)) < (uint32_t)a.w_loc;
+                            sr[k][h][j] = ok ? sr[k][h][j] : -INFINITY;
+                        }
                     }
                     mx = fmaxf(fmaxf(mx, sr[k][h][0]), sr[k][h][1]);
                     mx = fmaxf(fmaxf(mx, sr[k][h][2]), sr[k][h][3]);
@@ -536,8 +557,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
             }
             const float mm = max_over_groups(mx) * c;
             const float m_use = mm == -INFINITY ? 0.f : mm;
-            // Probabilities, their column sums (the ones-row MFMA), then O^T one 16-row block at a
-            // time, each stored as soon as it is complete, so the stores spread over the compute.
+            // Probabilities, their column sums, then O^T one 16-row block at a time, each stored as
+            // soon as it is complete, so the stores spread over the compute.
             bf16x8 pf[4];
             float l = 0.f;  // this lane's keys; the lane groups are added below
 #pragma unroll
@@ -550,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                 l = sum8(pf[k], l);
             }
             l = sum_over_groups(l);
-            const float inv = 1.f / l;
+            const float inv = __builtin_amdgcn_rcpf(l);  // (1 ulp; the exact quotient takes ten instructions)
             if (a.lse != nullptr && g16 == 0 && valid[qb])
                 store_lse(a, bc.b, tok[qb], head[qb], m_use, l);
             const uint32_t oa = row_off(qb, c16 & 7), ob = row_off(qb, (c16 & 7) + 8);
@@ -581,8 +602,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
                     od_lo = od;
             }
         };
-        pass(std::integral_constant<int, 0>());
-        pass(std::integral_constant<int, 1>());
+        if (usual) {
+            pass(std::integral_constant<int, 0>(), std::true_type());
+            pass(std::integral_constant<int, 1>(), std::true_type());
+        } else {
+            pass(std::integral_constant<int, 0>(), std::false_type());
+            pass(std::integral_constant<int, 1>(), std::false_type());
+        }
     } else {
         const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
         const WalkSplit sp = split_walk(tw, t0, t1, a.w_loc, kTileN);
