@@ -261,14 +261,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 
     // This lane's query column in each of its 16-column blocks (the wave owns rows
     // 16 NQB wave .. +16 NQB - 1).
+    // Row r of the workgroup is head slot r / Tm, token t0 + r % Tm.  Tm >= 32, so a 16-column
+    // block (first row `base`, uniform) crosses at most one head boundary: with base = gh0 Tm +
+    // rem (scalar arithmetic; gh0 <= 3), column col is head slot gh0 + (rem + col >= Tm).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int hbase = bc.hkv * a.G + bc.hs * a.Gw;  // first q-head of the workgroup
+    auto row_of = [&](int qb, int col, int &gh, int &tk) __attribute__((always_inline)) {
+        const int base = wave_s * 16 * NQB + qb * 16;
+        const int gh0 = (base >= a.Tm) + (base >= 2 * a.Tm) + (base >= 3 * a.Tm);
+        const int x = base - gh0 * a.Tm + col;
+        const bool next = x >= a.Tm;
+        gh = gh0 + (next ? 1 : 0);
+        tk = t0 + (next ? x - a.Tm : x);
+    };
     int tok[NQB], head[NQB];
     bool valid[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-        const int r = wave * 16 * NQB + qb * 16 + c16;
-        const int gh = r / a.Tm;
-        tok[qb] = t0 + r % a.Tm;
-        head[qb] = bc.hkv * a.G + bc.hs * a.Gw + gh;
+        int gh;
+        row_of(qb, c16, gh, tok[qb]);
+        head[qb] = hbase + gh;
         valid[qb] = gh < a.Gw && tok[qb] < a.L;
     }
 
@@ -295,11 +307,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.out + ((size_t)bc.b * a.Lq + (t0 - a.q_lo)) * a.Hq * D, 0, (t1 - t0 + 1) * a.Hq * D * 4, 0x00020000);
     auto row_off = [&](int qb, int col) __attribute__((always_inline)) {
-        const int r = wave * 16 * NQB + qb * 16 + col;
-        const int gh = r / a.Tm;
-        const int tk = t0 + r % a.Tm;
-        const int hd = bc.hkv * a.G + bc.hs * a.Gw + gh;
-        const uint32_t off = (uint32_t)(((tk - t0) * a.Hq + hd) * D + 16 * (c16 >> 3) + 4 * g16) * 4u;
+        int gh, tk;
+        row_of(qb, col, gh, tk);
+        // (24-bit products: tk - t0 < 2^8 and Hq < 2^16, and the offset is below 2^31)
+        const uint32_t off = ((uint32_t)__umul24(tk - t0, a.Hq) + hbase + gh) * (D * 4u) + (16 * (c16 >> 3) + 4 * g16) * 4u;
         return (gh < a.Gw && tk < a.L) ? off : kDropOffset;
     };
     const int kv_row = a.Hkv * D;  // elements between consecutive positions
