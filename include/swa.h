@@ -90,7 +90,10 @@ int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, i
  *
  *   form            0: the tile walk (64-key tiles; edge tiles masked, middle tiles unmasked);
  *                   1: resident (every 32-key chunk a q-tile needs held in LDS at once, at most
- *                      four: Tm/32 + ceil((w_loc-1)/32) + ceil(s/32) <= 4 for Tm-token q-tiles)
+ *                      four: Tm/32 + ceil((w_loc-1)/32) + ceil(s/32) <= 4 for Tm-token q-tiles);
+ *                   2: resident with 64-row workgroups (Tm/32 read as 1 for 16-token q-tiles),
+ *                      launched where form 1 does not apply or would start fewer than 512
+ *                      workgroups
  *   tokens_per_tile query tokens per workgroup; heads_per_tile q-heads per workgroup
  *   workgroups      grid size
  *   executed_pairs  (query row, key) pairs whose scores and value products the matrix cores

@@ -61,10 +61,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = 64;     // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves
-// 16-column MFMA blocks per wave: a workgroup holds 64 NQB query rows.
-constexpr int kMainNQB = 2;  // tile walk: 128 rows
-constexpr int kResNQB = 2;   // resident form: 128 rows
-constexpr int rows_per_block(int form) { return 64 * (form != 0 ? kResNQB : kMainNQB); }
+// 16-column MFMA blocks per wave: a workgroup holds 64 NQB query rows.  Forms: 0 the tile walk,
+// 1 resident with two blocks per wave (128 rows), 2 resident with one (64 rows: twice the
+// workgroups, each with half the serial work, for grids too small to fill the chip).
+constexpr int kMainNQB = 2;
+constexpr int nqb_of_form(int form) { return form == 0 ? kMainNQB : (form == 1 ? 2 : 1); }
+constexpr int rows_per_block(int form) { return 64 * nqb_of_form(form); }
+// Below this many 128-row resident workgroups (two per CU) the 64-row resident form is launched.
+constexpr long long kSmallGrid = 512;
 
 struct PrefillArgs {
     const uint16_t *q;
@@ -228,7 +232,7 @@ template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
     constexpr bool RES = FORM != 0;
-    constexpr int NQB = RES ? kResNQB : kMainNQB;  // 16-column blocks per wave
+    constexpr int NQB = nqb_of_form(FORM);  // 16-column blocks per wave
     constexpr int kPieces = Lds<D>::kPieces;
     constexpr int kKSteps = D / 32;    // MFMA k-steps for S
     constexpr int kDBlocks = D / 16;   // 16-row blocks of O^T
@@ -261,9 +265,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 
     // This lane's query column in each of its 16-column blocks (the wave owns rows
     // 16 NQB wave .. +16 NQB - 1).
-    // Row r of the workgroup is head slot r / Tm, token t0 + r % Tm.  Tm >= 32, so a 16-column
+    // Row r of the workgroup is head slot r / Tm, token t0 + r % Tm.  Tm >= 16, so a 16-column
     // block (first row `base`, uniform) crosses at most one head boundary: with base = gh0 Tm +
-    // rem (scalar arithmetic; gh0 <= 3), column col is head slot gh0 + (rem + col >= Tm).
+    // rem (scalar arithmetic; gh0 <= 3 as base < 4 Tm), column col is head slot
+    // gh0 + (rem + col >= Tm).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int hbase = bc.hkv * a.G + bc.hs * a.Gw;  // first q-head of the workgroup
     auto row_of = [&](int qb, int col, int &gh, int &tk) __attribute__((always_inline)) {
@@ -615,10 +620,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         };
         if (usual) {
             pass(std::integral_constant<int, 0>(), std::true_type());
-            pass(std::integral_constant<int, 1>(), std::true_type());
+            if constexpr (NQB > 1)
+                pass(std::integral_constant<int, NQB - 1>(), std::true_type());
         } else {
             pass(std::integral_constant<int, 0>(), std::false_type());
-            pass(std::integral_constant<int, 1>(), std::false_type());
+            if constexpr (NQB > 1)
+                pass(std::integral_constant<int, NQB - 1>(), std::false_type());
         }
     } else {
         const TileWalk tw = plan_tiles(t0, t1, a.w_loc, a.s, kTileN);
@@ -960,10 +967,16 @@ __global__ void fill_zero_kernel(uint8_t *p, size_t n)
 bool prefill_resident(int Tm, int q_lo, int w_loc, int s)
 {
     // With q-tiles starting on 32-key boundaries a q-tile needs at most Tm/32 + ceil((w_loc-1)/32)
-    // window chunks and ceil(s/32) sink chunks.
-    if (Tm % kChunkN != 0 || q_lo % kChunkN != 0)
+    // window chunks; 16-token q-tiles on 16-key boundaries at most 1 + ceil((w_loc-1)/32) (a tile
+    // starting mid-chunk reaches no further); and ceil(s/32) sink chunks.
+    long long win;
+    if (Tm % kChunkN == 0 && q_lo % kChunkN == 0)
+        win = Tm / kChunkN;
+    else if (Tm == kChunkN / 2 && q_lo % (kChunkN / 2) == 0)
+        win = 1;
+    else
         return false;
-    const long long n = Tm / kChunkN + ((long long)w_loc - 1 + kChunkN - 1) / kChunkN + ((long long)s + kChunkN - 1) / kChunkN;
+    const long long n = win + ((long long)w_loc - 1 + kChunkN - 1) / kChunkN + ((long long)s + kChunkN - 1) / kChunkN;
     return n <= 4;
 }
 
@@ -984,22 +997,28 @@ PrefillGeometry prefill_geometry(int L, int Hq, int Hkv, int form)
     return g;
 }
 
-int prefill_form(int Hq, int Hkv, int q_lo, int w_loc, int s)
+int prefill_form(int B, int Hq, int Hkv, int Lq, int q_lo, int w_loc, int s)
 {
-    return prefill_resident(prefill_geometry(1, Hq, Hkv, 1).Tm, q_lo, w_loc, s) ? 1 : 0;
+    const PrefillGeometry g1 = prefill_geometry(Lq, Hq, Hkv, 1), g2 = prefill_geometry(Lq, Hq, Hkv, 2);
+    const bool r1 = prefill_resident(g1.Tm, q_lo, w_loc, s), r2 = prefill_resident(g2.Tm, q_lo, w_loc, s);
+    // The 64-row form where the 128-row one would leave the chip short of workgroups.
+    const long long wg1 = (long long)B * Hkv * g1.n_hslices * g1.n_qtiles;
+    if (r2 && (!r1 || wg1 < kSmallGrid))
+        return 2;
+    return r1 ? 1 : 0;
 }
 
 PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
 {
     PrefillPlan p;
-    p.form = prefill_form(Hq, Hkv, 0, w_loc, s);
+    p.form = prefill_form(B, Hq, Hkv, L, 0, w_loc, s);
     p.g = prefill_geometry(L, Hq, Hkv, p.form);
     const long long per_tile_group = (long long)B * Hkv * p.g.n_hslices;  // workgroups per q-tile
     p.workgroups = per_tile_group * p.g.n_qtiles;
     long long keys = 0;  // summed over the q-tiles: keys whose products one row of the tile computes
     for (int qt = 0; qt < p.g.n_qtiles; ++qt) {
         const int t0 = qt * p.g.Tm, t1 = std::min(t0 + p.g.Tm - 1, L - 1);
-        if (p.form == 1) {
+        if (p.form != 0) {
             keys += 4 * kChunkN;  // four chunk slots per pass
         } else {
             const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
@@ -1030,11 +1049,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     // load instead of a chain of dependent tile steps).  No query admits a padding row: the
     // first query's window starts right after the padding, and the padding lies past the sinks.
     if (cached != nullptr && cached->ns == s && cached->n_cached - cached->ns == w_loc - 1 &&
-        q_lo % kChunkN != 0 && prefill_form(Hq, Hkv, 0, w_loc, s) == 1)
+        q_lo % kChunkN != 0 && prefill_form(B, Hq, Hkv, Lq, 0, w_loc, s) != 0)
         gap = kChunkN - q_lo % kChunkN;
     L += gap;
     q_lo += gap;
-    const int form = prefill_form(Hq, Hkv, q_lo, w_loc, s);
+    const int form = prefill_form(B, Hq, Hkv, Lq, q_lo, w_loc, s);
     const PrefillGeometry g = prefill_geometry(Lq, Hq, Hkv, form);
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
@@ -1065,11 +1084,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    void (*const kernels[2][2][2])(PrefillArgs) = {
-        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>},
-         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>}},
-        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>},
-         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>}}};
+    void (*const kernels[2][2][3])(PrefillArgs) = {
+        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>, prefill_kernel<64, 2, false>},
+         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>, prefill_kernel<128, 2, false>}},
+        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>, prefill_kernel<64, 2, true>},
+         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>, prefill_kernel<128, 2, true>}}};
     void (*kern)(PrefillArgs) = kernels[a.n_cached > 0 ? 1 : 0][d == 128 ? 1 : 0][form];
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);
