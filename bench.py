@@ -616,7 +616,8 @@ def decode_label(swa, dw, B: int) -> str:
 def describe(swa, wl):
     """The prefill kernel launched for workload wl (swa_prefill_describe) and its label."""
     info = swa.prefill_describe(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.s, wl.conv)
-    names = {0: "tile walk", 1: "resident form", 2: "resident form, 64-row workgroups"}
+    names = {0: "tile walk", 1: "resident form", 2: "resident form, 64-row workgroups",
+             3: "tile walk, 64-row workgroups"}
     info["kernel"] = f"prefill_kernel<{wl.d}, {info['form']}> ({names[info['form']]}, " \
                      f"{info['tokens_per_tile']}-token q-tiles x {info['heads_per_tile']} q-heads)"
     return info

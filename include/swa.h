@@ -93,7 +93,9 @@ int swa_prefill_timed(const void *q, const void *k, const void *v, float *out, i
  *                      four: Tm/32 + ceil((w_loc-1)/32) + ceil(s/32) <= 4 for Tm-token q-tiles);
  *                   2: resident with 64-row workgroups (Tm/32 read as 1 for 16-token q-tiles),
  *                      launched where form 1 does not apply or would start fewer than 512
- *                      workgroups
+ *                      workgroups;
+ *                   3: the tile walk with 64-row workgroups, launched instead of 0 where form 0
+ *                      would start at most 256 workgroups (one per CU)
  *   tokens_per_tile query tokens per workgroup; heads_per_tile q-heads per workgroup
  *   workgroups      grid size
  *   executed_pairs  (query row, key) pairs whose scores and value products the matrix cores

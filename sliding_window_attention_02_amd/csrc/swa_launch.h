@@ -9,7 +9,7 @@ namespace swa {
 
 // ----------------------------------------------------------------------------- prefill
 //
-// A workgroup computes `rows` query rows (128; 64 for the small-grid resident form): Tm
+// A workgroup computes `rows` query rows (128; 64 for the small-grid forms): Tm
 // consecutive tokens times Gw q-heads of one kv-head (GQA packing), so each K/V tile staged in
 // LDS serves Gw heads at once.
 struct PrefillGeometry {
@@ -20,15 +20,15 @@ struct PrefillGeometry {
     int n_hslices;  // G / Gw
     int n_qtiles;   // ceil(L / Tm)
 };
-// The geometry of kernel form `form` (0 tile walk, 1 resident, 2 resident with 64-row
-// workgroups) over L query tokens.
+// The geometry of kernel form `form` (0 tile walk, 1 resident; 2 resident and 3 tile walk with
+// 64-row workgroups) over L query tokens.
 PrefillGeometry prefill_geometry(int L, int Hq, int Hkv, int form);
 // Whether q-tiles of Tm tokens starting at q_lo need at most four 32-key chunks for any q-tile:
 // then the prefill keeps all of a q-tile's keys in LDS at once (the resident form).
 bool prefill_resident(int Tm, int q_lo, int w_loc, int s);
 // The form launched for Lq queries (per sequence, B sequences) starting at key index q_lo:
-// resident where its bound holds for its q-tiles (the 64-row form when the 128-row grid would be
-// small), else the tile walk.
+// resident where its bound holds for its q-tiles, else the tile walk; each with 64-row workgroups
+// when the 128-row grid would be small.
 int prefill_form(int B, int Hq, int Hkv, int Lq, int q_lo, int w_loc, int s);
 
 // What launch_prefill launches for a whole-sequence prefill: the kernel form (0 tile walk,

@@ -61,14 +61,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = 64;     // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves
-// 16-column MFMA blocks per wave: a workgroup holds 64 NQB query rows.  Forms: 0 the tile walk,
-// 1 resident with two blocks per wave (128 rows), 2 resident with one (64 rows: twice the
-// workgroups, each with half the serial work, for grids too small to fill the chip).
-constexpr int kMainNQB = 2;
-constexpr int nqb_of_form(int form) { return form == 0 ? kMainNQB : (form == 1 ? 2 : 1); }
+// 16-column MFMA blocks per wave: a workgroup holds 64 NQB query rows.  Forms: 0 the tile walk
+// and 1 resident, with two blocks per wave (128 rows); 2 resident and 3 the tile walk with one
+// (64 rows: twice the workgroups, each with half the serial work, for grids too small to fill
+// the chip).
+constexpr int nqb_of_form(int form) { return form <= 1 ? 2 : 1; }
+constexpr bool resident_form(int form) { return form == 1 || form == 2; }
 constexpr int rows_per_block(int form) { return 64 * nqb_of_form(form); }
-// Below this many 128-row resident workgroups (two per CU) the 64-row resident form is launched.
-constexpr long long kSmallGrid = 512;
+// Grids of 128-row workgroups that take the 64-row forms instead: the resident form below two
+// workgroups per CU, the tile walk (whose workgroups each walk many tiles) at most one.
+constexpr long long kSmallResidentGrid = 512;
+constexpr long long kSmallWalkGrid = 256;
 
 struct PrefillArgs {
     const uint16_t *q;
@@ -231,7 +234,7 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
 template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
-    constexpr bool RES = FORM != 0;
+    constexpr bool RES = resident_form(FORM);
     constexpr int NQB = nqb_of_form(FORM);  // 16-column blocks per wave
     constexpr int kPieces = Lds<D>::kPieces;
     constexpr int kKSteps = D / 32;    // MFMA k-steps for S
@@ -930,7 +933,7 @@ __global__ void debug_prefill_mask_kernel(uint8_t *mask, int L, int Tm, int form
         if (admitted)
             ++row[min(key, L - 1)];
     };
-    if (form != 0) {
+    if (resident_form(form)) {
         const ChunkWalk cw = plan_chunks(t0, t1, w_loc, s, kChunkN);
         for (int k = 0; k < 4; ++k)
             for (int r = 0; r < kChunkN; ++r) {
@@ -1001,11 +1004,14 @@ int prefill_form(int B, int Hq, int Hkv, int Lq, int q_lo, int w_loc, int s)
 {
     const PrefillGeometry g1 = prefill_geometry(Lq, Hq, Hkv, 1), g2 = prefill_geometry(Lq, Hq, Hkv, 2);
     const bool r1 = prefill_resident(g1.Tm, q_lo, w_loc, s), r2 = prefill_resident(g2.Tm, q_lo, w_loc, s);
-    // The 64-row form where the 128-row one would leave the chip short of workgroups.
+    // The 64-row forms where the 128-row ones would leave the chip short of workgroups (both
+    // 128-row forms have the same grid).
     const long long wg1 = (long long)B * Hkv * g1.n_hslices * g1.n_qtiles;
-    if (r2 && (!r1 || wg1 < kSmallGrid))
+    if (r2 && (!r1 || wg1 < kSmallResidentGrid))
         return 2;
-    return r1 ? 1 : 0;
+    if (r1)
+        return 1;
+    return wg1 <= kSmallWalkGrid ? 3 : 0;
 }
 
 PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
@@ -1018,7 +1024,7 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int L, int w_loc, int s)
     long long keys = 0;  // summed over the q-tiles: keys whose products one row of the tile computes
     for (int qt = 0; qt < p.g.n_qtiles; ++qt) {
         const int t0 = qt * p.g.Tm, t1 = std::min(t0 + p.g.Tm - 1, L - 1);
-        if (p.form != 0) {
+        if (resident_form(p.form)) {
             keys += 4 * kChunkN;  // four chunk slots per pass
         } else {
             const TileWalk tw = plan_tiles(t0, t1, w_loc, s, kTileN);
@@ -1084,11 +1090,15 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     if (nb > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     a.nblocks = (int)nb;
-    void (*const kernels[2][2][3])(PrefillArgs) = {
-        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>, prefill_kernel<64, 2, false>},
-         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>, prefill_kernel<128, 2, false>}},
-        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>, prefill_kernel<64, 2, true>},
-         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>, prefill_kernel<128, 2, true>}}};
+    void (*const kernels[2][2][4])(PrefillArgs) = {
+        {{prefill_kernel<64, 0, false>, prefill_kernel<64, 1, false>, prefill_kernel<64, 2, false>,
+          prefill_kernel<64, 3, false>},
+         {prefill_kernel<128, 0, false>, prefill_kernel<128, 1, false>, prefill_kernel<128, 2, false>,
+          prefill_kernel<128, 3, false>}},
+        {{prefill_kernel<64, 0, true>, prefill_kernel<64, 1, true>, prefill_kernel<64, 2, true>,
+          prefill_kernel<64, 3, true>},
+         {prefill_kernel<128, 0, true>, prefill_kernel<128, 1, true>, prefill_kernel<128, 2, true>,
+          prefill_kernel<128, 3, true>}}};
     void (*kern)(PrefillArgs) = kernels[a.n_cached > 0 ? 1 : 0][d == 128 ? 1 : 0][form];
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), 0, stream, start, stop, 0, a);

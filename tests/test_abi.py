@@ -145,7 +145,8 @@ def allowed_pairs(L, w_loc, s):
     (1, 32, 8, 16384, 4096, 4, 0, 32),   # Mistral w=4096: tile walk
     (1, 32, 8, 1024, 64, 4, 2, 16),      # Llama SWA(64,4), 256 workgroups of 128 rows: the 64-row form
     (1, 8, 4, 500, 30, 2, 2, 32),        # two q-heads per kv-head, small window: 64-row resident
-    (2, 6, 6, 300, 64, 4, 0, 128),       # no GQA: 128-token q-tiles never fit four chunks
+    (2, 6, 6, 300, 64, 4, 3, 64),        # no GQA, 36 workgroups: the 64-row tile walk
+    (4, 16, 16, 2100, 64, 4, 0, 128),    # no GQA, 1,088 workgroups: 128-token q-tiles never fit four chunks
 ])
 def test_prefill_describe_reports_the_launched_form(lib, B, Hq, Hkv, L, w, s, form, tm):
     info = binding.prefill_describe(B, Hq, Hkv, L, 128, w, s)
@@ -153,7 +154,7 @@ def test_prefill_describe_reports_the_launched_form(lib, B, Hq, Hkv, L, w, s, fo
     assert info["workgroups"] == B * Hkv * (Hq // Hkv // info["heads_per_tile"]) * -(-L // tm)
     # every allowed (query, key) pair of every head is computed at least once
     assert info["executed_pairs"] >= B * Hq * allowed_pairs(L, w, s)
-    if form != 0:  # 128 (form 1) or 64 (form 2) rows x four 32-key chunks per workgroup
+    if form in (1, 2):  # 128 (form 1) or 64 (form 2) rows x four 32-key chunks per workgroup
         assert info["executed_pairs"] == info["workgroups"] * (128 if form == 1 else 64) * 128
 
 

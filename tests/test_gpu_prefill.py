@@ -44,6 +44,9 @@ MASK_CASES = [
     # the resident form over 2,000+ tokens and 8-16 kv-heads (three window chunks and no sinks,
     # the total-window convention, sinks in a chunk of their own)
     (2085, 32, 8, 96, 0, 0), (2048, 32, 8, 68, 4, 1), (2100, 64, 16, 33, 30, 0),
+    # the 128-row tile walk (grids of 512 workgroups and more): two q-heads per kv-head, the
+    # total-window convention; the cases above with windows past four chunks take the 64-row walk
+    (4096, 32, 8, 128, 4, 1), (4100, 16, 8, 300, 7, 0),
 ]
 
 
@@ -53,8 +56,8 @@ def launched_form(L, Hq, Hkv, w, s, conv, d=128):
 
 def test_index_set_cases_cover_every_kernel_form():
     forms = {launched_form(L, Hq, Hkv, w, s, conv) for L, Hq, Hkv, w, s, conv in MASK_CASES}
-    assert forms == {0, 1, 2}
-    for form in (1, 2):  # both resident forms over more than twenty q-tiles, at least three times
+    assert forms == {0, 1, 2, 3}
+    for form in (0, 1, 2, 3):  # every form over more than twenty q-tiles, at least three times
         assert len([c for c in MASK_CASES if launched_form(*c) == form and c[0] > 640]) >= 3
 
 
@@ -123,6 +126,11 @@ PARITY = [
     (1, 513, 5, 1, 128, 100, 1, 0, 1.0, 4),
     # the resident form (G = 4) at d = 64: a last q-tile of one token
     (3, 161, 8, 2, 64, 64, 4, 0, 1.0, 4),
+    # the 128-row tile walk (512 workgroups and more; the smaller grids above take the 64-row
+    # walk or a resident form): G = 4, 2 and 1, both head sizes, both conventions, ragged tails
+    (8, 1100, 8, 2, 128, 512, 4, 0, 1.0, 4),
+    (5, 1300, 12, 6, 64, 300, 0, 1, 1.0, 0),
+    (2, 2100, 16, 16, 128, 1000, 3, 0, 1.0, 4),
 ]
 
 # Many 32-token q-tiles per kv-head in the 128-row resident form (grids of 512 workgroups and
