@@ -8,7 +8,8 @@
 // rescaled running sum) is the published method of Milakov & Gimelshein (2018).
 //
 // Workgroup: 256 threads = 4 waves, 128 query rows = Tm tokens x Gw q-heads of one
-// kv-head.  Wave w owns rows 32w .. 32w+31 as two 16-column MFMA blocks.
+// kv-head.  Wave w owns rows 32w .. 32w+31 as two 16-column MFMA blocks (64-row forms: rows
+// 16w .. 16w+15, one block).
 //
 // Matrix layout trick.  With v_mfma_f32_16x16x32_bf16, lane l holds row (l % 16) of the
 // A operand and column (l % 16) of the B operand, eight k-values each, and receives
@@ -33,13 +34,14 @@
 // re-read the same K/V tiles.  The fp32 output goes out in whole 128-byte lines with
 // non-temporal stores (store_pair).
 //
-// Two forms.  The main form walks the tiles with a running softmax: edge tiles one per step,
-// then the middle tiles through a software pipeline.  The resident form, for windows whose
-// 32-token q-tiles need at most four 32-key chunks (SWA(64,4)), loads all of a q-tile's keys
-// into LDS at once, takes the exact maximum, and stores O block by block as it completes: no
-// load follows any store, so the output drains under the compute (the chip counts loads and
-// stores in one in-order counter, so in the main form the output of a round of workgroups is
-// written after its compute and overlaps nothing).
+// Two kinds of form.  The tile walk (main form) goes through the tiles with a running softmax:
+// edge tiles one per step, then the middle tiles through a software pipeline.  The resident
+// form, for windows whose q-tiles need at most four 32-key chunks (SWA(64,4)), loads all of a
+// q-tile's keys into LDS at once, takes the exact maximum, and stores O block by block as it
+// completes: no load follows any store, so the output drains under the compute (the chip
+// counts loads and stores in one in-order counter, so in the tile walk the output of a round
+// of workgroups is written after its compute and overlaps nothing).  Each comes with 128-row
+// workgroups and, for grids too small to fill the chip, 64-row ones (twice the workgroups).
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -228,9 +230,9 @@ __device__ __forceinline__ BlockCoord block_coord(const PrefillArgs &a)
     return c;
 }
 
-// FORM: 0 main (tile walk), 1 resident (32-token q-tiles, four chunk slots).  CACHED: the key
-// sequence begins with a.n_cached keys held in the sink+ring cache (chunked prefill); the
-// whole-sequence instantiation has no cache code at all.
+// FORM: 0 tile walk, 1 resident (four chunk slots), 2 resident and 3 tile walk with 64-row
+// workgroups.  CACHED: the key sequence begins with a.n_cached keys held in the sink+ring cache
+// (chunked prefill); the whole-sequence instantiation has no cache code at all.
 template <int D, int FORM, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 {
