@@ -48,10 +48,15 @@ DEVICE_SRC = os.path.join(ROOT, "sliding_window_attention_02_amd", "csrc", "swa_
 
 
 def kernel_source_digest() -> str:
+    """Digest of the prefill kernel's code: its sources with comments and blank space removed,
+    so that a profile stays matched to the code it measured across comment-only edits."""
     h = hashlib.sha256()
     for p in (PREFILL_SRC, DEVICE_SRC):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 
