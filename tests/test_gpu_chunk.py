@@ -58,6 +58,11 @@ CASES = [
     (1, 8, 2, 128, 200, 4, 0, [300, 150, 200, 77]),
     (2, 16, 4, 64, 160, 8, 1, [70, 200, 130, 100]),
     (1, 16, 4, 128, 512, 4, 0, [512, 512, 300]),
+    # chunks whose grids fill the chip (the 128-row forms over cached keys; the smaller chunks
+    # above take the 64-row forms): the tile walk at 512-560 workgroups per chunk, the resident
+    # form on padded chunks of 2,048 tokens
+    (2, 32, 8, 128, 300, 4, 0, [1100, 1024, 400]),
+    (1, 32, 8, 128, 64, 4, 0, [2048, 2048]),
 ]
 
 
