@@ -464,7 +464,7 @@ def model_sweep(args, dev):
     8 kv-heads, d 128, SwiGLU 14336) with seeded random bf16 weights; attention is SWA(w,4) on a
     sink + ring cache for w in 64..512, full attention (a cache holding every position), or a
     hybrid stack (every layer SWA(64,4) but the last, which is full).  Each point is a HIP graph
-    of T tokens, every token one swa_layer_decode_step per layer; caches hold seeded random
+    of T tokens, every token one swa_stack_decode_step through the layers; caches hold seeded random
     keys and values for the positions before the context.  One JSON line."""
     import math
 
@@ -550,8 +550,9 @@ def model_sweep(args, dev):
                 vc.copy_(torch.randn(vc.shape, generator=gen, device=dev))
                 caches.append((kc, vc))
             state_bytes = sum(kc.numel() * 2 * 2 for kc, _ in caches)
-            ws = torch.empty(max(swa.layer_workspace_bytes(B, dm, Hq, Hkv, d, f, w, s) for w, s in layer_cfg),
-                             dtype=torch.uint8, device=dev)
+            windows = [(w, s, 0) for w, s in layer_cfg]
+            ws = torch.empty(swa.stack_workspace_bytes(windows, B, dm, Hq, Hkv, d, f), dtype=torch.uint8, device=dev)
+            stack = [(weights[li], caches[li][0], caches[li][1], w, s, 0) for li, (w, s) in enumerate(layer_cfg)]
             xin = torch.stack([inputs.residual(seed, i, B, dm) for i in range(T)]).to(dev)
             x = torch.empty(B, dm, dtype=torch.float32, device=dev)
             dpos = [torch.full((B,), P + i, dtype=torch.int64, device=dev) for i in range(T)]
@@ -559,9 +560,7 @@ def model_sweep(args, dev):
             def tokens():
                 for i in range(T):
                     x.copy_(xin[i])
-                    for li, (w, s) in enumerate(layer_cfg):
-                        swa.layer_decode_step(x, weights[li], caches[li][0], caches[li][1], dpos[i], Hq, w, s, scale,
-                                              0, eps, workspace=ws)
+                    swa.stack_decode_step(x, stack, dpos[i], Hq, scale, eps, workspace=ws)
 
             stream = torch.cuda.Stream(device=dev)
             stream.wait_stream(torch.cuda.current_stream())
@@ -585,7 +584,7 @@ def model_sweep(args, dev):
                                   "tokens_per_s": round(1e3 / ms_tok, 1), "kv_state_mb": round(state_bytes / 2 ** 20, 3),
                                   "weight_gb_per_s": round(weight_bytes / (ms_tok * 1e-3) / 1e9, 1)})
             print(json.dumps(rec["points"][-1]), file=sys.stderr, flush=True)
-            del graph, caches, ws
+            del graph, caches, ws, stack
             torch.cuda.empty_cache()
     print(json.dumps(rec), flush=True)
 

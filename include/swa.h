@@ -335,6 +335,34 @@ int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache,
                           float scale, int conv, float eps, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/*
+ * Hybrid stacks: decoder layers whose attention windows differ, SWA layers interleaved with
+ * global layers at a fixed ratio (page "Hybrid Sliding Window Attention (Hybrid SWA)", section
+ * 一.2, the design mechanism; the same page's note on caches: a rolling cache for the SWA layers,
+ * a growing one for the global layers).  A global layer is a window at least as long as the
+ * context with s = 0: its ring then holds every position (swa_cache_slots gives its slots).
+ *
+ * swa_stack_workspace_bytes -- the workspace swa_stack_decode_step needs: the largest of the
+ * layers' swa_layer_workspace_bytes (the layers run one after another on one stream and share
+ * it).  w, s, conv: host int [n_layers].  0 for invalid arguments.
+ *
+ * swa_stack_decode_step -- one decode step through n_layers layers for B sequences: layer i is
+ * swa_layer_decode_step with weights wts[i], cache k_caches[i] / v_caches[i] (bf16
+ * [B][Hkv][s[i] + w_loc(i)][d] each) and window (w[i], s[i], conv[i]); x fp32 [B][dm] is the
+ * residual stream in and out, pos int64 [B] device the step's positions.  wts, k_caches,
+ * v_caches, w, s, conv are host arrays of n_layers entries (the cache pointers are device
+ * addresses).  7 n_layers launches on `stream`.
+ * Errors: SWA_EINVAL for n_layers < 1, a null array, or any layer that swa_layer_decode_step
+ * would reject (message names the layer); every layer is checked before the first launch, so
+ * on an error x and the caches are untouched.  SWA_EHIP if a launch fails.
+ */
+size_t swa_stack_workspace_bytes(int n_layers, const int *w, const int *s, const int *conv, int B, int dm, int Hq,
+                                 int Hkv, int d, int f);
+int swa_stack_decode_step(float *x, int n_layers, const swa_layer_weights *wts, void *const *k_caches,
+                          void *const *v_caches, const int *w, const int *s, const int *conv, const int64_t *pos,
+                          int B, int dm, int Hq, int Hkv, int d, int f, float scale, float eps, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char *swa_last_error(void);
 

@@ -28,4 +28,6 @@ from .binding import (  # noqa: F401
     prefill_chunk,
     prefill_describe,
     rmsnorm,
+    stack_decode_step,
+    stack_workspace_bytes,
 )

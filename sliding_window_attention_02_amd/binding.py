@@ -43,6 +43,8 @@ EXPORTS = (
     "swa_linear",
     "swa_layer_workspace_bytes",
     "swa_layer_decode_step",
+    "swa_stack_workspace_bytes",
+    "swa_stack_decode_step",
 )
 
 LINEAR_MODES = {"store": 0, "add": 1, "silu_mul": 2}
@@ -121,6 +123,12 @@ def lib() -> ctypes.CDLL:
     L.swa_layer_decode_step.argtypes = [vp, ctypes.POINTER(_LayerWeightsC), vp, vp, vp] + [i32] * 8 + [f32, i32, f32,
                                                                                              vp, sz, vp]
     L.swa_layer_decode_step.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.swa_stack_workspace_bytes.argtypes = [i32, ip, ip, ip] + [i32] * 6
+    L.swa_stack_workspace_bytes.restype = sz
+    L.swa_stack_decode_step.argtypes = [vp, i32, ctypes.POINTER(_LayerWeightsC), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ip, ip, ip, vp] + [i32] * 6 + [f32, f32, vp, sz, vp]
+    L.swa_stack_decode_step.restype = i32
     _lib = L
     return L
 
@@ -430,4 +438,52 @@ def layer_decode_step(x, weights: dict, k_cache, v_cache, pos, Hq: int, w: int, 
     _check(lib().swa_layer_decode_step(x.data_ptr(), ctypes.byref(cw), k_cache.data_ptr(), v_cache.data_ptr(),
                                        pos.data_ptr(), B, dm, Hq, Hkv, d, f, w, s, scale, conv, float(eps),
                                        workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return x
+
+
+def _ints(xs):
+    return (ctypes.c_int * len(xs))(*[int(x) for x in xs])
+
+
+def stack_workspace_bytes(windows, B: int, dm: int, Hq: int, Hkv: int, d: int, f: int) -> int:
+    """Workspace of swa_stack_decode_step for layers with windows [(w, s, conv)]."""
+    n = len(windows)
+    return int(lib().swa_stack_workspace_bytes(n, _ints([w for w, _, _ in windows]), _ints([s for _, s, _ in windows]),
+                                               _ints([c for _, _, c in windows]), B, dm, Hq, Hkv, d, f))
+
+
+def stack_decode_step(x, layers, pos, Hq: int, scale: float | None = None, eps: float = 1e-5, workspace=None):
+    """One decode step through a stack of decoder layers (swa_stack_decode_step); x fp32 [B][dm]
+    is updated in place.
+
+    layers: list of (weights, k_cache, v_cache, w, s, conv), each as for layer_decode_step; a
+    global layer is a window at least as long as the context with s = 0.
+    """
+    B, dm = x.shape
+    _need(x, "x", torch.float32)
+    _need(pos, "pos", torch.int64, (B,))
+    _, Hkv, _, d = layers[0][1].shape
+    f = layers[0][0]["w_down"].shape[1]
+    names = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
+    shapes = {"attn_norm": (dm,), "w_qkv": ((Hq + 2 * Hkv) * d, dm), "w_o": (dm, Hq * d), "mlp_norm": (dm,),
+              "w_gate_up": (2 * f, dm), "w_down": (dm, f)}
+    n = len(layers)
+    cws = (_LayerWeightsC * n)()
+    kcs, vcs = (ctypes.c_void_p * n)(), (ctypes.c_void_p * n)()
+    for i, (wts, kc, vc, w, s, conv) in enumerate(layers):
+        for name in names:
+            _need(wts[name], name, torch.bfloat16, shapes[name])
+        _need(kc, "k_cache", torch.bfloat16, (B, Hkv, cache_slots(w, s, conv), d))
+        _need(vc, "v_cache", torch.bfloat16, kc.shape)
+        cws[i] = _LayerWeightsC(*[wts[m].data_ptr() for m in names])
+        kcs[i], vcs[i] = kc.data_ptr(), vc.data_ptr()
+    windows = [(w, s, conv) for _, _, _, w, s, conv in layers]
+    if workspace is None:
+        workspace = torch.empty(max(stack_workspace_bytes(windows, B, dm, Hq, Hkv, d, f), 1), dtype=torch.uint8,
+                                device=x.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().swa_stack_decode_step(x.data_ptr(), n, cws, kcs, vcs, _ints([w for w, _, _ in windows]),
+                                       _ints([s for _, s, _ in windows]), _ints([c for _, _, c in windows]),
+                                       pos.data_ptr(), B, dm, Hq, Hkv, d, f, scale, float(eps), workspace.data_ptr(),
+                                       workspace.numel(), _stream(x)))
     return x

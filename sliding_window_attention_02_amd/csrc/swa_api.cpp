@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 namespace {
 
@@ -250,6 +251,67 @@ int check_eps(const char *fn, float eps)
     if (!std::isfinite(eps) || eps < 0.f)
         return fail(SWA_EINVAL, "%s: eps must be finite and >= 0", fn);
     return SWA_OK;
+}
+
+// Everything swa_layer_decode_step checks for one layer except the workspace size; on success
+// *w_loc is the layer's local window and *need its workspace bytes.
+int check_layer(const char *fn, const swa_layer_weights *wts, const void *k_cache, const void *v_cache, int B, int dm,
+                int Hq, int Hkv, int d, int f, int w, int s, int conv, int *w_loc, size_t *need)
+{
+    if (wts == nullptr)
+        return fail(SWA_EINVAL, "%s: wts is null", fn);
+    CHECK_PTR(wts->attn_norm);
+    CHECK_PTR(wts->w_qkv);
+    CHECK_PTR(wts->w_o);
+    CHECK_PTR(wts->mlp_norm);
+    CHECK_PTR(wts->w_gate_up);
+    CHECK_PTR(wts->w_down);
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    int rc = check_layer_dims(fn, B, dm, Hq, Hkv, d, f);
+    if (rc)
+        return rc;
+    if ((rc = resolve_window(fn, w, s, conv, w_loc)))
+        return rc;
+    if ((long long)s + *w_loc > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    *need = layer_workspace(B, dm, Hq, Hkv, d, f, swa::decode_plan(B, Hq, Hkv, d, *w_loc, s).workspace_bytes).total;
+    return SWA_OK;
+}
+
+// The seven launches of one checked layer step: h = norm(x); q, k_new, v_new = W_qkv h; attend
+// (appending k_new, v_new); x += W_o o; h = norm(x); act = silu(W_gate h) * (W_up h);
+// x += W_down act.
+hipError_t run_layer(float *x, const swa_layer_weights *wts, void *k_cache, void *v_cache, const int64_t *pos, int B,
+                     int dm, int Hq, int Hkv, int d, int f, int w_loc, int s, float scale, float eps, char *ws,
+                     hipStream_t st)
+{
+    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
+    const LayerWorkspace L = layer_workspace(B, dm, Hq, Hkv, d, f, plan.workspace_bytes);
+    void *h = ws + L.h, *q = ws + L.q, *kn = ws + L.kn, *vn = ws + L.vn, *act = ws + L.act;
+    float *o = reinterpret_cast<float *>(ws + L.o);
+    const int nq = Hq * d, nkv = Hkv * d, nqkv = nq + 2 * nkv;
+    void *none[3] = {nullptr, nullptr, nullptr};
+    const int seg_none[4] = {0, 0, 0, 0};
+    void *qkv_out[3] = {q, kn, vn};
+    const int qkv_seg[4] = {0, nq, nq + nkv, nqkv};
+    void *act_out[3] = {act, act, act};
+    const int act_seg[4] = {0, f, f, f};
+    hipError_t e = swa::launch_rmsnorm(x, wts->attn_norm, h, B, dm, eps, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_STORE, false, wts->w_qkv, h, B, nqkv, dm, qkv_out, qkv_seg, nullptr, st);
+    if (e == hipSuccess)
+        e = swa::launch_decode(q, k_cache, v_cache, kn, vn, o, pos, B, Hq, Hkv, d, w_loc, s, scale,
+                               plan.workspace_bytes > 0 ? ws + L.dec : nullptr, plan, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_ADD, true, wts->w_o, o, B, dm, nq, none, seg_none, x, st);
+    if (e == hipSuccess)
+        e = swa::launch_rmsnorm(x, wts->mlp_norm, h, B, dm, eps, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_SILU_MUL, false, wts->w_gate_up, h, B, f, dm, act_out, act_seg, nullptr, st);
+    if (e == hipSuccess)
+        e = swa::launch_linear(swa::LIN_ADD, false, wts->w_down, act, B, dm, f, none, seg_none, x, st);
+    return e;
 }
 
 }  // namespace
@@ -499,61 +561,79 @@ int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache,
 {
     const char *fn = "swa_layer_decode_step";
     CHECK_PTR(x);
-    if (wts == nullptr)
-        return fail(SWA_EINVAL, "%s: wts is null", fn);
-    CHECK_PTR(wts->attn_norm);
-    CHECK_PTR(wts->w_qkv);
-    CHECK_PTR(wts->w_o);
-    CHECK_PTR(wts->mlp_norm);
-    CHECK_PTR(wts->w_gate_up);
-    CHECK_PTR(wts->w_down);
-    CHECK_PTR(k_cache);
-    CHECK_PTR(v_cache);
     CHECK_PTR(workspace);
     if (pos == nullptr)
         return fail(SWA_EINVAL, "%s: pos is null", fn);
-    int rc = check_layer_dims(fn, B, dm, Hq, Hkv, d, f);
-    if (rc)
-        return rc;
-    int w_loc = 0;
-    if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
+    int w_loc = 0, rc;
+    size_t need = 0;
+    if ((rc = check_layer(fn, wts, k_cache, v_cache, B, dm, Hq, Hkv, d, f, w, s, conv, &w_loc, &need)))
         return rc;
     if ((rc = check_scale(fn, scale)) || (rc = check_eps(fn, eps)))
         return rc;
-    if ((long long)s + w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
-    const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
-    const LayerWorkspace L = layer_workspace(B, dm, Hq, Hkv, d, f, plan.workspace_bytes);
-    if (workspace_bytes < L.total)
-        return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, L.total, workspace_bytes);
-    char *ws = static_cast<char *>(workspace);
-    void *h = ws + L.h, *q = ws + L.q, *kn = ws + L.kn, *vn = ws + L.vn, *act = ws + L.act;
-    float *o = reinterpret_cast<float *>(ws + L.o);
+    if (workspace_bytes < need)
+        return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+    return hip_status(fn, run_layer(x, wts, k_cache, v_cache, pos, B, dm, Hq, Hkv, d, f, w_loc, s, scale, eps,
+                                    static_cast<char *>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+size_t swa_stack_workspace_bytes(int n_layers, const int *w, const int *s, const int *conv, int B, int dm, int Hq,
+                                 int Hkv, int d, int f)
+{
+    const char *fn = "swa_stack_workspace_bytes";
+    if (n_layers < 1 || w == nullptr || s == nullptr || conv == nullptr) {
+        fail(SWA_EINVAL, "%s: n_layers must be >= 1 and w, s, conv non-null", fn);
+        return 0;
+    }
+    size_t most = 0;
+    for (int i = 0; i < n_layers; ++i) {
+        const size_t need = swa_layer_workspace_bytes(B, dm, Hq, Hkv, d, f, w[i], s[i], conv[i]);
+        if (need == 0)
+            return 0;
+        most = need > most ? need : most;
+    }
+    return most;
+}
+
+int swa_stack_decode_step(float *x, int n_layers, const swa_layer_weights *wts, void *const *k_caches,
+                          void *const *v_caches, const int *w, const int *s, const int *conv, const int64_t *pos,
+                          int B, int dm, int Hq, int Hkv, int d, int f, float scale, float eps, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    const char *fn = "swa_stack_decode_step";
+    CHECK_PTR(x);
+    CHECK_PTR(workspace);
+    if (pos == nullptr)
+        return fail(SWA_EINVAL, "%s: pos is null", fn);
+    if (n_layers < 1)
+        return fail(SWA_EINVAL, "%s: n_layers must be >= 1 (got %d)", fn, n_layers);
+    if (wts == nullptr || k_caches == nullptr || v_caches == nullptr || w == nullptr || s == nullptr || conv == nullptr)
+        return fail(SWA_EINVAL, "%s: a per-layer array is null", fn);
+    int rc;
+    if ((rc = check_scale(fn, scale)) || (rc = check_eps(fn, eps)))
+        return rc;
+    // Every layer is checked before the first launch, so an invalid layer leaves x and every
+    // cache untouched.
+    std::vector<int> w_loc(n_layers);
+    for (int i = 0; i < n_layers; ++i) {
+        size_t need = 0;
+        if ((rc = check_layer(fn, &wts[i], k_caches[i], v_caches[i], B, dm, Hq, Hkv, d, f, w[i], s[i], conv[i],
+                              &w_loc[i], &need)))
+        {
+            const std::string what = g_last_error;
+            return fail(rc, "%s (layer %d)", what.c_str(), i);
+        }
+        if (workspace_bytes < need)
+            return fail(SWA_EINVAL, "%s: workspace of %zu bytes needed (layer %d), %zu given", fn, need, i,
+                        workspace_bytes);
+    }
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const int nq = Hq * d, nkv = Hkv * d, nqkv = nq + 2 * nkv;
-    void *none[3] = {nullptr, nullptr, nullptr};
-    const int seg_none[4] = {0, 0, 0, 0};
-    void *qkv_out[3] = {q, kn, vn};
-    const int qkv_seg[4] = {0, nq, nq + nkv, nqkv};
-    void *act_out[3] = {act, act, act};
-    const int act_seg[4] = {0, f, f, f};
-    // h = norm(x); q, k_new, v_new = W_qkv h; attend (appending k_new, v_new); x += W_o o;
-    // h = norm(x); act = silu(W_gate h) * (W_up h); x += W_down act.
-    hipError_t e = swa::launch_rmsnorm(x, wts->attn_norm, h, B, dm, eps, st);
-    if (e == hipSuccess)
-        e = swa::launch_linear(swa::LIN_STORE, false, wts->w_qkv, h, B, nqkv, dm, qkv_out, qkv_seg, nullptr, st);
-    if (e == hipSuccess)
-        e = swa::launch_decode(q, k_cache, v_cache, kn, vn, o, pos, B, Hq, Hkv, d, w_loc, s, scale,
-                               plan.workspace_bytes > 0 ? ws + L.dec : nullptr, plan, st);
-    if (e == hipSuccess)
-        e = swa::launch_linear(swa::LIN_ADD, true, wts->w_o, o, B, dm, nq, none, seg_none, x, st);
-    if (e == hipSuccess)
-        e = swa::launch_rmsnorm(x, wts->mlp_norm, h, B, dm, eps, st);
-    if (e == hipSuccess)
-        e = swa::launch_linear(swa::LIN_SILU_MUL, false, wts->w_gate_up, h, B, f, dm, act_out, act_seg, nullptr, st);
-    if (e == hipSuccess)
-        e = swa::launch_linear(swa::LIN_ADD, false, wts->w_down, act, B, dm, f, none, seg_none, x, st);
-    return hip_status(fn, e);
+    for (int i = 0; i < n_layers; ++i) {
+        const hipError_t e = run_layer(x, &wts[i], k_caches[i], v_caches[i], pos, B, dm, Hq, Hkv, d, f, w_loc[i],
+                                       s[i], scale, eps, static_cast<char *>(workspace), st);
+        if (e != hipSuccess)
+            return hip_status(fn, e);
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -240,3 +240,34 @@ def test_layer_step_workspace_query_and_rejection(lib):
     assert f(*args(eps=float("inf"))) == binding.SWA_EINVAL and "eps" in err(lib)
     assert f(*args(wts=binding._LayerWeightsC(A, A, None, A, A, A))) == binding.SWA_EINVAL and "w_o" in err(lib)
     assert f(*args(x=MIS)) == binding.SWA_EINVAL and "aligned" in err(lib)
+
+
+def test_stack_step_workspace_query_and_rejection(lib):
+    """swa_stack_workspace_bytes is the largest layer's; swa_stack_decode_step checks every layer
+    before launching anything (a bad layer is named, x and the caches stay untouched)."""
+    dims = (1, 4096, 32, 8, 128, 14336)
+    ints = lambda xs: (ctypes.c_int * len(xs))(*xs)
+    w, s, conv = [64, 4096, 64], [4, 0, 4], [0, 0, 0]
+    per = [lib.swa_layer_workspace_bytes(*dims, wi, si, ci) for wi, si, ci in zip(w, s, conv)]
+    ws = lib.swa_stack_workspace_bytes(3, ints(w), ints(s), ints(conv), *dims)
+    assert ws == max(per) and per[1] > per[0]  # the global layer's split decode needs the most
+    assert lib.swa_stack_workspace_bytes(0, ints(w), ints(s), ints(conv), *dims) == 0
+    assert lib.swa_stack_workspace_bytes(2, ints([64, 4]), ints([4, 4]), ints([0, 1]), *dims) == 0  # no local window
+    wts = (binding._LayerWeightsC * 3)(*[binding._LayerWeightsC(A, A, A, A, A, A)] * 3)
+    caches = (ctypes.c_void_p * 3)(A, A, A)
+    f = lib.swa_stack_decode_step
+
+    def call(n=3, wts=wts, kcs=caches, w=w, s=s, conv=conv, ws=ws, pos=A, eps=1e-5):
+        return f(A, n, wts, kcs, caches, None if w is None else ints(w), ints(s), ints(conv), pos, *dims, 0.1, eps,
+                 A, ws, None)
+
+    assert call(n=0) == binding.SWA_EINVAL and "n_layers" in err(lib)
+    assert call(w=None) == binding.SWA_EINVAL and "array is null" in err(lib)
+    assert call(pos=None) == binding.SWA_EINVAL and "pos" in err(lib)
+    assert call(eps=-1.0) == binding.SWA_EINVAL and "eps" in err(lib)
+    assert call(ws=ws - 1) == binding.SWA_EINVAL and "workspace" in err(lib) and "layer 1" in err(lib)
+    assert call(w=[64, 4, 64], conv=[0, 1, 0], s=[4, 4, 4]) == binding.SWA_EINVAL and "layer 1" in err(lib)
+    bad = (binding._LayerWeightsC * 3)(binding._LayerWeightsC(A, A, A, A, A, A), binding._LayerWeightsC(A, A, A, A, A, A),
+                                       binding._LayerWeightsC(A, A, A, None, A, A))
+    assert call(wts=bad) == binding.SWA_EINVAL and "mlp_norm" in err(lib) and "layer 2" in err(lib)
+    assert call(kcs=(ctypes.c_void_p * 3)(A, MIS, A)) == binding.SWA_EINVAL and "aligned" in err(lib)

@@ -188,3 +188,37 @@ def test_hybrid_stack_of_window_and_full_layers():
     worst = run_stack(layers, B, dm, Hq, Hkv, d, f, steps=24, seed=51)
     say(f"max {worst:.3e}")
     assert worst <= TOL
+
+
+def test_stack_step_equals_the_layer_steps_one_by_one():
+    """swa_stack_decode_step over an SWA(8,2) / global / SWA(16,4; total-window convention)
+    stack, 20 chained steps from empty (NaN-filled) caches: the residual stream and every cache
+    equal, bit for bit, those of the same layer steps called one by one (whose results the tests
+    above check against the oracle, layer by layer)."""
+    B, dm, Hq, Hkv, d, f = 2, 512, 8, 4, 128, 512
+    spec = [(8, 2, 0), (64, 0, 0), (16, 4, 1)]
+    say("stack step", spec)
+    wts = [{k: v.cuda() for k, v in inputs.layer_weights(61, i, dm, Hq, Hkv, d, f).items()} for i in range(len(spec))]
+
+    def caches():
+        out = []
+        for w, s, conv in spec:
+            kc, vc = swa.alloc_cache(B, Hkv, d, w, s, conv)
+            kc.fill_(float("nan"))
+            vc.fill_(float("nan"))
+            out.append((kc, vc))
+        return out
+
+    ca, cb = caches(), caches()
+    for step in range(20):
+        x = inputs.residual(61, step, B, dm).cuda()
+        xa, xb = x.clone(), x.clone()
+        pos = torch.full((B,), step, dtype=torch.int64, device="cuda")
+        swa.stack_decode_step(xa, [(wts[i], ca[i][0], ca[i][1], *spec[i]) for i in range(len(spec))], pos, Hq)
+        for i, (w, s, conv) in enumerate(spec):
+            swa.layer_decode_step(xb, wts[i], cb[i][0], cb[i][1], pos, Hq, w, s, conv=conv)
+        assert torch.isfinite(xa).all()
+        assert torch.equal(xa, xb), step
+    for (ka, va), (kb, vb) in zip(ca, cb):
+        assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+        assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
