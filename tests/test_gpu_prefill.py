@@ -131,6 +131,8 @@ PARITY = [
     (8, 1100, 8, 2, 128, 512, 4, 0, 1.0, 4),
     (5, 1300, 12, 6, 64, 300, 0, 1, 1.0, 0),
     (2, 2100, 16, 16, 128, 1000, 3, 0, 1.0, 4),
+    # the 64-row tile walk at d = 64 (16-token q-tiles, a window past four chunks)
+    (2, 700, 8, 2, 64, 300, 4, 0, 1.0, 4),
 ]
 
 # Many 32-token q-tiles per kv-head in the 128-row resident form (grids of 512 workgroups and
