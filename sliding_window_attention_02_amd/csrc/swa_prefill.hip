@@ -1054,10 +1054,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, float *ou
     // A chunk after the cache has filled (all s sinks and w_loc - 1 window keys cached) whose
     // queries start off a 32-key boundary: padding rows between the sinks and the window move
     // them onto one, so the resident form can take the chunk (all of a q-tile's keys in one
-    // load instead of a chain of dependent tile steps).  No query admits a padding row: the
+    // load instead of a chain of dependent tile steps), and the tile walk's q-tiles start on a
+    // chunk boundary (each diagonal in one chunk, not two).  No query admits a padding row: the
     // first query's window starts right after the padding, and the padding lies past the sinks.
     if (cached != nullptr && cached->ns == s && cached->n_cached - cached->ns == w_loc - 1 &&
-        q_lo % kChunkN != 0 && prefill_form(B, Hq, Hkv, Lq, 0, w_loc, s) != 0)
+        q_lo % kChunkN != 0)
         gap = kChunkN - q_lo % kChunkN;
     L += gap;
     q_lo += gap;
