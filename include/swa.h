@@ -187,8 +187,9 @@ int swa_decode_describe(int B, int Hq, int Hkv, int d, int w, int s, int conv, s
  *   pos        int64 [B] device  (in)  must be >= 0
  *   workspace  device scratch of at least swa_decode_workspace_bytes(...) bytes, or
  *              NULL when that is 0; contents on entry are ignored.
- * Errors: as swa_prefill, plus SWA_EINVAL for a too-small workspace.  Concurrent calls
- * that share a workspace must be ordered by the caller.
+ * Errors: as swa_prefill, plus SWA_EINVAL for a too-small workspace and SWA_EUNSUPPORTED
+ * for B above 65535 (the launch grid indexes sequences by a dimension of at most 65535
+ * blocks).  Concurrent calls that share a workspace must be ordered by the caller.
  */
 int swa_decode_step(const void *q, const void *k_cache, const void *v_cache, float *out,
                     const int64_t *pos, int B, int Hq, int Hkv, int d, int w, int s, float scale,
@@ -352,9 +353,10 @@ int swa_layer_decode_step(float *x, const swa_layer_weights *wts, void *k_cache,
  * residual stream in and out, pos int64 [B] device the step's positions.  wts, k_caches,
  * v_caches, w, s, conv are host arrays of n_layers entries (the cache pointers are device
  * addresses).  7 n_layers launches on `stream`.
- * Errors: SWA_EINVAL for n_layers < 1, a null array, or any layer that swa_layer_decode_step
- * would reject (message names the layer); every layer is checked before the first launch, so
- * on an error x and the caches are untouched.  SWA_EHIP if a launch fails.
+ * Errors: SWA_EINVAL for n_layers < 1 or a null array; for a layer that swa_layer_decode_step
+ * would reject, the code it would return (the message names the layer); every layer is checked
+ * before the first launch, so on an error x and the caches are untouched.  SWA_EHIP if a launch
+ * fails.
  */
 size_t swa_stack_workspace_bytes(int n_layers, const int *w, const int *s, const int *conv, int B, int dm, int Hq,
                                  int Hkv, int d, int f);

@@ -82,6 +82,17 @@ int check_scale(const char *fn, float scale)
     return SWA_OK;
 }
 
+// The decode launches index sequences by the grid's third dimension (the merge by its second),
+// which holds at most 65535 blocks.
+constexpr int kMaxDecodeBatch = 65535;
+
+int check_decode_batch(const char *fn, int B)
+{
+    if (B > kMaxDecodeBatch)
+        return fail(SWA_EUNSUPPORTED, "%s: B=%d exceeds the decode launch's %d sequences", fn, B, kMaxDecodeBatch);
+    return SWA_OK;
+}
+
 int hip_status(const char *fn, hipError_t e)
 {
     if (e != hipSuccess)
@@ -127,7 +138,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
     if (pos == nullptr)
         return fail(SWA_EINVAL, "%s: pos is null", fn);
     int rc = check_heads(fn, B, Hq, Hkv, d);
-    if (rc)
+    if (rc || (rc = check_decode_batch(fn, B)))
         return rc;
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
@@ -269,7 +280,7 @@ int check_layer(const char *fn, const swa_layer_weights *wts, const void *k_cach
     CHECK_PTR(k_cache);
     CHECK_PTR(v_cache);
     int rc = check_layer_dims(fn, B, dm, Hq, Hkv, d, f);
-    if (rc)
+    if (rc || (rc = check_decode_batch(fn, B)))
         return rc;
     if ((rc = resolve_window(fn, w, s, conv, w_loc)))
         return rc;
@@ -404,7 +415,7 @@ long long swa_cache_slots(int w, int s, int conv)
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, int conv)
 {
     const char *fn = "swa_decode_workspace_bytes";
-    if (check_heads(fn, B, Hq, Hkv, d))
+    if (check_heads(fn, B, Hq, Hkv, d) || check_decode_batch(fn, B))
         return 0;
     int w_loc = 0;
     if (resolve_window(fn, w, s, conv, &w_loc))
@@ -421,7 +432,7 @@ int swa_decode_describe(int B, int Hq, int Hkv, int d, int w, int s, int conv, s
     if (info == nullptr)
         return fail(SWA_EINVAL, "%s: info is null", fn);
     int rc = check_heads(fn, B, Hq, Hkv, d);
-    if (rc)
+    if (rc || (rc = check_decode_batch(fn, B)))
         return rc;
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
@@ -547,7 +558,7 @@ int swa_linear(const void *W, const void *x, int x_f32, void *out, int mode, int
 size_t swa_layer_workspace_bytes(int B, int dm, int Hq, int Hkv, int d, int f, int w, int s, int conv)
 {
     const char *fn = "swa_layer_workspace_bytes";
-    if (check_layer_dims(fn, B, dm, Hq, Hkv, d, f))
+    if (check_layer_dims(fn, B, dm, Hq, Hkv, d, f) || check_decode_batch(fn, B))
         return 0;
     int w_loc = 0;
     if (resolve_window(fn, w, s, conv, &w_loc) || (long long)s + w_loc > 0x7fffffffLL)

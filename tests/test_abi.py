@@ -101,6 +101,21 @@ def test_decode_workspace_query_and_rejection(lib):
     assert f(A, A, A, A, A, 1, 32, 8, 128, 200, 4, 0.0, 0, A, ws, None) == binding.SWA_EINVAL
 
 
+def test_decode_batch_limit(lib):
+    # The decode launches index sequences by a grid dimension of at most 65535 blocks.
+    assert binding.decode_describe(65535, 32, 8, 128, 64, 4)["workgroups"] == 65535 * 8
+    with pytest.raises(binding.SwaError):
+        binding.decode_describe(65536, 32, 8, 128, 64, 4)
+    assert lib.swa_decode_workspace_bytes(65535, 32, 8, 128, 200, 4, 0) > 0
+    assert lib.swa_decode_workspace_bytes(65536, 32, 8, 128, 200, 4, 0) == 0
+    rc = lib.swa_decode_step(A, A, A, A, A, 65536, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None)
+    assert rc == binding.SWA_EUNSUPPORTED and "65535" in err(lib)
+    rc = lib.swa_append_decode_step(A, A, A, A, A, A, A, 65536, 32, 8, 128, 64, 4, 0.1, 0, None, 0, None)
+    assert rc == binding.SWA_EUNSUPPORTED
+    assert lib.swa_layer_workspace_bytes(65535, 4096, 32, 8, 128, 14336, 64, 4, 0) > 0
+    assert lib.swa_layer_workspace_bytes(65536, 4096, 32, 8, 128, 14336, 64, 4, 0) == 0
+
+
 def test_debug_hooks_reject_on_host(lib):
     assert lib.swa_debug_prefill_mask(None, 16, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
     assert lib.swa_debug_prefill_mask(A, 9000, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
