@@ -10,7 +10,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # Parity errors of the GPU path against the oracle, per named case: the GPU tests record them and
-# the session writes them as JSON (SWA_PARITY_REPORT, default gpurun_out/parity_report.json).
+# the session writes them as JSON to the path in SWA_PARITY_REPORT (nothing when it is unset).
 _PARITY = {}
 
 
@@ -53,11 +53,11 @@ def parity():
 
 
 def pytest_sessionfinish(session, exitstatus):
-    if not _PARITY:
+    path = os.environ.get("SWA_PARITY_REPORT")
+    if not _PARITY or not path:
         return
-    path = os.environ.get("SWA_PARITY_REPORT", os.path.join(ROOT, "gpurun_out", "parity_report.json"))
     try:
-        os.makedirs(os.path.dirname(path), exist_ok=True)
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
         with open(path, "w") as f:
             json.dump({"tolerance_max_abs": 2e-2, "cases": dict(sorted(_PARITY.items()))}, f, indent=1)
     except OSError:  # pragma: no cover
