@@ -39,7 +39,7 @@ extern "C" {
 /* Status codes. */
 #define SWA_OK 0
 #define SWA_EINVAL (-1)        /* bad argument (null/misaligned pointer, bad size...) */
-#define SWA_EUNSUPPORTED (-2)  /* valid request this build does not implement (d, sizes) */
+#define SWA_EUNSUPPORTED (-2)  /* valid request the library does not implement (d, sizes) */
 #define SWA_EHIP (-3)          /* the HIP runtime reported an error at launch */
 
 /* Window conventions. */
