@@ -25,6 +25,10 @@
  *     as the PaperWeekly page "几亿Token白练了？" phrases SWA(64,4)).  w_loc must be >= 1.
  *   - Grouped-query attention: Hq % Hkv == 0 and q-head h reads kv-head h / (Hq/Hkv).
  *   - Supported head dimensions: d = 64 and d = 128 (others give SWA_EUNSUPPORTED).
+ *   - Every call that takes a sink+ring cache (swa_kv_append, the decode steps, the chunked
+ *     prefill, the layer and stack steps and their workspace queries) gives SWA_EUNSUPPORTED
+ *     when one (sequence, kv-head) cache, (s + w_loc) * d * 2 bytes, exceeds 2^31 - 1 bytes
+ *     (more than 8,388,607 slots at d = 128): the kernels address it with 32-bit offsets.
  */
 #ifndef SWA_H
 #define SWA_H

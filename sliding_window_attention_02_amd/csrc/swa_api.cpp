@@ -82,6 +82,17 @@ int check_scale(const char *fn, float scale)
     return SWA_OK;
 }
 
+// A (sequence, kv-head) cache of s + w_loc rows of d bf16 values is addressed by 32-bit signed
+// byte offsets in the kernels: at most 2^31 - 1 bytes.
+int check_cache(const char *fn, int s, int w_loc, int d)
+{
+    const long long rows = (long long)s + w_loc;
+    if (rows * d * 2 > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: a cache of s + w_loc = %lld rows of d = %d exceeds 2^31 - 1 bytes per sequence and kv-head",
+                    fn, rows, d);
+    return SWA_OK;
+}
+
 // The decode launches index sequences by the grid's third dimension (the merge by its second),
 // which holds at most 65535 blocks.
 constexpr int kMaxDecodeBatch = 65535;
@@ -145,8 +156,8 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
         return rc;
     if ((rc = check_scale(fn, scale)))
         return rc;
-    if ((long long)s + w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    if ((rc = check_cache(fn, s, w_loc, d)))
+        return rc;
     const swa::DecodePlan plan = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
     if (use_scratch && plan.workspace_bytes > 0) {  // the static scratch stands in for the workspace
         if (plan.workspace_bytes > swa::scratch_capacity())
@@ -193,6 +204,8 @@ int chunk_impl(const char *fn, const void *q, const void *k, const void *v, void
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
         return rc;
     if ((rc = check_scale(fn, scale)))
+        return rc;
+    if ((rc = check_cache(fn, s, w_loc, d)))
         return rc;
     // (the key rows may grow by up to 31 padding rows between the sinks and the window)
     if ((long long)s + w_loc - 1 + C + 31 > 0x7fffffffLL || (long long)C * Hq * d > 0x7fffffffLL)
@@ -284,8 +297,8 @@ int check_layer(const char *fn, const swa_layer_weights *wts, const void *k_cach
         return rc;
     if ((rc = resolve_window(fn, w, s, conv, w_loc)))
         return rc;
-    if ((long long)s + *w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    if ((rc = check_cache(fn, s, *w_loc, d)))
+        return rc;
     *need = layer_workspace(B, dm, Hq, Hkv, d, f, swa::decode_plan(B, Hq, Hkv, d, *w_loc, s).workspace_bytes).total;
     return SWA_OK;
 }
@@ -397,8 +410,8 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
         return rc;
-    if ((long long)s + w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    if ((rc = check_cache(fn, s, w_loc, d)))
+        return rc;
     return hip_status(fn, swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, B, Hkv, d, w_loc, s,
                                                 n_new, static_cast<hipStream_t>(stream)));
 }
@@ -420,7 +433,7 @@ size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int w, int s, i
     int w_loc = 0;
     if (resolve_window(fn, w, s, conv, &w_loc))
         return 0;
-    if ((long long)s + w_loc > 0x7fffffffLL)
+    if (check_cache(fn, s, w_loc, d))
         return 0;
     return swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes;
 }
@@ -437,8 +450,8 @@ int swa_decode_describe(int B, int Hq, int Hkv, int d, int w, int s, int conv, s
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
         return rc;
-    if ((long long)s + w_loc > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: s + w_loc overflows", fn);
+    if ((rc = check_cache(fn, s, w_loc, d)))
+        return rc;
     const swa::DecodePlan p = swa::decode_plan(B, Hq, Hkv, d, w_loc, s);
     info->splits = p.n_split;
     info->waves_per_workgroup = p.wg_waves;
@@ -561,7 +574,7 @@ size_t swa_layer_workspace_bytes(int B, int dm, int Hq, int Hkv, int d, int f, i
     if (check_layer_dims(fn, B, dm, Hq, Hkv, d, f) || check_decode_batch(fn, B))
         return 0;
     int w_loc = 0;
-    if (resolve_window(fn, w, s, conv, &w_loc) || (long long)s + w_loc > 0x7fffffffLL)
+    if (resolve_window(fn, w, s, conv, &w_loc) || check_cache(fn, s, w_loc, d))
         return 0;
     return layer_workspace(B, dm, Hq, Hkv, d, f, swa::decode_plan(B, Hq, Hkv, d, w_loc, s).workspace_bytes).total;
 }

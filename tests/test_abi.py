@@ -116,6 +116,21 @@ def test_decode_batch_limit(lib):
     assert lib.swa_layer_workspace_bytes(65536, 4096, 32, 8, 128, 14336, 64, 4, 0) == 0
 
 
+def test_cache_size_limit(lib):
+    # One (sequence, kv-head) cache holds at most 2^31 - 1 bytes: 8,388,607 slots at d = 128.
+    big = (1 << 23) - 4  # s + w_loc = 2^23: one row too many at d = 128, fine at d = 64
+    assert lib.swa_decode_workspace_bytes(1, 8, 8, 128, big, 4, 0) == 0
+    assert lib.swa_decode_workspace_bytes(1, 8, 8, 128, big - 1, 4, 0) > 0
+    assert lib.swa_decode_workspace_bytes(1, 8, 8, 64, big, 4, 0) > 0
+    rc = lib.swa_decode_step(A, A, A, A, A, 1, 8, 8, 128, big, 4, 0.1, 0, A, 1 << 40, None)
+    assert rc == binding.SWA_EUNSUPPORTED and "2^31 - 1 bytes" in err(lib)
+    rc = lib.swa_kv_append(A, A, A, A, A, 1, 8, 128, big, 4, 1, 0, None)
+    assert rc == binding.SWA_EUNSUPPORTED
+    rc = lib.swa_prefill_chunk(A, A, A, A, A, A, None, 0, 1, 8, 8, 16, 128, big, 4, 0.1, 0, None)
+    assert rc == binding.SWA_EUNSUPPORTED
+    assert lib.swa_layer_workspace_bytes(1, 4096, 32, 8, 128, 14336, big, 4, 0) == 0
+
+
 def test_debug_hooks_reject_on_host(lib):
     assert lib.swa_debug_prefill_mask(None, 16, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
     assert lib.swa_debug_prefill_mask(A, 9000, 4, 4, 128, 8, 2, 0, None) == binding.SWA_EINVAL
