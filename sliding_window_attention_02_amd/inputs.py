@@ -145,6 +145,24 @@ def random_qkv(B, L, Hq, Hkv, d, seed, std=1.0, sink_boost_n=0, sink_boost=1.0):
     return _round_bf16(q), _round_bf16(k), _round_bf16(v)
 
 
+def random_qkv_device(B, L, Hq, Hkv, d, seed, device, std=1.0, sink_boost_n=0, sink_boost=1.0):
+    """Seeded bf16 q [B][L][Hq][d], k, v [B][L][Hkv][d] drawn on `device` (a generator of that
+    device, one sequence at a time, so inputs of many GiB need no host copy); the same recipe as
+    random_qkv with another stream of random numbers."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = []
+    for H in (Hq, Hkv, Hkv):
+        t = torch.empty(B, L, H, d, dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            x = torch.randn(L, H, d, generator=g, dtype=torch.float32, device=device) * std
+            t[b] = x.to(torch.bfloat16)  # round to nearest even
+            del x
+        out.append(t)
+    if sink_boost_n > 0:
+        out[1][:, :sink_boost_n] *= sink_boost  # x4 is exact in bf16
+    return tuple(out)
+
+
 def kv_at(seed: int, position: int, B: int, Hkv: int, d: int, std: float = 1.0,
           sink_boost_n: int = 0, sink_boost: float = 1.0):
     """(k, v) bf16 [B][Hkv][d] of one absolute position."""

@@ -224,6 +224,32 @@ def test_full_size_workloads_sampled_rows(name, parity):
         check_close(got, np.stack([ref[t] for t in rows]), f"{name} prefill (sampled rows)", parity)
 
 
+@pytest.mark.parametrize("w,s,form", [(64, 4, 1), (1000, 4, 0)])
+def test_longest_sequence_sampled_rows(w, s, form, parity):
+    """Two sequences, each of the most q elements the boundary accepts (L Hq d = 2^31 - 1024 at
+    Hq = 8, d = 128: L = 2,097,151, a ragged last q-tile): the second sequence's q, k, v and
+    output start past 2^31 elements and its output past 2^33 bytes.  The resident form and the
+    tile walk, checked on sampled rows of both sequences."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    L = (2 ** 31 - 1) // (Hq * d)
+    assert swa.prefill_describe(B, Hq, Hkv, L, d, w, s)["form"] == form
+    say("longest", B, L, Hq, Hkv, d, w, s)
+    q, k, v = inputs.random_qkv_device(B, L, Hq, Hkv, d, seed=77, device="cuda", sink_boost_n=4, sink_boost=4.0)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.prefill(q, k, v, w, s, scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(77)
+    for b in range(B):
+        rows = sample_rows(L, w, s, rng) + [L - 33, L - 32, L - 31]
+        rows = sorted(set(rows))
+        ref = oracle_rows(q, k, v, b, rows, w, s, 0, scale)
+        got = out[b, rows].cpu().numpy()
+        check_close(got, np.stack([ref[t] for t in rows]), "prefill at the longest sequence (sampled rows)", parity)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
 def test_prefill_is_deterministic_and_keeps_guard_bands():
     B, L, Hq, Hkv, d = 1, 700, 32, 8, 128
     q, k, v = [t.cuda() for t in inputs.random_qkv(B, L, Hq, Hkv, d, seed=5, sink_boost_n=4, sink_boost=4.0)]
