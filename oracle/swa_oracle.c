@@ -273,6 +273,28 @@ int swa_oracle_lse_rows(const double *q, const double *k, double *lse, int64_t B
  * The entries whose position is in A(t) are kept (by the predicate), the others are
  * ignored, and out[h] = softmax-weighted sum over the kept entries for each q-head.
  * Returns the number of kept entries, or -1 on bad arguments / duplicate positions. */
+static int cmp_i64(const void *a, const void *b)
+{
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* 1 if two of pos[0..n-1] are equal, 0 if not, -1 if out of memory (a sorted copy, then
+ * neighbours compared: n log n, so explicit sets of millions of entries stay cheap). */
+static int has_duplicates(const int64_t *pos, int64_t n)
+{
+    int64_t *c = (int64_t *)malloc((size_t)n * sizeof(int64_t));
+    if (!c)
+        return -1;
+    memcpy(c, pos, (size_t)n * sizeof(int64_t));
+    qsort(c, (size_t)n, sizeof(int64_t), cmp_i64);
+    int dup = 0;
+    for (int64_t i = 1; i < n && !dup; ++i)
+        dup = c[i] == c[i - 1];
+    free(c);
+    return dup;
+}
+
 int64_t swa_oracle_decode_row(const double *q, const int64_t *pos, const double *k,
                               const double *v, int64_t n, int64_t t, int64_t Hq, int64_t Hkv,
                               int64_t d, int64_t w_loc, int64_t s, double scale, double *out)
@@ -280,10 +302,8 @@ int64_t swa_oracle_decode_row(const double *q, const int64_t *pos, const double 
     if (!q || !pos || !k || !v || !out || n < 1 || Hkv < 1 || Hq % Hkv != 0 || w_loc < 1 ||
         s < 0)
         return -1;
-    for (int64_t a = 0; a < n; ++a)
-        for (int64_t b = a + 1; b < n; ++b)
-            if (pos[a] == pos[b])
-                return -1;
+    if (has_duplicates(pos, n) != 0)
+        return -1;
     const int64_t group = Hq / Hkv;
     double *lg = (double *)malloc((size_t)n * sizeof(double));
     if (!lg)

@@ -371,3 +371,47 @@ def test_full_attention_decode_at_long_context(P, B, Hq, Hkv, d, parity):
         worst = max(worst, float(np.abs(out[b] - ref).max()))
     say(f"max {worst:.3e}")
     assert worst <= TOL
+
+
+def test_decode_at_the_largest_cache(parity):
+    """A (sequence, kv-head) cache of the most slots the boundary accepts at d = 128
+    (s + w_loc = 2^23 - 1: 2^31 - 256 bytes per tensor, the end of the kernels' 32-bit
+    offsets), filled by one append and read by the fused step just after the ring wrapped:
+    every slot up to the last is read, over some 87,000 workgroup splits and their merge."""
+    B, Hq, Hkv, d, s = 1, 2, 1, 128, 4
+    n_slots = 2 ** 23 - 1
+    w = n_slots - s
+    assert swa.cache_slots(w, s) == n_slots
+    t = n_slots + 5  # the ring has wrapped: the newest positions sit in its first slots
+    say("largest-cache decode", n_slots, t)
+    q, k, v = inputs.random_qkv_device(B, t + 1, Hq, Hkv, d, seed=91, device="cuda", sink_boost_n=4, sink_boost=4.0)
+    del q
+    # Each head's query points at one key, so its row is about that key's value and a wrong slot
+    # address shows at full size: head 0 the position in the cache's last slot (s + w - 1), head 1
+    # one in the middle of the ring.
+    targets = [w - 1, w // 2]
+    qt = torch.stack([k[0, p_, 0].float() * 20.0 for p_ in targets]).to(torch.bfloat16)[None].contiguous()
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s)
+    swa.kv_append(kc, vc, k[:, :t], v[:, :t], gpos([0]), w, s)
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.append_decode_step(qt, kc, vc, k[:, t].contiguous(), v[:, t].contiguous(), gpos([t]), w, s,
+                                 scale, workspace=ws).cpu().numpy()
+    say("appended and attended")
+    # A(t): the sinks and the w keys ending at t (oracle input built from the same tensors)
+    lo = t - w + 1
+    pos = np.concatenate([np.arange(s), np.arange(lo, t + 1)]).astype(np.int64)
+    kk = f64(torch.cat([k[0, :s], k[0, lo:t + 1]]))
+    vv = f64(torch.cat([v[0, :s], v[0, lo:t + 1]]))
+    del k, v, kc, vc
+    torch.cuda.empty_cache()
+    say("oracle inputs on the host")
+    ref, kept = orc.decode_row(f64(qt[0]), pos, kk, vv, t, w, s, scale)
+    say("oracle row done")
+    assert kept == n_slots
+    for h, p_ in enumerate(targets):  # the rows are dominated by the targeted values
+        assert np.abs(ref[h] - vv[s + p_ - lo, 0]).max() < 0.1
+    err = np.abs(out[0] - ref)
+    parity("decode at the largest cache", err)
+    say(f"max {err.max():.3e}")
+    assert err.max() <= TOL

@@ -248,6 +248,30 @@ def test_decode_row_matches_prefill_row_any_order_and_ignores_extra_entries():
         np.testing.assert_allclose(out, ref[0, t], rtol=0, atol=1e-13)
     with pytest.raises(ValueError):
         orc.decode_row(f64(q)[0, 3], [0, 0], f64(k)[0, :2], f64(v)[0, :2], 3, w, s, 0.4)
+    with pytest.raises(ValueError):  # a repeat anywhere in the list, not only next to its twin
+        orc.decode_row(f64(q)[0, 3], [2, 0, 3, 0], f64(k)[0, :4], f64(v)[0, :4], 3, w, s, 0.4)
+
+
+def test_decode_row_takes_a_large_explicit_set():
+    """Hundreds of thousands of explicit entries (a very long window's cache) are checked for
+    repeats and attended in well under a second; the row equals the one over A(t) alone."""
+    n, Hq, Hkv, d, w, s = 300_000, 2, 1, 8, 250_000, 4
+    rng = np.random.default_rng(3)
+    pos = rng.permutation(n).astype(np.int64)
+    k = rng.standard_normal((n, Hkv, d))
+    v = rng.standard_normal((n, Hkv, d))
+    q = rng.standard_normal((Hq, d))
+    t = n - 1
+    out, used = orc.decode_row(q, pos, k, v, t, w, s, 0.3)
+    assert used == w + s
+    keep = [j for j in range(n) if pos[j] < s or pos[j] > t - w]
+    ref, used2 = orc.decode_row(q, pos[keep], k[keep], v[keep], t, w, s, 0.3)
+    assert used2 == used
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    dup = pos.copy()
+    dup[-1] = dup[0]
+    with pytest.raises(ValueError):
+        orc.decode_row(q, dup, k, v, t, w, s, 0.3)
 
 
 @pytest.mark.parametrize("w_loc,s", [(16, 3), (64, 4), (4, 0)])
