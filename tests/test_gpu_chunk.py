@@ -186,3 +186,47 @@ def _random_chunkings(n, seed):
 @pytest.mark.parametrize("B,Hq,Hkv,d,w,s,conv,chunks", _random_chunkings(6, 777))
 def test_chunked_prefill_on_drawn_chunkings(B, Hq, Hkv, d, w, s, conv, chunks, parity):
     test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks, parity)
+
+
+def test_chunk_at_the_largest_cache():
+    """A chunk of 64 tokens against the largest cache the boundary accepts (s + w_loc = 2^23 - 1
+    slots at d = 128, filled by one append, the ring wrapped): head 0 of every row aims at the
+    key in the cache's last slot, head 1 at the oldest key of the row's window (the ring's
+    wrap-around region), so a wrong cached-key address shows at full size; rows checked against
+    the oracle over every key they may see."""
+    B, Hq, Hkv, d, s, C = 1, 2, 1, 128, 4, 64
+    n_slots = 2 ** 23 - 1
+    w = n_slots - s
+    pos0 = n_slots + 100
+    say("chunk at the largest cache", n_slots, pos0)
+    _, k, v = inputs.random_qkv_device(B, pos0 + C, 1, Hkv, d, seed=93, device="cuda", sink_boost_n=4,
+                                       sink_boost=4.0)
+    kc, vc = swa.alloc_cache(B, Hkv, d, w, s)
+    swa.kv_append(kc, vc, k[:, :pos0], v[:, :pos0], torch.zeros(B, dtype=torch.int64, device="cuda"), w, s)
+    last_slot_pos = w - 1  # slot s + (p mod w) = n_slots - 1, inside every row's window
+    rows_t = [pos0 + r for r in range(C)]
+    aims = [[last_slot_pos, t - w + 1] for t in rows_t]
+    q = torch.stack([torch.stack([k[0, p_, 0].float() * 20.0 for p_ in a]) for a in aims])[None]
+    q = q.to(torch.bfloat16).contiguous()
+    scale = 1.0 / np.sqrt(d)
+    out = swa.prefill_chunk(q, k[:, pos0:].contiguous(), v[:, pos0:].contiguous(), kc, vc, pos0, w, s,
+                            scale).cpu().numpy()
+    say("chunk attended")
+    lo = pos0 - w + 1  # the first row's window start; later rows' windows start later
+    pos = np.concatenate([np.arange(s), np.arange(lo, pos0 + C)]).astype(np.int64)
+    kk = f64(torch.cat([k[0, :s], k[0, lo:pos0 + C]]))
+    vv = f64(torch.cat([v[0, :s], v[0, lo:pos0 + C]]))
+    qq = f64(q[0])
+    del k, v, kc, vc
+    torch.cuda.empty_cache()
+    say("oracle inputs on the host")
+    worst = 0.0
+    for r in (0, 1, 17, C - 1):
+        t = rows_t[r]
+        ref, kept = orc.decode_row(qq[r], pos, kk, vv, t, w, s, scale)
+        assert kept == n_slots
+        for h, p_ in enumerate(aims[r]):  # the rows are dominated by the targeted values
+            assert np.abs(ref[h] - vv[s + p_ - lo, 0]).max() < 0.1
+        worst = max(worst, float(np.abs(out[0, r] - ref).max()))
+        say("row", r, f"max {worst:.3e}")
+    assert worst <= TOL
