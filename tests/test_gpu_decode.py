@@ -415,3 +415,50 @@ def test_decode_at_the_largest_cache(parity):
     parity("decode at the largest cache", err)
     say(f"max {err.max():.3e}")
     assert err.max() <= TOL
+
+
+def test_decode_at_the_largest_batch(parity):
+    """The largest batch the decode launch indexes (65535 sequences, SWA(64,4), 32/8 heads, every
+    sequence at its own position past the ring's wrap): the fused step appends each sequence's
+    token and attends; sampled sequences, the last included, against the oracle row over their
+    68 cached entries as the test lays them out (the cache drawn at random as the state after
+    position t_b - 1)."""
+    B, Hq, Hkv, d, w, s = 65535, 32, 8, 128, 64, 4
+    n_slots = w + s
+    say("largest-batch decode", B)
+    g = torch.Generator(device="cuda").manual_seed(95)
+    kc = torch.empty(B, Hkv, n_slots, d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    step = 4096
+    for c in (kc, vc):
+        for b0 in range(0, B, step):
+            c[b0:b0 + step] = torch.randn(min(step, B - b0), Hkv, n_slots, d, generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn(B, Hq, d, generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(B, Hkv, d, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(B, Hkv, d, generator=g, device="cuda").to(torch.bfloat16)
+    t = 200 + 7 * np.arange(B, dtype=np.int64)
+    sample = [0, 1, 777, 32767, B - 2, B - 1]
+    before = {b: (f64(kc[b]), f64(vc[b])) for b in sample}  # [Hkv][n_slots][d]
+    ws = swa.alloc_workspace(B, Hq, Hkv, d, w, s)
+    scale = 1.0 / np.sqrt(d)
+    out = swa.append_decode_step(q, kc, vc, kn, vn, torch.from_numpy(t).cuda(), w, s, scale, workspace=ws)
+    out = out[sample].cpu().numpy()
+    say("appended and attended")
+    worst = 0.0
+    for i, b in enumerate(sample):
+        tb = int(t[b])
+        k0, v0 = before[b]
+        # slot j < s holds position j; ring slot s + r the latest position p <= tb with p mod w = r,
+        # the new token tb in its own slot
+        pos = list(range(s)) + [tb - ((tb - r) % w) for r in range(w)]
+        kk = np.transpose(k0, (1, 0, 2)).copy()
+        vv = np.transpose(v0, (1, 0, 2)).copy()
+        kk[s + tb % w] = f64(kn[b])
+        vv[s + tb % w] = f64(vn[b])
+        ref, kept = orc.decode_row(f64(q[b]), pos, kk, vv, tb, w, s, scale)
+        assert kept == n_slots
+        err = np.abs(out[i] - ref)
+        parity("decode at the largest batch", err)
+        worst = max(worst, float(err.max()))
+    say(f"max {worst:.3e}")
+    assert worst <= TOL
