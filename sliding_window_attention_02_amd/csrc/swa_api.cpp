@@ -104,6 +104,17 @@ int check_decode_batch(const char *fn, int B)
     return SWA_OK;
 }
 
+// One sequence of q (and so of k and v, Hkv <= Hq) holds fewer than 2^31 elements, and a
+// q-tile's output rows span less than 2 GiB: the kernels' 32-bit offsets.
+int check_prefill_sizes(const char *fn, int L, int Hq, int d)
+{
+    if ((long long)L * Hq * d > 0x7fffffffLL)
+        return fail(SWA_EUNSUPPORTED, "%s: one sequence of q holds more than 2^31-1 elements", fn);
+    if ((long long)Hq * d >= (1LL << 22))
+        return fail(SWA_EUNSUPPORTED, "%s: Hq * d = %lld reaches 2^22", fn, (long long)Hq * d);
+    return SWA_OK;
+}
+
 int hip_status(const char *fn, hipError_t e)
 {
     if (e != hipSuccess)
@@ -128,10 +139,8 @@ int prefill_impl(const char *fn, const void *q, const void *k, const void *v, fl
         return rc;
     if ((rc = check_scale(fn, scale)))
         return rc;
-    if ((long long)L * Hq * d > 0x7fffffffLL)
-        return fail(SWA_EUNSUPPORTED, "%s: one sequence of q holds more than 2^31-1 elements", fn);
-    if ((long long)Hq * d >= (1LL << 22))  // a q-tile's output rows must span less than 2 GiB
-        return fail(SWA_EUNSUPPORTED, "%s: Hq * d = %lld reaches 2^22", fn, (long long)Hq * d);
+    if ((rc = check_prefill_sizes(fn, L, Hq, d)))
+        return rc;
     return hip_status(fn, swa::launch_prefill(q, k, v, out, B, Hq, Hkv, L, d, w_loc, s, scale,
                                               static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start),
                                               static_cast<hipEvent_t>(stop)));
@@ -370,6 +379,8 @@ int swa_prefill_describe(int B, int Hq, int Hkv, int L, int d, int w, int s, int
         return rc;
     if (L < 1)
         return fail(SWA_EINVAL, "%s: L must be >= 1 (got %d)", fn, L);
+    if ((rc = check_prefill_sizes(fn, L, Hq, d)))
+        return rc;
     int w_loc = 0;
     if ((rc = resolve_window(fn, w, s, conv, &w_loc)))
         return rc;

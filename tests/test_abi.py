@@ -193,6 +193,11 @@ def test_prefill_describe_rejects_on_host(lib):
     assert lib.swa_prefill_describe(1, 4, 2, 16, 128, 8, 4, 0, None) == binding.SWA_EINVAL
     assert lib.swa_prefill_describe(1, 4, 2, 16, 96, 8, 4, 0, ctypes.byref(info)) == binding.SWA_EUNSUPPORTED
     assert lib.swa_prefill_describe(1, 4, 2, 0, 128, 8, 4, 0, ctypes.byref(info)) == binding.SWA_EINVAL
+    # the size limits of swa_prefill: L Hq d below 2^31, Hq d below 2^22
+    L = (2 ** 31 - 1) // (8 * 128)
+    assert lib.swa_prefill_describe(2, 8, 2, L, 128, 64, 4, 0, ctypes.byref(info)) == binding.SWA_OK
+    assert lib.swa_prefill_describe(2, 8, 2, L + 1, 128, 64, 4, 0, ctypes.byref(info)) == binding.SWA_EUNSUPPORTED
+    assert lib.swa_prefill_describe(1, 32768, 8, 4, 128, 64, 4, 0, ctypes.byref(info)) == binding.SWA_EUNSUPPORTED
 
 
 def test_prefill_timed_requires_events(lib):
