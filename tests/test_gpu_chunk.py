@@ -188,7 +188,7 @@ def test_chunked_prefill_on_drawn_chunkings(B, Hq, Hkv, d, w, s, conv, chunks, p
     test_chunked_prefill_equals_prefill_rows_and_cache(B, Hq, Hkv, d, w, s, conv, chunks, parity)
 
 
-def test_chunk_at_the_largest_cache():
+def test_chunk_at_the_largest_cache(parity):
     """A chunk of 64 tokens against the largest cache the boundary accepts (s + w_loc = 2^23 - 1
     slots at d = 128, filled by one append, the ring wrapped): head 0 of every row aims at the
     key in the cache's last slot, head 1 at the oldest key of the row's window (the ring's
@@ -227,6 +227,8 @@ def test_chunk_at_the_largest_cache():
         assert kept == n_slots
         for h, p_ in enumerate(aims[r]):  # the rows are dominated by the targeted values
             assert np.abs(ref[h] - vv[s + p_ - lo, 0]).max() < 0.1
-        worst = max(worst, float(np.abs(out[0, r] - ref).max()))
+        err = np.abs(out[0, r] - ref)
+        parity("chunked prefill at the largest cache", err)
+        worst = max(worst, float(err.max()))
         say("row", r, f"max {worst:.3e}")
     assert worst <= TOL
